@@ -1,0 +1,172 @@
+"""Sparse-decode benchmark of the PrHS hot path on one MI355X.
+
+One step = one pass of the whole hot path over one decode query batch:
+score (K scan) -> exact top-N select -> sparse attention over the selected
+rows with the fused dropped mass, on the Mistral-7B-shaped GQA layer with a
+32K context (batch 4, 32 query heads on 8 KV heads, d = 128, fp16, N = 2048).
+
+Prints one JSON line. ``value`` is heads*steps/s over the timed steps with
+inputs resident in HBM. Independent copies of K and V are rotated so that no
+step finds its KV cache in the 256 MB Infinity Cache left by the previous
+one. ``roofline`` reports the scan kernel (the dominant kernel): algorithmic
+bytes (the K cache it must read) over its mean duration from HIP events on
+the launch stream. ``cpu_baseline`` times the fp64 numpy oracle on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="mistral_gqa_32k")
+    ap.add_argument("--rotate", type=int, default=4, help="independent KV copies cycled over steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, n_steps, budget_s):
+    """Time the fp64 oracle on a bounded sample of the workload (heads of the first steps)."""
+    from oracle import prhs_oracle as O
+    cfg = w.cfg
+    K = w.K.double().cpu().numpy()
+    V = w.V.double().cpu().numpy()
+    q = w.q.double().cpu().numpy()
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+    done = 0
+    t0 = time.perf_counter()
+    s = 0
+    while time.perf_counter() - t0 < budget_s:
+        for (b, h) in heads:
+            O.decode_step(q[s % n_steps], K, V, "topn", N=cfg.budget, heads=[(b, h)])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        s += 1
+    el = time.perf_counter() - t0
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    return {"value": done / el, "unit": "heads*steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} (head, step) oracle passes (score+top-{cfg.budget}+attention+delta, fp64) "
+                      f"of the {cfg.name} workload in {el:.1f} s"}
+
+
+def main():
+    a = _parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path shards by "
+              f"(batch, KV head) with no communication, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+    from sparse_top_kv_head_amd import prhs as P
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+
+    P.lib()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[a.config]
+    w = make_workload(cfg, device=dev)
+    Ks = [w.K] + [w.K.clone() for _ in range(a.rotate - 1)]
+    Vs = [w.V] + [w.V.clone() for _ in range(a.rotate - 1)]
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    stream = torch.cuda.current_stream()
+    N = cfg.budget
+
+    def step(i, ev=None):
+        r = i % a.rotate
+        q = w.q[i % cfg.steps]
+        if ev is not None:
+            ev[0].record(stream)
+        eng.score(q, Ks[r], stream)
+        if ev is not None:
+            ev[1].record(stream)
+        eng.select(P.PRHS_TOPN, N, stream=stream)
+        eng.decode(q, Ks[r], Vs[r], True, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(a.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    scan_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+
+    B, Hq, Hkv, d, t, eb = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.elem_bytes
+    heads = B * Hq
+    value = heads * a.steps / (total_ms / 1e3)
+    scan_bytes = B * Hkv * t * d * eb
+    # distinct V rows per (b, kv head) selected at the last timed step (algorithmic gather bytes)
+    idx = eng.idx.cpu().numpy()
+    cnt = eng.count.cpu().numpy()
+    G = Hq // Hkv
+    rows = 0
+    for b in range(B):
+        for g in range(Hkv):
+            rows += np.unique(np.concatenate([idx[b, h, :cnt[b, h]] for h in range(g * G, (g + 1) * G)])).size
+    step_bytes = scan_bytes + rows * d * eb
+    scan_gbs = scan_bytes / (scan_ms.mean() / 1e3) / 1e9
+    res = {
+        "metric": "sparse decode attn heads*steps/s at 32K ctx + achieved HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "heads*steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(total_ms / a.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Mistral-7B-shaped GQA decode layer, B={B}, H_q={Hq}, "
+                               f"H_kv={Hkv}, d={d}, t={t}, top-N={N}, fp16 K/V",
+                   "batch": B, "ctx_len": t, "budget": N, "kv_copies_rotated": a.rotate},
+        "roofline": {"bound": "hbm", "kernel": "score_scan (K scan GEMV)",
+                     "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": scan_bytes,
+                     "mean_launch_ms": round(float(scan_ms.mean()), 5)},
+        "step": {"hbm_alg_bytes": int(step_bytes), "hbm_alg_gbs": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
+                 "frac_of_peak": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 5) for p in (10, 50, 90)],
+                 "scan_ms_p50": round(float(np.median(scan_ms)), 5),
+                 "wall_s": round(wall, 4)},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, cfg.steps, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * prhs.h -- C ABI of the MI355X (gfx950) hot path of Pre-hoc Sparsity (PrHS)
+ * sparse decode.
+ *
+ * Source: the page "Near-Oracle KV Selection via Pre-hoc Sparsity for
+ * Long-Context Inference" (Gao, Wang, Tu, Zhang, Cheng, Tao; arXiv 2602.08329).
+ * Per attention head and decode step the method picks a budget of N KV entries
+ * (Table I: selector S, index set S_t, budget N), attends over only those
+ * entries (Abstract; Table V caption: a fused sparse-attention kernel), and
+ * accounts for the attention mass it keeps and drops (Table I: tau(.), delta(.)).
+ * The critical-index set of one query may be shared, dilated, with temporally
+ * adjacent queries (Fig. 4; Table VIII radius r; CIS block size s).
+ *
+ * General contract of every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never frees or retains them. Inputs must stay unchanged until the work
+ *    enqueued on `stream` has completed.
+ *  - Every call validates its arguments on the host BEFORE any HIP call. On
+ *    any error it returns a negative status, enqueues nothing and leaves every
+ *    output untouched. A detail string is available from prhs_last_error()
+ *    (thread-local).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream), allocates no memory and does not synchronise,
+ *    unless the environment variable PRHS_DEBUG_SYNC=1 is set, in which case
+ *    each call synchronises its stream and reports kernel faults as
+ *    PRHS_E_HIP.
+ *  - Layout: q is [B, H_q, d] contiguous. K and V are [B, H_kv, t, d] with the
+ *    element strides given in prhs_dims (the d axis is contiguous). Scores are
+ *    fp32 [B, H_q, scores_ld]. Index sets are int32 [B, H_q, cap] plus int32
+ *    counts [B, H_q]; valid entries are ascending, unique and in [0, t);
+ *    entries past the count are unspecified. Per-head scalars (lse, delta,
+ *    tau) are fp32 [B, H_q].
+ *  - Query head h reads KV head h / G with G = H_q / H_kv (grouped-query
+ *    attention).
+ *  - Alignment: q, K, V and scores base pointers must be 16-byte aligned;
+ *    kv_stride_t * element size, kv_stride_h and kv_stride_b must keep every
+ *    row 16-byte aligned; scores_ld must be a multiple of 4.
+ */
+#ifndef PRHS_H
+#define PRHS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. 0 is success; every error is negative. */
+enum {
+  PRHS_OK = 0,
+  PRHS_E_NULL = -1,      /* a required pointer is NULL                                   */
+  PRHS_E_DIMS = -2,      /* H_q % H_kv != 0, t < 1, d unsupported, bad strides/ld, t too large */
+  PRHS_E_DTYPE = -3,     /* unknown element type                                         */
+  PRHS_E_BUDGET = -4,    /* N outside [1, t], delta target outside [0, 1], radius < 0, bad mode */
+  PRHS_E_CAPACITY = -5,  /* an index buffer is smaller than the result may need           */
+  PRHS_E_WORKSPACE = -6, /* workspace NULL or smaller than prhs_workspace_bytes()         */
+  PRHS_E_HIP = -7,       /* the HIP runtime reported an error at launch (or at debug sync) */
+  PRHS_E_ALIGN = -8      /* a pointer, stride or ld breaks the alignment rules above      */
+};
+
+/* Element type of q, K and V. Scores, outputs and mass values are always fp32. */
+enum { PRHS_F32 = 0, PRHS_F16 = 1 };
+
+/* Selection modes of prhs_select_topk. */
+enum { PRHS_TOPN = 0, PRHS_DELTA = 1 };
+
+/* Operations for prhs_workspace_bytes. */
+enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2 };
+
+/* Largest context length the selection kernel keeps resident on chip. */
+#define PRHS_MAX_SELECT_CTX 65536
+
+typedef struct prhs_dims {
+  int32_t batch;        /* B >= 1                                           */
+  int32_t n_q_heads;    /* H_q >= 1, a multiple of n_kv_heads               */
+  int32_t n_kv_heads;   /* H_kv >= 1                                        */
+  int32_t head_dim;     /* d: 64 or 128                                     */
+  int32_t ctx_len;      /* t >= 1: keys in the cache                        */
+  int32_t dtype;        /* PRHS_F32 or PRHS_F16                             */
+  int64_t kv_stride_b;  /* element strides of K and V (same layout for both) */
+  int64_t kv_stride_h;
+  int64_t kv_stride_t;  /* >= d                                             */
+  int32_t scores_ld;    /* row stride of the scores buffer, >= t            */
+} prhs_dims;
+
+/*
+ * prhs_score -- scaled dot-product scores of the decode query against every
+ * cached key, and the dense log-sum-exp (Table I: q, K, d and the attention
+ * weight A(.); the scale 1/sqrt(d) is the standard one).
+ *
+ *   scores[b,h,i] = (sum_c q[b,h,c] * K[b,h/G,i,c]) / sqrt(d)   for i < t
+ *   lse_all[b,h]  = log sum_i exp(scores[b,h,i])
+ *
+ * Products are accumulated in fp32. The K row of every key is read once for
+ * all G query heads of its group. lse_all may be NULL (then ws may be NULL).
+ * ws: device workspace of at least prhs_workspace_bytes(dims, PRHS_OP_SCORE, 0)
+ * bytes (per-chunk partial maxima and sums); its contents on entry do not matter.
+ */
+int prhs_score(const prhs_dims* dims, const void* q, const void* k, float* scores,
+               float* lse_all, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prhs_select_topk -- the per-head index set S (Table I: selector S, set S_t,
+ * budget N).
+ *
+ * mode PRHS_TOPN: the top-k oracle (Fig. 1, Fig. 2, Fig. 9): the n_budget keys
+ *   of largest score; ties at the boundary go to the lower index.
+ * mode PRHS_DELTA: control of the dropped mass (Abstract): the smallest
+ *   N* >= 1 whose top-N* set leaves delta = sum of the dropped weights
+ *   exp(s - lse_all) <= delta_target, capped at n_budget. Needs lse_all. When
+ *   the cap binds, cap_hit[b,h] = 1 (else 0) if cap_hit is not NULL.
+ *   Weights are accumulated in 2^-40 fixed point, so the result does not
+ *   depend on the order of accumulation.
+ *
+ * Output: idx[b,h,0:count) ascending; count[b,h] = N (TOPN) or N* (DELTA).
+ * Requires 1 <= n_budget <= t, n_budget <= idx_cap, 0 <= delta_target <= 1,
+ * t <= PRHS_MAX_SELECT_CTX. Scores must be finite or -inf (NaN is outside
+ * the contract); -0.0 and +0.0 compare equal. lse_all may be NULL in TOPN mode.
+ */
+int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* lse_all,
+                     int32_t mode, int32_t n_budget, float delta_target, int32_t* idx,
+                     int32_t idx_cap, int32_t* count, int32_t* cap_hit, hipStream_t stream);
+
+/*
+ * prhs_cis_reuse -- critical-index-set sharing with dilation (Fig. 4: the set
+ * of one query serves the next queries, grown around its clusters; Table VIII:
+ * radius r).
+ *
+ *   out = sorted union over i in anchor set of [max(0, i - r), min(t - 1, i + r)]
+ *
+ * anchor_idx[b,h,0:anchor_count) must be ascending and unique (as
+ * prhs_select_topk writes it). radius 0 returns the anchor set unchanged.
+ * out_cap must be >= min(t, (2r + 1) * anchor_cap). Counts are clamped to
+ * [0, anchor_cap] and writes never pass out_cap.
+ * Optional similarity gate (Fig. 8, Fig. 9(c)): when q_cur, q_anchor and
+ * reuse_ok are all non-NULL, reuse_ok[b,h] = (cos(q_cur[b,h], q_anchor[b,h]) >=
+ * sim_tau); the dilated set is written either way and the caller refreshes
+ * the heads whose flag is 0. The queries use dims->dtype and layout [B,H_q,d].
+ */
+int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                   const int32_t* anchor_count, int32_t radius, const void* q_cur,
+                   const void* q_anchor, float sim_tau, int32_t* out_idx, int32_t out_cap,
+                   int32_t* out_count, int32_t* reuse_ok, hipStream_t stream);
+
+/*
+ * prhs_sparse_decode -- attention over the selected entries only (Abstract;
+ * Table V caption), with the softmax renormalised over the set:
+ *
+ *   m_S = max_{i in S} s_i,  out = sum_{i in S} e^{s_i - m_S} v_i / sum_{i in S} e^{s_i - m_S}
+ *   lse_sel = m_S + log sum_{i in S} e^{s_i - m_S}
+ *
+ * S = idx[b,h,0:count[b,h]). s_i is read from `scores` when it is non-NULL
+ * (the scores of the same step from prhs_score); otherwise the K rows at S
+ * are gathered and scored (k must then be non-NULL). The set is split over
+ * workgroups and the partial (max, sum, output) triples are merged exactly.
+ * Indices outside [0, t) are skipped; counts are clamped to [0, idx_cap]; an
+ * empty set gives out = 0, lse_sel = -inf.
+ * Fused dropped mass: when lse_all and delta are non-NULL,
+ * delta = clamp(-expm1(lse_sel - lse_all), 0, 1) and, if tau is non-NULL,
+ * tau = 1 - delta.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_DECODE, idx_cap) bytes.
+ */
+int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* idx, int32_t idx_cap, const int32_t* count,
+                       const float* scores, const float* lse_all, float* out, float* lse_sel,
+                       float* delta, float* tau, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
+ * prhs_dropped_mass -- dropped and retained attention mass of the selected
+ * sets (Table I: delta(.), tau(.)):
+ *   delta = clamp(-expm1(lse_sel - lse_all), 0, 1),  tau = 1 - delta.
+ * tau may be NULL.
+ */
+int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* lse_all,
+                      float* delta, float* tau, hipStream_t stream);
+
+/* Workspace bytes needed by `op` (PRHS_OP_*) for these dims; `cap` is the
+ * idx_cap of prhs_sparse_decode and is ignored otherwise. Returns 0 for
+ * invalid dims. */
+size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap);
+
+/* Static text for a status code. */
+const char* prhs_status_string(int status);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* prhs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRHS_H */

@@ -1,0 +1,254 @@
+// Sparse attention over the selected entries (page "Near-Oracle KV Selection
+// via Pre-hoc Sparsity for Long-Context Inference": Abstract and the Table V
+// caption's fused sparse-attention kernel; Table I tau(.) / delta(.)).
+//
+// Split-budget decode: the selected list of a head is cut into splits of
+// kDecodeRows entries, one 256-thread workgroup each, so even a few heads fill
+// the chip. A workgroup gathers its entries' scores (stored by the score scan,
+// or recomputed from gathered K rows on steps without a scan), takes their
+// maximum, turns them into weights in LDS, then streams the V rows at those
+// indices with 16-byte lane loads (LPR lanes per row, several rows in flight
+// per lane) and accumulates weight * v in fp32. Each split leaves a partial
+// (max, sum, output) triple; the merge kernel combines them exactly as the
+// online softmax does and, when the dense log-sum-exp is given, writes the
+// dropped mass delta and the retained mass tau of the set.
+#include "prhs_device.hpp"
+#include "prhs_launch.hpp"
+
+namespace prhs {
+namespace {
+
+constexpr int kDecThreads = 256;
+
+template <typename T, int D, bool HAS_SCORES>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int* __restrict__ idx, int idx_cap, const int* __restrict__ count,
+    const float* __restrict__ scores, int Hq, int Hkv, int t, long long sb, long long sh,
+    long long st, int ld, float scale, float* __restrict__ part, int nsplit) {
+  constexpr int NW = kDecThreads / kWave;
+  constexpr int ROWS = kDecodeRows;
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  constexpr int RPW = kWave / LPR;
+  constexpr int U = 4;
+
+  __shared__ int sidx[ROWS];
+  __shared__ float sp[ROWS];
+  __shared__ float sred[NW];
+  __shared__ __align__(16) float so[NW][D];
+
+  const int split = blockIdx.x;
+  const int head = blockIdx.y;
+  const int b = head / Hq;
+  const int h = head - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int c = lane % LPR;
+  const int rr = lane / LPR;
+
+  const int n = max(0, min(count[head], idx_cap));
+  const int beg = split * ROWS;
+  const int nr = max(0, min(ROWS, n - beg));
+  const int* irow = idx + (size_t)head * idx_cap + beg;
+
+  for (int i = tid; i < nr; i += kDecThreads) {
+    const int id = irow[i];
+    const bool ok = id >= 0 && id < t;
+    sidx[i] = ok ? id : -1;
+    if constexpr (HAS_SCORES) sp[i] = ok ? scores[(size_t)head * ld + id] : -INFINITY;
+  }
+  __syncthreads();
+
+  const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
+  if constexpr (!HAS_SCORES) {
+    const uint4 qv = load16(q + (size_t)head * D + c * E);
+    const char* kbase = reinterpret_cast<const char*>(k + kv_off) + c * 16;
+    for (int i0 = w * RPW * U; i0 < nr; i0 += NW * RPW * U) {
+      uint4 kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * RPW + rr;
+        const int id = i < nr ? sidx[i] : -1;
+        kv[u] = id >= 0 ? load16(kbase + (size_t)id * st * sizeof(T)) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * RPW + rr;
+        const float s = group_sum<LPR>(dot16(kv[u], qv, 0.f, T()));
+        if (c == 0 && i < nr) sp[i] = sidx[i] >= 0 ? s * scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+  }
+
+  // split maximum
+  float m = -INFINITY;
+  for (int i = tid; i < nr; i += kDecThreads) m = fmaxf(m, sp[i]);
+  m = wave_max(m);
+  if (lane == 0) sred[w] = m;
+  __syncthreads();
+  m = sred[0];
+#pragma unroll
+  for (int k2 = 1; k2 < NW; ++k2) m = fmaxf(m, sred[k2]);
+  __syncthreads();
+  // weights and their sum
+  float l = 0.f;
+  for (int i = tid; i < nr; i += kDecThreads) {
+    const float p = (m == -INFINITY) ? 0.f : __expf(sp[i] - m);
+    sp[i] = p;
+    l += p;
+  }
+  l = wave_sum(l);
+  if (lane == 0) sred[w] = l;
+  __syncthreads();
+  l = 0.f;
+#pragma unroll
+  for (int k2 = 0; k2 < NW; ++k2) l += sred[k2];
+
+  // weighted V rows
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  const char* vbase = reinterpret_cast<const char*>(v + kv_off) + c * 16;
+  for (int i0 = w * RPW * U; i0 < nr; i0 += NW * RPW * U) {
+    uint4 vv[U];
+    float pw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * RPW + rr;
+      const int id = i < nr ? sidx[i] : -1;
+      pw[u] = id >= 0 ? sp[i] : 0.f;
+      vv[u] = id >= 0 ? load16(vbase + (size_t)id * st * sizeof(T)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) axpy16(pw[u], vv[u], acc, T());
+  }
+  // sum the RPW row slots of the wave (lanes c, c+LPR, ...)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (rr == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) so[w][c * E + e] = acc[e];
+  }
+  __syncthreads();
+  float* dst = part + ((size_t)head * nsplit + split) * (D + 2);
+  for (int col = tid; col < D; col += kDecThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < NW; ++k2) s += so[k2][col];
+    dst[col] = s;
+  }
+  if (tid == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part, int nsplit,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ lse_sel,
+                                                         const float* __restrict__ lse_all,
+                                                         float* __restrict__ delta,
+                                                         float* __restrict__ tau) {
+  const int head = blockIdx.x;
+  const int col = threadIdx.x;
+  const float* p = part + (size_t)head * nsplit * (D + 2);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p[(size_t)s * (D + 2) + D]);
+  float l = 0.f, o = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ps = p + (size_t)s * (D + 2);
+      const float ms = ps[D];
+      if (ms == -INFINITY) continue;
+      const float f = __expf(ms - m);
+      l += ps[D + 1] * f;
+      o += ps[col] * f;
+    }
+  }
+  out[(size_t)head * D + col] = l > 0.f ? o / l : 0.f;
+  if (col == 0) {
+    const float lse = l > 0.f ? m + __logf(l) : -INFINITY;
+    lse_sel[head] = lse;
+    if (lse_all != nullptr && delta != nullptr) {
+      const float dlt = fminf(fmaxf(-expm1f(lse - lse_all[head]), 0.f), 1.f);
+      delta[head] = dlt;
+      if (tau != nullptr) tau[head] = 1.f - dlt;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restrict__ lse_sel,
+                                                           const float* __restrict__ lse_all,
+                                                           float* __restrict__ delta,
+                                                           float* __restrict__ tau, int nheads) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= nheads) return;
+  const float dlt = fminf(fmaxf(-expm1f(lse_sel[h] - lse_all[h]), 0.f), 1.f);
+  delta[h] = dlt;
+  if (tau != nullptr) tau[h] = 1.f - dlt;
+}
+
+template <typename T, int D>
+void launch_split(const prhs_dims& d, const void* q, const void* k, const void* v, const int* idx,
+                  int idx_cap, const int* count, const float* scores, float* part, int nsplit,
+                  hipStream_t stream) {
+  dim3 grid(nsplit, d.batch * d.n_q_heads);
+  const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
+  if (scores)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(kDecThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), idx, idx_cap, count, scores, d.n_q_heads,
+                       d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
+                       (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
+                       part, nsplit);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(kDecThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), idx, idx_cap, count, scores, d.n_q_heads,
+                       d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
+                       (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
+                       part, nsplit);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const void* v,
+                         const int* idx, int idx_cap, const int* count, const float* scores,
+                         const float* lse_all, float* out, float* lse_sel, float* delta, float* tau,
+                         void* ws, hipStream_t stream) {
+  const int nsplit = decode_nsplit(idx_cap);
+  float* part = static_cast<float*>(ws);
+  if (d.dtype == PRHS_F16) {
+    if (d.head_dim == 128) launch_split<__half, 128>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+    else launch_split<__half, 64>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+  } else {
+    if (d.head_dim == 128) launch_split<float, 128>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+    else launch_split<float, 64>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+  }
+  const int nheads = d.batch * d.n_q_heads;
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(nheads), dim3(128), 0, stream, part, nsplit,
+                       out, lse_sel, lse_all, delta, tau);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(nheads), dim3(64), 0, stream, part, nsplit,
+                       out, lse_sel, lse_all, delta, tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_dropped_mass(const prhs_dims& d, const float* lse_sel, const float* lse_all,
+                               float* delta, float* tau, hipStream_t stream) {
+  const int nheads = d.batch * d.n_q_heads;
+  hipLaunchKernelGGL(dropped_mass_kernel, dim3((nheads + 255) / 256), dim3(256), 0, stream,
+                     lse_sel, lse_all, delta, tau, nheads);
+  return hipGetLastError();
+}
+
+}  // namespace prhs

@@ -1,0 +1,211 @@
+// C ABI of the PrHS decode hot path: host-side validation and dispatch.
+//
+// Every entry point checks all of its arguments before touching the HIP
+// runtime, so an invalid call returns its status with nothing enqueued and no
+// output written. Launch errors are reported as PRHS_E_HIP.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "prhs.h"
+#include "prhs_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return PRHS_OK;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("PRHS_DEBUG_SYNC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+int finish(hipError_t err, hipStream_t stream, const char* what) {
+  if (err == hipSuccess && debug_sync()) {
+    err = hipStreamSynchronize(stream);
+    if (err == hipSuccess) err = hipGetLastError();
+  }
+  if (err != hipSuccess) return fail(PRHS_E_HIP, "%s: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+size_t elem_size(int dtype) { return dtype == PRHS_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every call that takes dims.
+int check_dims(const prhs_dims* d) {
+  if (d == nullptr) return fail(PRHS_E_NULL, "dims is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(PRHS_E_DIMS, "batch and head counts must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(PRHS_E_DIMS, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", d->n_q_heads,
+                d->n_kv_heads);
+  if ((long long)d->batch * d->n_q_heads > 65535)
+    return fail(PRHS_E_DIMS, "batch * n_q_heads must be <= 65535");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PRHS_E_DIMS, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->ctx_len < 1) return fail(PRHS_E_DIMS, "ctx_len must be >= 1");
+  if (d->dtype != PRHS_F32 && d->dtype != PRHS_F16)
+    return fail(PRHS_E_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->kv_stride_t < d->head_dim || d->kv_stride_h < 0 || d->kv_stride_b < 0)
+    return fail(PRHS_E_DIMS, "kv strides must be non-negative and kv_stride_t >= head_dim");
+  const long long es = (long long)elem_size(d->dtype);
+  if ((d->kv_stride_t * es) % 16 || (d->kv_stride_h * es) % 16 || (d->kv_stride_b * es) % 16)
+    return fail(PRHS_E_ALIGN, "kv strides must keep rows 16-byte aligned");
+  if (d->scores_ld < d->ctx_len) return fail(PRHS_E_DIMS, "scores_ld must be >= ctx_len");
+  if (d->scores_ld % 4) return fail(PRHS_E_ALIGN, "scores_ld must be a multiple of 4");
+  return PRHS_OK;
+}
+
+size_t score_ws(const prhs_dims* d) {
+  return (size_t)d->batch * d->n_q_heads * prhs::score_nchunks(*d) * 2 * sizeof(float);
+}
+
+size_t decode_ws(const prhs_dims* d, int cap) {
+  return (size_t)d->batch * d->n_q_heads * prhs::decode_nsplit(cap) * (d->head_dim + 2) *
+         sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* prhs_status_string(int status) {
+  switch (status) {
+    case PRHS_OK: return "ok";
+    case PRHS_E_NULL: return "a required pointer is NULL";
+    case PRHS_E_DIMS: return "invalid dimensions";
+    case PRHS_E_DTYPE: return "unsupported element type";
+    case PRHS_E_BUDGET: return "budget, target or radius out of range";
+    case PRHS_E_CAPACITY: return "index buffer capacity too small";
+    case PRHS_E_WORKSPACE: return "workspace missing or too small";
+    case PRHS_E_HIP: return "HIP runtime error";
+    case PRHS_E_ALIGN: return "misaligned pointer, stride or leading dimension";
+    default: return "unknown status";
+  }
+}
+
+const char* prhs_last_error(void) { return g_last_error; }
+
+size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap) {
+  if (check_dims(dims) != PRHS_OK) return 0;
+  switch (op) {
+    case PRHS_OP_SCORE: return score_ws(dims);
+    case PRHS_OP_SELECT: return 0;
+    case PRHS_OP_DECODE: return cap >= 1 ? decode_ws(dims, cap) : 0;
+    default: return 0;
+  }
+}
+
+int prhs_score(const prhs_dims* dims, const void* q, const void* k, float* scores, float* lse_all,
+               void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k || !scores) return fail(PRHS_E_NULL, "q, k and scores are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores))
+    return fail(PRHS_E_ALIGN, "q, k and scores must be 16-byte aligned");
+  if (lse_all) {
+    if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required when lse_all is requested");
+    if (ws_bytes < score_ws(dims))
+      return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", score_ws(dims), ws_bytes);
+    if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return finish(prhs::launch_score(*dims, q, k, scores, lse_all, ws, stream), stream, "prhs_score");
+}
+
+int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* lse_all, int32_t mode,
+                     int32_t n_budget, float delta_target, int32_t* idx, int32_t idx_cap,
+                     int32_t* count, int32_t* cap_hit, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
+    return fail(PRHS_E_DIMS, "selection supports ctx_len <= %d", PRHS_MAX_SELECT_CTX);
+  if (!scores || !idx || !count) return fail(PRHS_E_NULL, "scores, idx and count are required");
+  if (mode != PRHS_TOPN && mode != PRHS_DELTA) return fail(PRHS_E_BUDGET, "unknown mode %d", mode);
+  if (mode == PRHS_DELTA && !lse_all) return fail(PRHS_E_NULL, "DELTA mode needs lse_all");
+  if (!aligned16(scores)) return fail(PRHS_E_ALIGN, "scores must be 16-byte aligned");
+  if (n_budget < 1 || n_budget > dims->ctx_len)
+    return fail(PRHS_E_BUDGET, "n_budget %d outside [1, %d]", n_budget, dims->ctx_len);
+  if (mode == PRHS_DELTA && !(delta_target >= 0.f && delta_target <= 1.f))
+    return fail(PRHS_E_BUDGET, "delta_target must lie in [0, 1]");
+  if (idx_cap < n_budget)
+    return fail(PRHS_E_CAPACITY, "idx_cap %d < n_budget %d", idx_cap, n_budget);
+  return finish(prhs::launch_select(*dims, scores, lse_all, mode, n_budget, delta_target, idx,
+                                    idx_cap, count, cap_hit, stream),
+                stream, "prhs_select_topk");
+}
+
+int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                   const int32_t* anchor_count, int32_t radius, const void* q_cur,
+                   const void* q_anchor, float sim_tau, int32_t* out_idx, int32_t out_cap,
+                   int32_t* out_count, int32_t* reuse_ok, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!anchor_idx || !anchor_count || !out_idx || !out_count)
+    return fail(PRHS_E_NULL, "anchor_idx, anchor_count, out_idx and out_count are required");
+  if (reuse_ok && (!q_cur || !q_anchor))
+    return fail(PRHS_E_NULL, "the similarity gate needs q_cur and q_anchor");
+  if (radius < 0) return fail(PRHS_E_BUDGET, "radius must be >= 0");
+  if (reuse_ok && std::isnan(sim_tau)) return fail(PRHS_E_BUDGET, "sim_tau is NaN");
+  if (anchor_cap < 1) return fail(PRHS_E_CAPACITY, "anchor_cap must be >= 1");
+  const long long need_ll = (2LL * radius + 1) * (long long)anchor_cap;
+  const long long need = need_ll < dims->ctx_len ? need_ll : dims->ctx_len;
+  if (out_cap < need)
+    return fail(PRHS_E_CAPACITY, "out_cap %d < min(t, (2r+1)*anchor_cap) = %lld", out_cap, need);
+  return finish(prhs::launch_cis(*dims, anchor_idx, anchor_cap, anchor_count, radius, q_cur,
+                                 q_anchor, sim_tau, out_idx, out_cap, out_count, reuse_ok, stream),
+                stream, "prhs_cis_reuse");
+}
+
+int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                       const int32_t* idx, int32_t idx_cap, const int32_t* count,
+                       const float* scores, const float* lse_all, float* out, float* lse_sel,
+                       float* delta, float* tau, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!v || !idx || !count || !out || !lse_sel)
+    return fail(PRHS_E_NULL, "v, idx, count, out and lse_sel are required");
+  if (!scores && (!q || !k)) return fail(PRHS_E_NULL, "without scores, q and k are required");
+  if (delta && !lse_all) return fail(PRHS_E_NULL, "delta needs lse_all");
+  if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
+  if (!aligned16(v) || (k && !aligned16(k)) || (q && !aligned16(q)))
+    return fail(PRHS_E_ALIGN, "q, k and v must be 16-byte aligned");
+  if (idx_cap < 1) return fail(PRHS_E_CAPACITY, "idx_cap must be >= 1");
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < decode_ws(dims, idx_cap))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", decode_ws(dims, idx_cap),
+                ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
+                                    lse_sel, delta, tau, ws, stream),
+                stream, "prhs_sparse_decode");
+}
+
+int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* lse_all,
+                      float* delta, float* tau, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!lse_sel || !lse_all || !delta) return fail(PRHS_E_NULL, "lse_sel, lse_all and delta are required");
+  return finish(prhs::launch_dropped_mass(*dims, lse_sel, lse_all, delta, tau, stream), stream,
+                "prhs_dropped_mass");
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// Device-side helpers shared by the PrHS kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace prhs {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element types: one 16-byte lane load holds kElems elements.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int kPer16B = 4; };
+template <> struct Elem<__half> { static constexpr int kPer16B = 8; };
+
+// Dot product of one 16-byte slice of a key row with the matching slice of a
+// query (kept as raw 16 bytes), accumulated in fp32.
+__device__ __forceinline__ float dot16(const uint4 a, const uint4 b, float acc, float /*tag*/) {
+  const float* x = reinterpret_cast<const float*>(&a);
+  const float* y = reinterpret_cast<const float*>(&b);
+  acc = __builtin_fmaf(x[0], y[0], acc);
+  acc = __builtin_fmaf(x[1], y[1], acc);
+  acc = __builtin_fmaf(x[2], y[2], acc);
+  acc = __builtin_fmaf(x[3], y[3], acc);
+  return acc;
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot16(const uint4 a, const uint4 b, float acc, __half /*tag*/) {
+  const half2_t* x = reinterpret_cast<const half2_t*>(&a);
+  const half2_t* y = reinterpret_cast<const half2_t*>(&b);
+  acc = __builtin_amdgcn_fdot2(x[0], y[0], acc, false);
+  acc = __builtin_amdgcn_fdot2(x[1], y[1], acc, false);
+  acc = __builtin_amdgcn_fdot2(x[2], y[2], acc, false);
+  acc = __builtin_amdgcn_fdot2(x[3], y[3], acc, false);
+  return acc;
+}
+
+// Widen one 16-byte slice to fp32 and accumulate w * slice into acc[kPer16B].
+__device__ __forceinline__ void axpy16(float w, const uint4 a, float* acc, float /*tag*/) {
+  const float* x = reinterpret_cast<const float*>(&a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w, x[i], acc[i]);
+}
+
+__device__ __forceinline__ void axpy16(float w, const uint4 a, float* acc, __half /*tag*/) {
+  const half2_t* x = reinterpret_cast<const half2_t*>(&a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = __builtin_fmaf(w, (float)x[i].x, acc[2 * i]);
+    acc[2 * i + 1] = __builtin_fmaf(w, (float)x[i].y, acc[2 * i + 1]);
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming load: the data is read once, so mark it non-temporal.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane data movement
+// ---------------------------------------------------------------------------
+// DPP controls (GFX9 encoding).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR consecutive lanes; every lane of the group
+// receives the group total. LPR in {4, 8, 16, 32, 64}.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if constexpr (LPR >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (LPR >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (LPR >= 32) {
+    // swap the two 16-lane halves of each 32-lane group
+    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+  }
+  if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Combine two (max, sum-of-exp) pairs: sum is relative to its max; an empty
+// pair is (-inf, 0).
+__device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) { m = mn; l = 0.f; return; }
+  l = l * __expf(m - mn) + l2 * __expf(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void wave_ml(float& m, float& l) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o);
+    const float l2 = __shfl_xor(l, o);
+    ml_combine(m, l, m2, l2);
+  }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename U>
+__device__ __forceinline__ U wave_inclusive_scan(U x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const U y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a whole workgroup of NT threads. `tmp` is LDS of
+// at least NT / 64 elements. Returns the exclusive prefix; `total` receives the
+// workgroup total. Contains two barriers.
+template <int NT, typename U>
+__device__ __forceinline__ U block_exclusive_scan(U x, U* tmp, U& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const U inc = wave_inclusive_scan(x);
+  if (lane == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  U base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const U v = tmp[i];
+    if (i < w) base += v;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return base + inc - x;
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving 32-bit key of an fp32 score (larger score -> larger key).
+// -0.0 is folded onto +0.0 so that the two compare equal.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __builtin_bit_cast(uint32_t, s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace prhs

@@ -1,0 +1,175 @@
+// K-scan scoring kernel: s[b,h,i] = q[b,h,:] . K[b,h/G,i,:] / sqrt(d) for every
+// cached key, plus per-chunk (max, sum-of-exp) partials of the dense softmax
+// (page "Near-Oracle KV Selection via Pre-hoc Sparsity for Long-Context
+// Inference", Table I: query q, keys K, per-head dimension d, attention weight A).
+//
+// HBM-bound GEMV: every K row is read exactly once, by one wave, with 16-byte
+// loads, and is scored against all G query heads of its group in registers.
+// Layout on the wave: LPR lanes cover one row (LPR = 16 for d=128 fp16), so
+// one load instruction covers RPW = 64/LPR rows; the LPR partial dot products
+// of a row are summed with DPP row operations. Scores are staged in LDS and
+// written back coalesced; the chunk's softmax partials come from the staged
+// values.
+#include "prhs_device.hpp"
+#include "prhs_launch.hpp"
+
+namespace prhs {
+namespace {
+
+constexpr int kScoreThreads = 256;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
+    float2* __restrict__ part, int Hq, int Hkv, int t, long long sb, long long sh, long long st,
+    int ld, int nchunks, int g_off, float scale) {
+  constexpr int NW = kScoreThreads / kWave;
+  constexpr int CHUNK = kScoreChunk;
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  constexpr int RPW = kWave / LPR;
+  constexpr int U = 8;
+  constexpr int RW = CHUNK / NW;
+  constexpr int ITERS = RW / (U * RPW);
+  static_assert(G <= LPR, "one lane per head in a row group");
+  static_assert(RW % (U * RPW) == 0, "chunk tiling");
+
+  __shared__ __align__(16) float sc[G][CHUNK];
+
+  const int chunk = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv;
+  const int g = unit - b * Hkv;
+  const int h0 = g * (Hq / Hkv) + g_off;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int c = lane % LPR;
+  const int rr = lane / LPR;
+
+  uint4 qv[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) qv[j] = load16(q + ((size_t)(b * Hq + h0 + j) * D + c * E));
+
+  const char* kbase = reinterpret_cast<const char*>(k + b * sb + g * sh) + c * 16;
+  const size_t row_bytes = (size_t)st * sizeof(T);
+  const int wrow0 = w * RW;
+  const int grow0 = chunk * CHUNK + wrow0;
+
+#pragma unroll 1
+  for (int it = 0; it < ITERS; ++it) {
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = grow0 + it * U * RPW + u * RPW + rr;
+      if (r < t) {
+        kv[u] = load16_stream(kbase + (size_t)r * row_bytes);
+      } else {
+        kv[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float acc[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) acc[j] = group_sum<LPR>(dot16(kv[u], qv[j], 0.f, T()));
+      float val = acc[0];
+#pragma unroll
+      for (int j = 1; j < G; ++j) val = (c == j) ? acc[j] : val;
+      if (c < G) sc[c][wrow0 + it * U * RPW + u * RPW + rr] = val * scale;
+    }
+  }
+  __syncthreads();
+
+  const int base_row = chunk * CHUNK;
+  const int nrows = min(CHUNK, t - base_row);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
+    for (int i = threadIdx.x * 4; i < nrows; i += kScoreThreads * 4) {
+      if (i + 4 <= nrows) {
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
+      } else {
+        for (int e = 0; i + e < nrows; ++e) dst[i + e] = sc[j][i + e];
+      }
+    }
+  }
+  if (part != nullptr) {
+    for (int j = w; j < G; j += NW) {
+      float m = -INFINITY;
+      for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
+      m = wave_max(m);
+      float l = 0.f;
+      if (m != -INFINITY)
+        for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
+      l = wave_sum(l);
+      if (lane == 0) part[(size_t)(b * Hq + h0 + j) * nchunks + chunk] = make_float2(m, l);
+    }
+  }
+}
+
+// Merge the per-chunk partials of each head into its dense log-sum-exp.
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float2* __restrict__ part,
+                                                        float* __restrict__ lse_all, int nheads,
+                                                        int nchunks) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= nheads) return;
+  float m = -INFINITY, l = 0.f;
+  for (int c = 0; c < nchunks; ++c) {
+    const float2 p = part[(size_t)h * nchunks + c];
+    ml_combine(m, l, p.x, p.y);
+  }
+  lse_all[h] = (l > 0.f) ? m + __logf(l) : -INFINITY;
+}
+
+template <typename T, int D, int G>
+void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores, float2* part,
+                 int g_off, hipStream_t stream) {
+  const int nchunks = score_nchunks(d);
+  dim3 grid(nchunks, d.batch * d.n_kv_heads);
+  const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
+  hipLaunchKernelGGL((score_scan_kernel<T, D, G>), grid, dim3(kScoreThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k), scores, part, d.n_q_heads,
+                     d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
+                     (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
+}
+
+template <typename T, int D>
+void launch_scan_group(const prhs_dims& d, const void* q, const void* k, float* scores,
+                       float2* part, int G, hipStream_t stream) {
+  // Power-of-two sub-groups of the query heads that share one KV head.
+  int off = 0;
+  while (off < G) {
+    const int rest = G - off;
+    const int sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
+    switch (sub) {
+      case 8: launch_scan<T, D, 8>(d, q, k, scores, part, off, stream); break;
+      case 4: launch_scan<T, D, 4>(d, q, k, scores, part, off, stream); break;
+      case 2: launch_scan<T, D, 2>(d, q, k, scores, part, off, stream); break;
+      default: launch_scan<T, D, 1>(d, q, k, scores, part, off, stream); break;
+    }
+    off += sub;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const prhs_dims& d, const void* q, const void* k, float* scores,
+                        float* lse_all, void* ws, hipStream_t stream) {
+  float2* part = lse_all ? static_cast<float2*>(ws) : nullptr;
+  const int G = d.n_q_heads / d.n_kv_heads;
+  if (d.dtype == PRHS_F16) {
+    if (d.head_dim == 128) launch_scan_group<__half, 128>(d, q, k, scores, part, G, stream);
+    else launch_scan_group<__half, 64>(d, q, k, scores, part, G, stream);
+  } else {
+    if (d.head_dim == 128) launch_scan_group<float, 128>(d, q, k, scores, part, G, stream);
+    else launch_scan_group<float, 64>(d, q, k, scores, part, G, stream);
+  }
+  if (lse_all) {
+    const int nheads = d.batch * d.n_q_heads;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((nheads + 255) / 256), dim3(256), 0, stream, part,
+                       lse_all, nheads, score_nchunks(d));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace prhs

@@ -1,0 +1,81 @@
+"""Decode-step driver over the C ABI: owns the per-step buffers and enqueues
+score -> select -> sparse decode (anchor steps), dilate -> sparse decode (CIS
+reuse steps) on one stream. Buffers are allocated once; a step allocates
+nothing.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import prhs as P
+
+
+class DecodeEngine:
+    """Buffers and calls for one layer shape.
+
+    K, V layout [B, H_kv, t, d]; q [B, H_q, d]; index capacity ``cap`` per head
+    (TOPN budget, DELTA cap, or the dilated size of a reused set).
+    """
+
+    def __init__(self, K: torch.Tensor, n_q_heads: int, cap: int, device=None):
+        self.dims = P.make_dims(K, n_q_heads)
+        d = self.dims
+        dev = device or K.device
+        self.nheads = d.batch * d.n_q_heads
+        self.cap = cap
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.scores = torch.empty((d.batch, d.n_q_heads, d.scores_ld), **f32)
+        self.lse_all = torch.empty((d.batch, d.n_q_heads), **f32)
+        self.idx = torch.empty((d.batch, d.n_q_heads, cap), **i32)
+        self.count = torch.empty((d.batch, d.n_q_heads), **i32)
+        self.cap_hit = torch.empty((d.batch, d.n_q_heads), **i32)
+        self.out = torch.empty((d.batch, d.n_q_heads, d.head_dim), **f32)
+        self.lse_sel = torch.empty((d.batch, d.n_q_heads), **f32)
+        self.delta = torch.empty((d.batch, d.n_q_heads), **f32)
+        self.tau = torch.empty((d.batch, d.n_q_heads), **f32)
+        self.reuse_ok = torch.empty((d.batch, d.n_q_heads), **i32)
+        ws = max(P.prhs_workspace_bytes(d, P.PRHS_OP_SCORE),
+                 P.prhs_workspace_bytes(d, P.PRHS_OP_DECODE, cap))
+        self.ws = torch.empty(((ws + 15) // 16 * 16,), dtype=torch.uint8, device=dev)
+
+    def score(self, q, K, stream=None):
+        P.prhs_score(self.dims, q, K, self.scores, self.lse_all, self.ws, stream=stream)
+
+    def select(self, mode, n_budget, delta_target=0.0, stream=None):
+        P.prhs_select_topk(self.dims, self.scores, self.lse_all, mode, n_budget, delta_target,
+                           self.idx, self.cap, self.count, self.cap_hit, stream=stream)
+
+    def decode(self, q, K, V, use_scores=True, idx=None, count=None, cap=None, stream=None):
+        idx = self.idx if idx is None else idx
+        count = self.count if count is None else count
+        cap = self.cap if cap is None else cap
+        P.prhs_sparse_decode(self.dims, q, K, V, idx, cap, count,
+                             self.scores if use_scores else None,
+                             self.lse_all if use_scores else None, self.out, self.lse_sel,
+                             self.delta if use_scores else None, self.tau if use_scores else None,
+                             self.ws, stream=stream)
+
+    def topn_step(self, q, K, V, N, stream=None):
+        """Anchor step: exact top-N over fresh scores, then attention over it."""
+        self.score(q, K, stream)
+        self.select(P.PRHS_TOPN, N, stream=stream)
+        self.decode(q, K, V, True, stream=stream)
+
+    def delta_step(self, q, K, V, cap, delta_target, stream=None):
+        """Smallest set with dropped mass <= delta_target (capped), then attention."""
+        self.score(q, K, stream)
+        self.select(P.PRHS_DELTA, cap, delta_target, stream=stream)
+        self.decode(q, K, V, True, stream=stream)
+
+    def reuse_step(self, q, K, V, anchor_idx, anchor_count, anchor_cap, radius,
+                   q_anchor=None, sim_tau=0.0, stream=None):
+        """CIS reuse step: dilate the anchor's set, then attend with gathered K and V rows."""
+        P.prhs_cis_reuse(self.dims, anchor_idx, anchor_cap, anchor_count, radius,
+                         q if q_anchor is not None else None, q_anchor, sim_tau, self.idx, self.cap,
+                         self.count, self.reuse_ok if q_anchor is not None else None, stream=stream)
+        self.decode(q, K, V, use_scores=False, stream=stream)
+
+    def dropped_mass(self, stream=None):
+        P.prhs_dropped_mass(self.dims, self.lse_sel, self.lse_all, self.delta, self.tau, stream=stream)

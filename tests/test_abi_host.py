@@ -1,0 +1,183 @@
+"""The C-ABI library loads, exports every symbol prhs.h declares, and rejects
+invalid arguments on the host before any HIP call (CPU only: every call here
+fails validation, so nothing is ever launched)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_top_kv_head_amd import prhs as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prhs.h")
+
+FAKE = 0x100000          # 16-byte aligned, never dereferenced: every call below is invalid
+FAKE_MIS = 0x100008      # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(P._LIB_PATH):
+        from sparse_top_kv_head_amd import build
+        build.build()
+    return P.lib()
+
+
+def _dims(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, ctx_len=1000, dtype=P.PRHS_F16,
+                kv_stride_b=2 * 1000 * 128, kv_stride_h=1000 * 128, kv_stride_t=128, scores_ld=1000)
+    base.update(kw)
+    return P.PrhsDims(**base)
+
+
+def test_header_symbols_are_exported(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(prhs_\w+)\s*\(", text, re.M))
+    assert declared == set(P.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert P.PRHS_MAX_SELECT_CTX == int(re.search(r"PRHS_MAX_SELECT_CTX\s+(\d+)", text).group(1))
+    for const, value in re.findall(r"^\s*(PRHS_\w+)\s*=\s*(-?\d+)", text, re.M):
+        assert getattr(P, const) == int(value), const
+
+
+def _score(L, d, q=FAKE, k=FAKE, s=FAKE, lse=None, ws=None, wsb=0):
+    return L.prhs_score(ctypes.byref(d) if d is not None else None, q, k, s, lse, ws, wsb, None)
+
+
+def _select(L, d, scores=FAKE, lse=FAKE, mode=P.PRHS_TOPN, n=64, dt=0.05, idx=FAKE, cap=64, cnt=FAKE):
+    return L.prhs_select_topk(ctypes.byref(d) if d is not None else None, scores, lse, mode, n, dt,
+                              idx, cap, cnt, None, None)
+
+
+def _cis(L, d, a=FAKE, acap=64, acnt=FAKE, r=2, qc=None, qa=None, tau=0.8, o=FAKE, ocap=320,
+         ocnt=FAKE, ok=None):
+    return L.prhs_cis_reuse(ctypes.byref(d) if d is not None else None, a, acap, acnt, r, qc, qa,
+                            tau, o, ocap, ocnt, ok, None)
+
+
+def _decode(L, d, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cap=64, cnt=FAKE, s=FAKE, lse=FAKE, out=FAKE,
+            lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_sparse_decode(ctypes.byref(d) if d is not None else None, q, k, v, idx, cap, cnt,
+                                s, lse, out, lsel, dl, tau, ws, wsb, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("n_q_heads", 7, P.PRHS_E_DIMS),
+    ("n_kv_heads", 0, P.PRHS_E_DIMS),
+    ("batch", 0, P.PRHS_E_DIMS),
+    ("batch", 10000, P.PRHS_E_DIMS),
+    ("head_dim", 96, P.PRHS_E_DIMS),
+    ("ctx_len", 0, P.PRHS_E_DIMS),
+    ("dtype", 7, P.PRHS_E_DTYPE),
+    ("kv_stride_t", 64, P.PRHS_E_DIMS),
+    ("kv_stride_t", 132, P.PRHS_E_ALIGN),
+    ("kv_stride_h", -128, P.PRHS_E_DIMS),
+    ("kv_stride_b", 4, P.PRHS_E_ALIGN),
+    ("scores_ld", 999, P.PRHS_E_DIMS),
+    ("scores_ld", 1002, P.PRHS_E_ALIGN),
+])
+def test_bad_dims_rejected_by_every_call(L, field, value, code):
+    d = _dims(**{field: value})
+    assert _score(L, d) == code
+    assert _select(L, d) == code
+    assert _cis(L, d) == code
+    assert _decode(L, d) == code
+    assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == code
+    assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0) == 0
+    assert L.prhs_last_error()
+
+
+def test_null_dims(L):
+    assert _score(L, None) == P.PRHS_E_NULL
+    assert _select(L, None) == P.PRHS_E_NULL
+    assert _cis(L, None) == P.PRHS_E_NULL
+    assert _decode(L, None) == P.PRHS_E_NULL
+    assert L.prhs_dropped_mass(None, FAKE, FAKE, FAKE, None, None) == P.PRHS_E_NULL
+
+
+def test_score_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0)
+    assert need == 2 * 8 * 1 * 8          # B*H_q*chunks*(max, sum)
+    assert _score(L, d, q=None) == P.PRHS_E_NULL
+    assert _score(L, d, k=None) == P.PRHS_E_NULL
+    assert _score(L, d, s=None) == P.PRHS_E_NULL
+    assert _score(L, d, q=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert _score(L, d, s=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert _score(L, d, lse=FAKE, ws=None) == P.PRHS_E_WORKSPACE
+    assert _score(L, d, lse=FAKE, ws=FAKE, wsb=need - 1) == P.PRHS_E_WORKSPACE
+    assert _score(L, d, lse=FAKE, ws=FAKE_MIS, wsb=need) == P.PRHS_E_ALIGN
+
+
+def test_select_argument_checks(L):
+    d = _dims()
+    assert _select(L, _dims(ctx_len=P.PRHS_MAX_SELECT_CTX + 1, scores_ld=P.PRHS_MAX_SELECT_CTX + 4)) == P.PRHS_E_DIMS
+    assert _select(L, d, scores=None) == P.PRHS_E_NULL
+    assert _select(L, d, idx=None) == P.PRHS_E_NULL
+    assert _select(L, d, cnt=None) == P.PRHS_E_NULL
+    assert _select(L, d, mode=5) == P.PRHS_E_BUDGET
+    assert _select(L, d, mode=P.PRHS_DELTA, lse=None) == P.PRHS_E_NULL
+    assert _select(L, d, n=0) == P.PRHS_E_BUDGET
+    assert _select(L, d, n=1001, cap=2000) == P.PRHS_E_BUDGET
+    assert _select(L, d, n=65, cap=64) == P.PRHS_E_CAPACITY
+    for bad in (-0.1, 1.5, math.nan):
+        assert _select(L, d, mode=P.PRHS_DELTA, dt=bad) == P.PRHS_E_BUDGET
+    assert _select(L, d, scores=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SELECT, 0) == 0
+
+
+def test_cis_argument_checks(L):
+    d = _dims()
+    assert _cis(L, d, a=None) == P.PRHS_E_NULL
+    assert _cis(L, d, acnt=None) == P.PRHS_E_NULL
+    assert _cis(L, d, o=None) == P.PRHS_E_NULL
+    assert _cis(L, d, ocnt=None) == P.PRHS_E_NULL
+    assert _cis(L, d, r=-1) == P.PRHS_E_BUDGET
+    assert _cis(L, d, acap=0) == P.PRHS_E_CAPACITY
+    assert _cis(L, d, ocap=319) == P.PRHS_E_CAPACITY          # (2r+1)*64 = 320 < t
+    assert _cis(L, d, r=100, ocap=999) == P.PRHS_E_CAPACITY   # min(t, ...) = 1000
+    assert _cis(L, d, ok=FAKE) == P.PRHS_E_NULL
+    assert _cis(L, d, ok=FAKE, qc=FAKE, qa=FAKE, tau=math.nan) == P.PRHS_E_BUDGET
+
+
+def test_decode_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DECODE, 600)
+    assert need == 2 * 8 * 3 * (128 + 2) * 4     # B*H_q*ceil(600/256)*(d+2) floats
+    assert _decode(L, d, v=None) == P.PRHS_E_NULL
+    assert _decode(L, d, idx=None) == P.PRHS_E_NULL
+    assert _decode(L, d, cnt=None) == P.PRHS_E_NULL
+    assert _decode(L, d, out=None) == P.PRHS_E_NULL
+    assert _decode(L, d, lsel=None) == P.PRHS_E_NULL
+    assert _decode(L, d, s=None, k=None) == P.PRHS_E_NULL
+    assert _decode(L, d, s=None, q=None) == P.PRHS_E_NULL
+    assert _decode(L, d, lse=None) == P.PRHS_E_NULL              # delta without lse_all
+    assert _decode(L, d, dl=None) == P.PRHS_E_NULL               # tau without delta
+    assert _decode(L, d, cap=0) == P.PRHS_E_CAPACITY
+    assert _decode(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _decode(L, d, cap=600, wsb=need - 4) == P.PRHS_E_WORKSPACE
+    assert _decode(L, d, v=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, None, None, None) == P.PRHS_E_NULL
+    assert L.prhs_dropped_mass(ctypes.byref(d), None, FAKE, FAKE, None, None) == P.PRHS_E_NULL
+
+
+def test_status_strings(L):
+    codes = [P.PRHS_OK, P.PRHS_E_NULL, P.PRHS_E_DIMS, P.PRHS_E_DTYPE, P.PRHS_E_BUDGET,
+             P.PRHS_E_CAPACITY, P.PRHS_E_WORKSPACE, P.PRHS_E_HIP, P.PRHS_E_ALIGN]
+    texts = [L.prhs_status_string(c) for c in codes]
+    assert len(set(texts)) == len(codes)
+    assert L.prhs_status_string(-99) == b"unknown status"
+
+
+def test_python_binding_raises(L):
+    d = _dims()
+    with pytest.raises(P.PrhsError) as e:
+        P.prhs_select_topk(d, FAKE, FAKE, P.PRHS_TOPN, 0, 0.0, FAKE, 64, FAKE, stream=0)
+    assert e.value.code == P.PRHS_E_BUDGET
+    assert "n_budget" in str(e.value)
