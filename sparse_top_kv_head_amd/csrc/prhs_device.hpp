@@ -128,6 +128,22 @@ __device__ __forceinline__ void wave_ml(float& m, float& l) {
   }
 }
 
+// Inclusive prefix sum of 32-bit values over the 64 lanes of a wave, with DPP
+// row shifts inside each 16-lane row and row broadcasts across rows.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lane_read(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 template <typename U>
 __device__ __forceinline__ U wave_inclusive_scan(U x) {

@@ -4,19 +4,32 @@
 // the dropped mass delta before attention).
 //
 // One 1024-thread workgroup per (b, h). The head's t scores are held in
-// registers as order-preserving 32-bit keys, KPT consecutive keys per thread.
-// A three-pass most-significant-digit radix search (11 + 11 + 10 bits) over
-// LDS histograms finds the exact boundary key T; later passes histogram only
-// the keys still matching the boundary prefix. The result set is every key
-// above T plus the lowest-index keys equal to T, written in ascending index
-// order through one workgroup prefix sum.
+// registers as order-preserving 32-bit keys: each wave owns a contiguous
+// range of 64*KPT keys, loaded with coalesced 16-byte loads, lane l holding
+// granules of 4 consecutive keys at stride 256.
 //
-// DELTA mode runs the same search on attention mass instead of counts: each
-// histogram bin also sums the dense weights exp(s - lse) in 2^-40 fixed point,
-// and the search walks up from the smallest keys to the first position whose
-// suffix mass exceeds the target. That gives the smallest N whose dropped mass
-// is within the target; when it exceeds the cap, a count search for the cap
-// follows.
+// TOPN: a 1-in-8 sample of the keys is histogrammed on its top 11 bits to
+// pick a threshold theta that at least N keys clear with a wide margin. The
+// keys >= theta (a few thousand) are compacted with their indices into an LDS
+// list, and the exact N-th largest key T is found by a radix search over that
+// list with 12-bit digits of key - theta (two passes for a typical range). One
+// wave locates the boundary bin of each pass while the others wait at the
+// barrier. If the sample misleads (fewer than N keys clear theta, or too many
+// for the list), a full radix search over the register keys runs instead:
+// 11 + 11 + 10-bit passes, the first adding into kRep1 copies of the
+// histogram (lane l into copy l % kRep1) because most keys land in a few
+// crowded bins, the later ones over the boundary bin's keys compacted to LDS.
+//
+// The result is every key above T plus the lowest-index keys equal to T. The
+// keys are marked in two LDS bitmaps (above T, equal to T) indexed by key
+// position; one workgroup scan over the bitmap words then gives each thread
+// its output offset, and the indices are written in ascending order.
+//
+// DELTA mode runs the full search on attention mass: each bin also sums the
+// dense weights exp(s - lse) in 2^-40 fixed point and the search walks up
+// from the smallest keys to the first position whose suffix mass exceeds the
+// target. That gives the smallest N whose dropped mass is within the target;
+// when it exceeds the cap, a count search for the cap follows.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
@@ -25,15 +38,17 @@
 namespace prhs {
 namespace {
 
-constexpr int kSelThreads = 1024;
 constexpr int kBins = 2048;
+constexpr int kRep1 = 4;                 // copies of the first-pass count histogram
+constexpr int kCandCap = 8192;           // boundary-bin keys kept in LDS
+constexpr int kMaxWords = PRHS_MAX_SELECT_CTX / 32;
 constexpr double kMassScale = 1099511627776.0;  // 2^40
 
 struct Pass {
   int shift;
   int bits;
 };
-__constant__ Pass kPasses[3] = {{21, 11}, {10, 11}, {0, 10}};
+constexpr Pass kPasses[3] = {{21, 11}, {10, 11}, {0, 10}};
 
 __device__ __forceinline__ float key_to_score(uint32_t key) {
   const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
@@ -45,254 +60,651 @@ __device__ __forceinline__ unsigned long long mass_fx(uint32_t key, float lse) {
   return (unsigned long long)__builtin_fmaf(a, (float)kMassScale, 0.5f);
 }
 
+// Register-resident keys of one thread. Key j = v*GR + e sits at index
+// w*64*KPT + v*64*GR + lane*GR + e (wave w, lane `lane`).
 template <int KPT>
 struct Keys {
+  static constexpr int GR = KPT >= 4 ? 4 : KPT;
+  static constexpr int NV = KPT / GR;
   uint32_t k[KPT];
+  unsigned long long valid;
 };
 
-// Histogram pass over keys matching (pre, pmask); bins of `bits` bits at `shift`.
-template <int KPT, bool MASS>
-__device__ __forceinline__ void histogram(const Keys<KPT>& K, int nvalid, uint32_t pre,
-                                          uint32_t pmask, int shift, int bits, float lse,
-                                          uint32_t* hist, unsigned long long* mhist) {
-  for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
-    hist[i] = 0;
-    if constexpr (MASS) mhist[i] = 0;
-  }
-  __syncthreads();
-  const uint32_t dmask = (1u << bits) - 1u;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t key = K.k[j];
-    if (j < nvalid && (key & pmask) == pre) {
-      const uint32_t dig = (key >> shift) & dmask;
-      atomicAdd(&hist[dig], 1u);
-      if constexpr (MASS) atomicAdd(&mhist[dig], mass_fx(key, lse));
-    }
-  }
-  __syncthreads();
+template <int KPT>
+__device__ __forceinline__ int key_index(int w, int lane, int j) {
+  constexpr int GR = Keys<KPT>::GR;
+  return w * kWave * KPT + (j / GR) * kWave * GR + lane * GR + (j % GR);
 }
 
+template <int NT, bool MASS>
 struct SelShared {
-  uint32_t hist[kBins];
-  unsigned long long scan64[kSelThreads / kWave];
-  uint32_t scan32[kSelThreads / kWave];
+  uint32_t hist[kBins * kRep1];
+  typename std::conditional<MASS, unsigned long long[kBins], char>::type mhist;
+  uint2 cand[kCandCap + kWave];   // (key, index) of the fast path; key only otherwise; + dummies
+  uint32_t gt_bits[kMaxWords];
+  uint32_t eq_bits[kMaxWords];
+  uint32_t wtot[NT / kWave];
+  uint32_t wtot2[NT / kWave];
+  unsigned long long wmass[NT / kWave];
+  uint32_t ncand;                 // fast-path list length
+  uint32_t ncand_r;               // register-path list length
+  uint32_t kmax;
   uint32_t digit;
   uint32_t above;
-  unsigned long long below;
+  uint32_t cT;
   int found;
+  unsigned long long below;
+  unsigned long long mT;
 };
 
-struct DeltaShared {
-  unsigned long long mhist[kBins];
-};
-
-// Count search: the krem-th largest key among the keys matching the prefix.
-// On return pre holds the boundary key T and krem how many keys equal to T
-// are taken.
-template <int KPT>
-__device__ __forceinline__ void count_search(const Keys<KPT>& K, int nvalid, uint32_t& pre, uint32_t& pmask,
-                             uint32_t& krem, int first_pass, SelShared& sh) {
-  for (int p = first_pass; p < 3; ++p) {
-    const int shift = kPasses[p].shift, bits = kPasses[p].bits;
-    const int nb = 1 << bits;
-    histogram<KPT, false>(K, nvalid, pre, pmask, shift, bits, 0.f, sh.hist, nullptr);
-    // Bins in descending order: thread i owns bins nb-1-2i and nb-2-2i.
-    const int hi = nb - 1 - 2 * (int)threadIdx.x;
-    const uint32_t c1 = hi >= 0 ? sh.hist[hi] : 0u;
-    const uint32_t c0 = hi >= 1 ? sh.hist[hi - 1] : 0u;
-    const uint32_t cnt = c1 + c0;
-    uint32_t total;
-    const uint32_t excl = block_exclusive_scan<kSelThreads>(cnt, sh.scan32, total);
-    if (cnt > 0 && excl < krem && krem <= excl + cnt) {
-      if (excl + c1 >= krem) {
-        sh.digit = (uint32_t)hi;
-        sh.above = excl;
-      } else {
-        sh.digit = (uint32_t)(hi - 1);
-        sh.above = excl + c1;
-      }
-    }
-    __syncthreads();
-    krem -= sh.above;
-    pre |= sh.digit << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-  }
+__device__ __forceinline__ int hist_slot(int p, uint32_t dig, int lane) {
+  return p == 0 ? (int)dig * kRep1 + (lane & (kRep1 - 1)) : (int)dig;
 }
 
-// Mass search (DELTA): the first key, walking up from the smallest, whose
-// suffix mass (itself and everything ranked below it) exceeds the remaining
-// budget. Returns false when the whole set's mass is within the budget.
-template <int KPT>
-__device__ __forceinline__ bool mass_search(const Keys<KPT>& K, int nvalid, float lse, unsigned long long budget,
-                            uint32_t& pre, uint32_t& pmask, uint32_t& above_total,
-                            unsigned long long& drem, SelShared& sh, DeltaShared& dsh) {
-  drem = budget;
-  above_total = 0;
-  for (int p = 0; p < 3; ++p) {
-    const int shift = kPasses[p].shift, bits = kPasses[p].bits;
-    const int nb = 1 << bits;
-    histogram<KPT, true>(K, nvalid, pre, pmask, shift, bits, lse, sh.hist, dsh.mhist);
-    // Bins in ascending order: thread i owns bins 2i and 2i+1.
-    const int lo = 2 * (int)threadIdx.x;
-    const uint32_t c0 = lo < nb ? sh.hist[lo] : 0u;
-    const uint32_t c1 = lo + 1 < nb ? sh.hist[lo + 1] : 0u;
-    const unsigned long long m0 = lo < nb ? dsh.mhist[lo] : 0ull;
-    const unsigned long long m1 = lo + 1 < nb ? dsh.mhist[lo + 1] : 0ull;
-    unsigned long long mtot;
-    const unsigned long long mex = block_exclusive_scan<kSelThreads>(m0 + m1, sh.scan64, mtot);
-    uint32_t ctot;
-    const uint32_t cex = block_exclusive_scan<kSelThreads>(c0 + c1, sh.scan32, ctot);
-    if (threadIdx.x == 0) sh.found = 0;
-    __syncthreads();
-    if (mex <= drem && drem < mex + m0 + m1) {
-      sh.found = 1;
-      if (mex + m0 > drem) {
-        sh.digit = (uint32_t)lo;
-        sh.below = mex;
-        sh.above = ctot - (cex + c0);
-      } else {
-        sh.digit = (uint32_t)(lo + 1);
-        sh.below = mex + m0;
-        sh.above = ctot - (cex + c0 + c1);
+// Read a bin's count (summing the copies of the first pass) and clear it.
+__device__ __forceinline__ uint32_t take_bin(uint32_t* hist, int p, int b) {
+  if (p == 0) {
+    uint4* q = reinterpret_cast<uint4*>(hist + b * kRep1);
+    const uint4 a = *q;
+    *q = make_uint4(0, 0, 0, 0);
+    return a.x + a.y + a.z + a.w;
+  }
+  const uint32_t c = hist[b];
+  hist[b] = 0;
+  return c;
+}
+
+// Atomics of pass p over the keys matching (pre, pmask), taken from the
+// registers (FROM_LDS false) or from the compacted candidate list.
+template <int KPT, int NT, bool MASS, bool FROM_LDS>
+__device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pre, uint32_t pmask,
+                                          float lse, SelShared<NT, MASS>& sh) {
+  const int shift = kPasses[p].shift;
+  const uint32_t dmask = (1u << kPasses[p].bits) - 1u;
+  const int lane = threadIdx.x & (kWave - 1);
+  if constexpr (FROM_LDS) {
+    const int n = (int)sh.ncand_r;
+    for (int c = threadIdx.x; c < n; c += NT) {
+      const uint32_t key = sh.cand[c].x;
+      if ((key & pmask) == pre) {
+        const uint32_t dig = (key >> shift) & dmask;
+        atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
+        if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
       }
     }
-    __syncthreads();
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t key = K.k[j];
+      if (((K.valid >> j) & 1ull) && (key & pmask) == pre) {
+        const uint32_t dig = (key >> shift) & dmask;
+        atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
+        if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Locate the bin holding the krem-th largest key of pass p (bins in
+// descending order; thread i owns bins nb-1-(BPT*i+k)). Clears the bins.
+template <int NT, bool MASS>
+__device__ __forceinline__ void find_count(int p, uint32_t krem, SelShared<NT, MASS>& sh) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kBins / NT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nb = 1 << kPasses[p].bits;
+  uint32_t c[BPT];
+  uint32_t local = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int b = nb - 1 - (BPT * (int)threadIdx.x + k);
+    c[k] = b >= 0 ? take_bin(sh.hist, p, b) : 0u;
+    local += c[k];
+  }
+  if constexpr (MASS) {
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int b = nb - 1 - (BPT * (int)threadIdx.x + k);
+      if (b >= 0) sh.mhist[b] = 0;
+    }
+  }
+  const uint32_t incl = wave_scan_u32(local);
+  if (lane == kWave - 1) sh.wtot[w] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  int wb = NW;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const uint32_t x = sh.wtot[u];
+    if (wb == NW) {
+      if (before + x >= krem) wb = u;
+      else before += x;
+    }
+  }
+  if (w == wb) {
+    uint32_t acc = before + incl - local;
+    if (acc < krem && krem <= acc + local) {
+#pragma unroll
+      for (int k = 0; k < BPT; ++k) {
+        if (acc < krem && krem <= acc + c[k]) {
+          sh.digit = (uint32_t)(nb - 1 - (BPT * (int)threadIdx.x + k));
+          sh.above = acc;
+          sh.cT = c[k];
+        }
+        acc += c[k];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Locate the bin, walking up from the smallest keys, where the suffix mass
+// first exceeds drem (bins ascending; thread i owns bins BPT*i+k). Clears
+// the bins. sh.found = 0 when the whole region's mass is within drem.
+template <int NT>
+__device__ __forceinline__ void find_mass(int p, unsigned long long drem, SelShared<NT, true>& sh) {
+  constexpr int NW = NT / kWave;
+  constexpr int BPT = kBins / NT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nb = 1 << kPasses[p].bits;
+  uint32_t c[BPT];
+  unsigned long long m[BPT];
+  uint32_t lc = 0;
+  unsigned long long lm = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int b = BPT * (int)threadIdx.x + k;
+    c[k] = b < nb ? take_bin(sh.hist, p, b) : 0u;
+    m[k] = 0;
+    if (b < nb) {
+      m[k] = sh.mhist[b];
+      sh.mhist[b] = 0;
+    }
+    lc += c[k];
+    lm += m[k];
+  }
+  const uint32_t cinc = wave_scan_u32(lc);
+  const unsigned long long minc = wave_inclusive_scan(lm);
+  if (lane == kWave - 1) {
+    sh.wtot[w] = cinc;
+    sh.wmass[w] = minc;
+  }
+  if (threadIdx.x == 0) sh.found = 0;
+  __syncthreads();
+  unsigned long long mbefore = 0;
+  uint32_t cbefore = 0, ctot = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    ctot += sh.wtot[u];
+    if (u < w) {
+      mbefore += sh.wmass[u];
+      cbefore += sh.wtot[u];
+    }
+  }
+  unsigned long long mex = mbefore + minc - lm;
+  uint32_t cex = cbefore + cinc - lc;
+  if (mex <= drem && drem < mex + lm) {
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      if (mex <= drem && drem < mex + m[k]) {
+        sh.found = 1;
+        sh.digit = (uint32_t)(BPT * (int)threadIdx.x + k);
+        sh.below = mex;
+        sh.above = ctot - (cex + c[k]);
+        sh.cT = c[k];
+        sh.mT = m[k];
+      }
+      mex += m[k];
+      cex += c[k];
+    }
+  }
+  __syncthreads();
+}
+
+// Copy the register keys matching (pre, pmask) into the LDS candidate list.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ void compact(const Keys<KPT>& K, uint32_t pre, uint32_t pmask,
+                                        SelShared<NT, MASS>& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned long long hit = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (((K.valid >> j) & 1ull) && (K.k[j] & pmask) == pre) hit |= 1ull << j;
+  const uint32_t cnt = (uint32_t)__popcll(hit);
+  const uint32_t incl = wave_scan_u32(cnt);
+  const uint32_t wtotal = lane_read(incl, kWave - 1);
+  uint32_t base = 0;
+  if (lane == 0 && wtotal) base = atomicAdd(&sh.ncand_r, wtotal);
+  base = lane_read(base, 0);
+  uint32_t pos = base + incl - cnt;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((hit >> j) & 1ull) sh.cand[pos++].x = K.k[j];
+  __syncthreads();
+}
+
+// Exact boundary of the krem-th largest key. Returns T; krem becomes the
+// number of keys equal to T that are taken.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ uint32_t count_search(const Keys<KPT>& K, uint32_t& krem,
+                                                 SelShared<NT, MASS>& sh) {
+  uint32_t pre = 0, pmask = 0;
+  if (threadIdx.x == 0) sh.ncand_r = 0;
+  hist_pass<KPT, NT, MASS, false>(K, 0, pre, pmask, 0.f, sh);
+  find_count<NT, MASS>(0, krem, sh);
+  krem -= sh.above;
+  pre = sh.digit << kPasses[0].shift;
+  pmask = (uint32_t)(kBins - 1) << kPasses[0].shift;
+  const bool lds = sh.cT <= (uint32_t)kCandCap;
+  if (lds) compact<KPT, NT, MASS>(K, pre, pmask, sh);
+#pragma unroll 1
+  for (int p = 1; p < 3; ++p) {
+    if (lds) hist_pass<KPT, NT, MASS, true>(K, p, pre, pmask, 0.f, sh);
+    else hist_pass<KPT, NT, MASS, false>(K, p, pre, pmask, 0.f, sh);
+    find_count<NT, MASS>(p, krem, sh);
+    krem -= sh.above;
+    pre |= sh.digit << kPasses[p].shift;
+    pmask |= (uint32_t)((1 << kPasses[p].bits) - 1) << kPasses[p].shift;
+  }
+  return pre;
+}
+
+// Mass search (DELTA): the boundary key T where the suffix mass (a key and
+// everything ranked below it) first exceeds the budget, walking up from the
+// smallest key. Returns false when the total mass is within the budget.
+// Otherwise n_above is the number of keys above T and take_T the number of
+// keys equal to T that are taken.
+template <int KPT, int NT>
+__device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse,
+                                            unsigned long long budget, uint32_t& T,
+                                            uint32_t& n_above, uint32_t& take_T,
+                                            SelShared<NT, true>& sh) {
+  uint32_t pre = 0, pmask = 0;
+  unsigned long long drem = budget;
+  n_above = 0;
+  bool lds = false;
+  if (threadIdx.x == 0) sh.ncand_r = 0;
+#pragma unroll 1
+  for (int p = 0; p < 3; ++p) {
+    if (p == 0) hist_pass<KPT, NT, true, false>(K, 0, pre, pmask, lse, sh);
+    else if (lds) hist_pass<KPT, NT, true, true>(K, p, pre, pmask, lse, sh);
+    else hist_pass<KPT, NT, true, false>(K, p, pre, pmask, lse, sh);
+    find_mass<NT>(p, drem, sh);
     if (!sh.found) return false;
     drem -= sh.below;
-    above_total += sh.above;
-    pre |= sh.digit << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    if (p == 2) {
-      // Boundary key T = pre: its c_T keys carry identical mass a each. Keys
-      // of rank j (by index) among them are taken while their suffix mass
-      // (c_T - j + 1) * a exceeds drem.
-      const uint32_t cT = sh.hist[sh.digit];
-      const unsigned long long a = dsh.mhist[sh.digit] / cT;
-      const unsigned long long keep_out = a ? drem / a : (unsigned long long)cT;
-      const uint32_t dropped = keep_out < cT ? (uint32_t)keep_out : cT;
-      above_total += cT - dropped;  // now the total count taken
+    n_above += sh.above;
+    pre |= sh.digit << kPasses[p].shift;
+    pmask |= (uint32_t)((1 << kPasses[p].bits) - 1) << kPasses[p].shift;
+    if (p == 0) {
+      lds = sh.cT <= (uint32_t)kCandCap;
+      if (lds) compact<KPT, NT, true>(K, pre, pmask, sh);
     }
-    __syncthreads();
   }
+  // Boundary key T = pre: its c_T keys carry identical mass a each. The key
+  // of rank j (by index) among them is taken while its suffix mass
+  // (c_T - j + 1) * a exceeds drem.
+  const uint32_t cT = sh.cT;
+  const unsigned long long a = sh.mT / cT;
+  const unsigned long long keep_out = a ? drem / a : (unsigned long long)cT;
+  take_T = cT - (keep_out < cT ? (uint32_t)keep_out : cT);
+  T = pre;
   return true;
 }
 
-// Write the keys above T and the first `take_eq` keys equal to T, ascending.
-template <int KPT>
-__device__ __forceinline__ void emit(const Keys<KPT>& K, int nvalid, int i0, uint32_t T, uint32_t take_eq,
-                     int* __restrict__ out, uint32_t cap, SelShared& sh) {
-  unsigned long long gt = 0, eq = 0;
+// Mark the register keys above T and equal to T in the LDS bitmaps.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ void mark_from_regs(const Keys<KPT>& K, uint32_t T,
+                                               SelShared<NT, MASS>& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    if (j < nvalid) {
-      if (K.k[j] > T) gt |= 1ull << j;
-      else if (K.k[j] == T) eq |= 1ull << j;
+    if ((K.valid >> j) & 1ull) {
+      const int i = key_index<KPT>(w, lane, j);
+      if (K.k[j] > T) atomicOr(&sh.gt_bits[i >> 5], 1u << (i & 31));
+      else if (K.k[j] == T) atomicOr(&sh.eq_bits[i >> 5], 1u << (i & 31));
     }
   }
-  const unsigned long long packed =
-      ((unsigned long long)__popcll(gt) << 32) | (unsigned long long)__popcll(eq);
-  unsigned long long tot;
-  const unsigned long long ex = block_exclusive_scan<kSelThreads>(packed, sh.scan64, tot);
-  const uint32_t ex_gt = (uint32_t)(ex >> 32), ex_eq = (uint32_t)ex;
-  uint32_t eq_take = take_eq > ex_eq ? take_eq - ex_eq : 0u;
-  uint32_t pos = ex_gt + (ex_eq < take_eq ? ex_eq : take_eq);
+  __syncthreads();
+}
+
+// Write the marked keys above T and the first take_eq keys equal to T in
+// ascending index order: thread i owns WPT consecutive bitmap words.
+template <int NT, bool MASS>
+__device__ __forceinline__ void emit_bitmaps(int t, uint32_t take_eq, int* __restrict__ out,
+                                             uint32_t cap, SelShared<NT, MASS>& sh) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nwords = (t + 31) >> 5;
+  constexpr int WPT = (kMaxWords + NT - 1) / NT;
+  uint32_t g[WPT], e[WPT];
+  uint32_t ng = 0, ne = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    bool sel = (gt >> j) & 1ull;
-    if ((eq >> j) & 1ull) {
-      if (eq_take) {
-        sel = true;
-        --eq_take;
-      }
+  for (int q = 0; q < WPT; ++q) {
+    const int wi = (int)threadIdx.x * WPT + q;
+    g[q] = wi < nwords ? sh.gt_bits[wi] : 0u;
+    e[q] = wi < nwords ? sh.eq_bits[wi] : 0u;
+    ng += __popc(g[q]);
+    ne += __popc(e[q]);
+  }
+  const uint32_t ginc = wave_scan_u32(ng);
+  const uint32_t einc = wave_scan_u32(ne);
+  if (lane == kWave - 1) {
+    sh.wtot[w] = ginc;
+    sh.wtot2[w] = einc;
+  }
+  __syncthreads();
+  uint32_t gb = ginc - ng, eb = einc - ne;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    if (u < w) {
+      gb += sh.wtot[u];
+      eb += sh.wtot2[u];
     }
-    if (sel) {
-      if (pos < cap) out[pos] = i0 + j;  // never past the row, whatever the counts
+  }
+  uint32_t pos = gb + (eb < take_eq ? eb : take_eq);
+  uint32_t eq_left = take_eq > eb ? take_eq - eb : 0u;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    uint32_t sel = g[q];
+    uint32_t ew = e[q];
+    while (eq_left && ew) {
+      const uint32_t low = ew & (0u - ew);
+      sel |= low;
+      ew ^= low;
+      --eq_left;
+    }
+    const int base_i = ((int)threadIdx.x * WPT + q) << 5;
+    while (sel) {
+      const int b = __builtin_ctz(sel);
+      sel &= sel - 1;
+      if (pos < cap) out[pos] = base_i + b;
       ++pos;
     }
   }
 }
 
-template <int KPT, int MODE>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+// ---------------------------------------------------------------------------
+// TOPN fast path: sampled threshold, compacted candidates, 12-bit passes.
+// ---------------------------------------------------------------------------
+
+// Histogram layout of the one-wave find: NB bins, REP copies each. Lane l of
+// the finding wave owns bins [NB - (l+1)*BPL, NB - l*BPL); bin b is stored at
+// word ((b % BPL) * 64 + b / BPL) * REP, so that the lanes' k-th bins are
+// adjacent words and every read of the find is free of bank conflicts.
+template <int NB, int REP>
+__device__ __forceinline__ int swz_slot(uint32_t b, int lane) {
+  constexpr int BPL = NB / kWave;
+  return ((int)(b % BPL) * kWave + (int)(b / BPL)) * REP + (REP > 1 ? (lane & (REP - 1)) : 0);
+}
+
+template <int NB, int REP>
+__device__ __forceinline__ uint32_t swz_bin(const uint32_t* hist, int b) {
+  constexpr int BPL = NB / kWave;
+  const int w0 = ((b % BPL) * kWave + b / BPL) * REP;
+  if constexpr (REP == 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(hist + w0);
+    return a.x + a.y + a.z + a.w;
+  } else {
+    return hist[w0];
+  }
+}
+
+// Wave 0 locates, over NB bins taken in descending order, the bin holding the
+// krem-th largest; it clears every bin. The result goes to sh.digit / above /
+// cT (left unchanged when the bins hold fewer than krem keys).
+template <int NB, int REP, int NT, bool MASS>
+__device__ __forceinline__ void find_count_w0(uint32_t krem, SelShared<NT, MASS>& sh) {
+  constexpr int BPL = NB / kWave;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int col = kWave - 1 - lane;  // = b / BPL for this lane's bins
+    uint32_t local = 0;
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int w0 = (k * kWave + col) * REP;
+      if constexpr (REP == 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(sh.hist + w0);
+        local += a.x + a.y + a.z + a.w;
+      } else {
+        local += sh.hist[w0];
+      }
+    }
+    const uint32_t incl = wave_scan_u32(local);
+    const uint32_t excl = incl - local;
+    // the lane whose range crosses krem (at most one), then its bins one per lane
+    const unsigned long long cross = __ballot(excl < krem && krem <= incl);
+    if (cross) {
+      const int L = __builtin_ctzll(cross);
+      const uint32_t baseL = lane_read(excl, L);
+      const int b = NB - (L + 1) * BPL + (BPL - 1 - lane);
+      const uint32_t c = lane < BPL ? swz_bin<NB, REP>(sh.hist, b) : 0u;
+      const uint32_t ce = wave_scan_u32(c) - c + baseL;
+      if (lane < BPL && ce < krem && krem <= ce + c) {
+        sh.digit = (uint32_t)b;
+        sh.above = ce;
+        sh.cT = c;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BPL; ++k) {
+      const int w0 = (k * kWave + col) * REP;
+      if constexpr (REP == 4) *reinterpret_cast<uint4*>(sh.hist + w0) = make_uint4(0, 0, 0, 0);
+      else sh.hist[w0] = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// Try the sampled-threshold path. Returns false (nothing written to the
+// output) when the threshold does not leave between N and kCandCap keys;
+// otherwise T and take_eq describe the result and the bitmaps are marked.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N, uint32_t& T,
+                                          uint32_t& take_eq, SelShared<NT, MASS>& sh) {
+  constexpr int SR = KPT >= 8 ? 8 : 1;  // sample one key in SR
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  uint32_t theta = 0;
+  if (t > kCandCap) {
+    if (threadIdx.x == 0) {
+      sh.digit = 0;
+      sh.ncand = 0;
+      sh.kmax = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; j += SR) {
+      if ((K.valid >> j) & 1ull)
+        atomicAdd(&sh.hist[swz_slot<kBins, kRep1>(K.k[j] >> 21, lane)], 1u);
+    }
+    __syncthreads();
+    // enough sampled keys above the bin edge for N keys with a margin of
+    // about two binomial standard deviations
+    const float ns = (float)N / SR;
+    const uint32_t target = (uint32_t)(ns + 2.f * sqrtf(ns) + 8.f);
+    find_count_w0<kBins, kRep1, NT, MASS>(target, sh);
+    theta = sh.digit << 21;
+  } else {
+    if (threadIdx.x == 0) {
+      sh.ncand = 0;
+      sh.kmax = 0;
+    }
+    __syncthreads();
+  }
+  // compact the keys >= theta with their indices; lanes without a hit write
+  // their own dummy slot past the list, so the loop has no branches
+  using Mask = typename std::conditional<(KPT > 32), unsigned long long, uint32_t>::type;
+  Mask hit = 0;
+  uint32_t kmx = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool h = ((K.valid >> j) & 1ull) && K.k[j] >= theta;
+    hit |= (Mask)h << j;
+    kmx = h && K.k[j] > kmx ? K.k[j] : kmx;
+  }
+  const uint32_t cnt = (uint32_t)__builtin_popcountll(hit);
+  const uint32_t incl = wave_scan_u32(cnt);
+  const uint32_t wtotal = lane_read(incl, kWave - 1);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(kmx, o);
+    kmx = y > kmx ? y : kmx;
+  }
+  uint32_t base = 0;
+  if (lane == 0 && wtotal) {
+    base = atomicAdd(&sh.ncand, wtotal);
+    atomicMax(&sh.kmax, kmx);
+  }
+  base = lane_read(base, 0) + incl - cnt;
+  const uint32_t dummy = (uint32_t)kCandCap + (uint32_t)lane;
+  const int ibase = key_index<KPT>(w, lane, 0);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t pos = base + (uint32_t)__builtin_popcountll(hit & (((Mask)1 << j) - 1));
+    const bool h = (hit >> j) & 1;
+    const uint32_t slot = (h && pos < (uint32_t)kCandCap) ? pos : dummy;
+    sh.cand[slot] = make_uint2(K.k[j], (uint32_t)(ibase + (j / Keys<KPT>::GR) * kWave * Keys<KPT>::GR + (j % Keys<KPT>::GR)));
+  }
+  __syncthreads();
+  const uint32_t C = sh.ncand;
+  if (C < N || C > (uint32_t)kCandCap) return false;
+
+  // exact N-th largest among the candidates: 12-bit digits of key - theta
+  const uint32_t range = sh.kmax - theta;
+  int shift = range ? 32 - __builtin_clz(range) - 12 : 0;
+  shift = shift > 0 ? shift : 0;
+  uint32_t pre = 0, pmask = 0, krem = N;
+#pragma unroll 1
+  while (true) {
+    if (threadIdx.x == 0) sh.digit = 0;
+    for (int c = threadIdx.x; c < (int)C; c += NT) {
+      const uint32_t o = sh.cand[c].x - theta;
+      if ((o & pmask) == pre) atomicAdd(&sh.hist[swz_slot<4096, 1>((o >> shift) & 4095u, 0)], 1u);
+    }
+    __syncthreads();
+    find_count_w0<4096, 1, NT, MASS>(krem, sh);
+    krem -= sh.above;
+    pre |= sh.digit << shift;
+    pmask |= 4095u << shift;
+    if (shift == 0) break;
+    shift = shift > 12 ? shift - 12 : 0;
+  }
+  T = theta + pre;
+  take_eq = krem;
+  // mark the result bits from the candidate list
+  for (int c = threadIdx.x; c < (int)C; c += NT) {
+    const uint2 ki = sh.cand[c];
+    if (ki.x > T) atomicOr(&sh.gt_bits[ki.y >> 5], 1u << (ki.y & 31));
+    else if (ki.x == T) atomicOr(&sh.eq_bits[ki.y >> 5], 1u << (ki.y & 31));
+  }
+  __syncthreads();
+  return true;
+}
+
+// Load the head's scores as keys: wave w owns [w*64*KPT, (w+1)*64*KPT), lane
+// `lane` the granules at w*64*KPT + v*64*GR + lane*GR.
+template <int KPT>
+__device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict__ row, int t) {
+  constexpr int GR = Keys<KPT>::GR, NV = Keys<KPT>::NV;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int base = w * kWave * KPT + lane * GR;
+  if (GR == 4 && (w + 1) * kWave * KPT <= t) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float4 x = *reinterpret_cast<const float4*>(row + base + v * kWave * GR);
+      K.k[GR * v] = score_key(x.x);
+      K.k[GR * v + 1 % GR] = score_key(x.y);
+      K.k[GR * v + 2 % GR] = score_key(x.z);
+      K.k[GR * v + 3 % GR] = score_key(x.w);
+    }
+    K.valid = KPT == 64 ? ~0ull : ((1ull << KPT) - 1ull);
+    return;
+  }
+  K.valid = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int i = base + v * kWave * GR;
+#pragma unroll
+    for (int e = 0; e < GR; ++e) {
+      const bool ok = i + e < t;
+      K.k[v * GR + e] = ok ? score_key(row[i + e]) : 0u;
+      if (ok) K.valid |= 1ull << (v * GR + e);
+    }
+  }
+}
+
+template <int KPT, int NT, int MODE>
+__global__ __launch_bounds__(NT) void select_kernel(
     const float* __restrict__ scores, const float* __restrict__ lse_all, int t, int ld,
     int n_budget, float delta_target, int* __restrict__ idx, int idx_cap,
     int* __restrict__ count, int* __restrict__ cap_hit) {
-  __shared__ SelShared sh;
-  __shared__ typename std::conditional<MODE == PRHS_DELTA, DeltaShared, char>::type dsh_raw;
+  constexpr bool MASS = MODE == PRHS_DELTA;
+  __shared__ SelShared<NT, MASS> sh;
 
   const int head = blockIdx.x;
   const float* row = scores + (size_t)head * ld;
-  const int i0 = threadIdx.x * KPT;
-  const int nvalid = max(0, min(KPT, t - i0));
 
-  Keys<KPT> K;
-  if constexpr (KPT >= 4) {
-#pragma unroll
-    for (int v = 0; v < KPT / 4; ++v) {
-      if (4 * v + 4 <= nvalid) {
-        const float4 x = *reinterpret_cast<const float4*>(row + i0 + 4 * v);
-        K.k[4 * v] = score_key(x.x);
-        K.k[4 * v + 1] = score_key(x.y);
-        K.k[4 * v + 2] = score_key(x.z);
-        K.k[4 * v + 3] = score_key(x.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          K.k[4 * v + e] = (4 * v + e < nvalid) ? score_key(row[i0 + 4 * v + e]) : 0u;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) K.k[j] = (j < nvalid) ? score_key(row[i0 + j]) : 0u;
+  for (int i = threadIdx.x; i < kBins * kRep1; i += NT) sh.hist[i] = 0;
+  if constexpr (MASS)
+    for (int i = threadIdx.x; i < kBins; i += NT) sh.mhist[i] = 0;
+  const int nwords = (t + 31) >> 5;
+  for (int i = threadIdx.x; i < nwords; i += NT) {
+    sh.gt_bits[i] = 0;
+    sh.eq_bits[i] = 0;
   }
 
-  uint32_t pre = 0, pmask = 0, take = 0;
+  Keys<KPT> K;
+  load_keys<KPT>(K, row, t);
+  __syncthreads();
+
+  uint32_t T = 0, take = 0;
   int n_sel = n_budget;
   int hit = 0;
-  if constexpr (MODE == PRHS_DELTA) {
-    DeltaShared& dsh = *reinterpret_cast<DeltaShared*>(&dsh_raw);
+  if constexpr (MASS) {
     const float lse = lse_all[head];
-    const unsigned long long budget =
-        (unsigned long long)((double)delta_target * kMassScale);
-    uint32_t n_delta = 0;
-    unsigned long long drem = 0;
-    const bool found = mass_search<KPT>(K, nvalid, lse, budget, pre, pmask, n_delta, drem, sh, dsh);
-    if (found && (int)n_delta <= n_budget) {
-      n_sel = (int)n_delta;
-      // pre is the boundary key; take the keys above it and enough equal keys.
-      uint32_t above = 0;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) above += (j < nvalid && K.k[j] > pre) ? 1u : 0u;
-      uint32_t tot;
-      (void)block_exclusive_scan<kSelThreads>(above, sh.scan32, tot);
-      take = n_delta - tot;
+    const unsigned long long budget = (unsigned long long)((double)delta_target * kMassScale);
+    uint32_t n_above = 0, take_T = 0;
+    const bool found = mass_search<KPT, NT>(K, lse, budget, T, n_above, take_T, sh);
+    if (found && (int)(n_above + take_T) <= n_budget) {
+      n_sel = (int)(n_above + take_T);
+      take = take_T;
     } else {
       hit = found ? 1 : 0;
       n_sel = found ? n_budget : 1;
-      pre = 0;
-      pmask = 0;
       take = (uint32_t)n_sel;
-      count_search<KPT>(K, nvalid, pre, pmask, take, 0, sh);
+      T = count_search<KPT, NT, MASS>(K, take, sh);
     }
+    mark_from_regs<KPT, NT, MASS>(K, T, sh);
   } else {
-    take = (uint32_t)n_budget;
-    count_search<KPT>(K, nvalid, pre, pmask, take, 0, sh);
+    if (!topn_fast<KPT, NT, MASS>(K, t, (uint32_t)n_budget, T, take, sh)) {
+      load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die
+      take = (uint32_t)n_budget;
+      T = count_search<KPT, NT, MASS>(K, take, sh);
+      mark_from_regs<KPT, NT, MASS>(K, T, sh);
+    }
   }
-  emit<KPT>(K, nvalid, i0, pre, take, idx + (size_t)head * idx_cap, (uint32_t)idx_cap, sh);
+  emit_bitmaps<NT, MASS>(t, take, idx + (size_t)head * idx_cap, (uint32_t)idx_cap, sh);
   if (threadIdx.x == 0) {
     count[head] = n_sel;
     if (cap_hit) cap_hit[head] = hit;
   }
 }
 
+constexpr int kSelThreads = 1024;
+
 template <int MODE>
 void launch_mode(int kpt, int nheads, const float* scores, const float* lse_all, int t, int ld,
                  int n_budget, float delta_target, int* idx, int idx_cap, int* count, int* cap_hit,
                  hipStream_t stream) {
-#define PRHS_SEL(K)                                                                            \
-  hipLaunchKernelGGL((select_kernel<K, MODE>), dim3(nheads), dim3(kSelThreads), 0, stream, scores, \
-                     lse_all, t, ld, n_budget, delta_target, idx, idx_cap, count, cap_hit)
+#define PRHS_SEL(K)                                                                          \
+  hipLaunchKernelGGL((select_kernel<K, kSelThreads, MODE>), dim3(nheads), dim3(kSelThreads), 0, \
+                     stream, scores, lse_all, t, ld, n_budget, delta_target, idx, idx_cap, count, \
+                     cap_hit)
   switch (kpt) {
     case 1: PRHS_SEL(1); break;
     case 2: PRHS_SEL(2); break;
