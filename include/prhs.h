@@ -68,7 +68,7 @@ enum { PRHS_F32 = 0, PRHS_F16 = 1 };
 enum { PRHS_TOPN = 0, PRHS_DELTA = 1 };
 
 /* Operations for prhs_workspace_bytes. */
-enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2 };
+enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2, PRHS_OP_ANCHOR_STEP = 3 };
 
 /* Largest context length the selection kernel keeps resident on chip. */
 #define PRHS_MAX_SELECT_CTX 65536
@@ -170,6 +170,26 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                        hipStream_t stream);
 
 /*
+ * prhs_anchor_step -- one exact-retrieval decode step in a single call: the
+ * score scan, the selection (TOPN or DELTA, as prhs_select_topk) and the
+ * sparse decode with the fused dropped mass, enqueued back to back on
+ * `stream` (Fig. 4: the query whose critical set is computed exactly; the
+ * Abstract: selection ahead of attention with the dropped mass controlled).
+ *
+ * Results are those of the three calls in sequence: scores, lse_all, idx,
+ * count, cap_hit (nullable), out, lse_sel, delta and tau (nullable; tau
+ * needs delta). The dense log-sum-exp is merged inside the selection kernel
+ * from the scan's per-chunk partials, so no separate merge runs. Argument
+ * rules are the union of the three calls' rules.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_ANCHOR_STEP, idx_cap) bytes.
+ */
+int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,
+                     const void* q, const void* k, const void* v, float* scores, float* lse_all,
+                     int32_t* idx, int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* out,
+                     float* lse_sel, float* delta, float* tau, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
  * prhs_dropped_mass -- dropped and retained attention mass of the selected
  * sets (Table I: delta(.), tau(.)):
  *   delta = clamp(-expm1(lse_sel - lse_all), 0, 1),  tau = 1 - delta.
@@ -179,8 +199,8 @@ int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* 
                       float* delta, float* tau, hipStream_t stream);
 
 /* Workspace bytes needed by `op` (PRHS_OP_*) for these dims; `cap` is the
- * idx_cap of prhs_sparse_decode and is ignored otherwise. Returns 0 for
- * invalid dims. */
+ * idx_cap of prhs_sparse_decode / prhs_anchor_step and is ignored otherwise.
+ * Returns 0 for invalid dims. */
 size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap);
 
 /* Static text for a status code. */

@@ -150,6 +150,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 }
 
+// Merge the split partials of one head: thread `col` owns one output column.
+// Splits are taken eight at a time with all their loads issued together, so
+// the merge costs about one memory round trip per eight splits.
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part, int nsplit,
                                                          float* __restrict__ out,
@@ -160,18 +163,39 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   const int head = blockIdx.x;
   const int col = threadIdx.x;
   const float* p = part + (size_t)head * nsplit * (D + 2);
-  float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p[(size_t)s * (D + 2) + D]);
-  float l = 0.f, o = 0.f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = p + (size_t)s * (D + 2);
-      const float ms = ps[D];
-      if (ms == -INFINITY) continue;
-      const float f = __expf(ms - m);
-      l += ps[D + 1] * f;
-      o += ps[col] * f;
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float ms[8], ls[8], os[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = s0 + i;
+      if (s < nsplit) {
+        const float* ps = p + (size_t)s * (D + 2);
+        ms[i] = ps[D];
+        ls[i] = ps[D + 1];
+        os[i] = ps[col];
+      } else {
+        ms[i] = -INFINITY;
+        ls[i] = 0.f;
+        os[i] = 0.f;
+      }
     }
+    float mg = m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mg = fmaxf(mg, ms[i]);
+    if (mg == -INFINITY) continue;
+    const float f = m == -INFINITY ? 0.f : __expf(m - mg);
+    l *= f;
+    o *= f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (ms[i] != -INFINITY) {
+        const float fi = __expf(ms[i] - mg);
+        l += ls[i] * fi;
+        o += os[i] * fi;
+      }
+    }
+    m = mg;
   }
   out[(size_t)head * D + col] = l > 0.f ? o / l : 0.f;
   if (col == 0) {

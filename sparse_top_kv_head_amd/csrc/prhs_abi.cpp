@@ -84,6 +84,10 @@ size_t decode_ws(const prhs_dims* d, int cap) {
          sizeof(float);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t step_ws(const prhs_dims* d, int cap) { return align256(score_ws(d)) + decode_ws(d, cap); }
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +115,7 @@ size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap) {
     case PRHS_OP_SCORE: return score_ws(dims);
     case PRHS_OP_SELECT: return 0;
     case PRHS_OP_DECODE: return cap >= 1 ? decode_ws(dims, cap) : 0;
+    case PRHS_OP_ANCHOR_STEP: return cap >= 1 ? step_ws(dims, cap) : 0;
     default: return 0;
   }
 }
@@ -148,8 +153,8 @@ int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* ls
     return fail(PRHS_E_BUDGET, "delta_target must lie in [0, 1]");
   if (idx_cap < n_budget)
     return fail(PRHS_E_CAPACITY, "idx_cap %d < n_budget %d", idx_cap, n_budget);
-  return finish(prhs::launch_select(*dims, scores, lse_all, mode, n_budget, delta_target, idx,
-                                    idx_cap, count, cap_hit, stream),
+  return finish(prhs::launch_select(*dims, scores, const_cast<float*>(lse_all), nullptr, mode,
+                                    n_budget, delta_target, idx, idx_cap, count, cap_hit, stream),
                 stream, "prhs_select_topk");
 }
 
@@ -197,6 +202,45 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
   return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
                                     lse_sel, delta, tau, ws, stream),
                 stream, "prhs_sparse_decode");
+}
+
+int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,
+                     const void* q, const void* k, const void* v, float* scores, float* lse_all,
+                     int32_t* idx, int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* out,
+                     float* lse_sel, float* delta, float* tau, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
+    return fail(PRHS_E_DIMS, "selection supports ctx_len <= %d", PRHS_MAX_SELECT_CTX);
+  if (!q || !k || !v || !scores || !lse_all || !idx || !count || !out || !lse_sel)
+    return fail(PRHS_E_NULL, "q, k, v, scores, lse_all, idx, count, out and lse_sel are required");
+  if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(scores))
+    return fail(PRHS_E_ALIGN, "q, k, v and scores must be 16-byte aligned");
+  if (mode != PRHS_TOPN && mode != PRHS_DELTA) return fail(PRHS_E_BUDGET, "unknown mode %d", mode);
+  if (n_budget < 1 || n_budget > dims->ctx_len)
+    return fail(PRHS_E_BUDGET, "n_budget %d outside [1, %d]", n_budget, dims->ctx_len);
+  if (mode == PRHS_DELTA && !(delta_target >= 0.f && delta_target <= 1.f))
+    return fail(PRHS_E_BUDGET, "delta_target must lie in [0, 1]");
+  if (idx_cap < n_budget)
+    return fail(PRHS_E_CAPACITY, "idx_cap %d < n_budget %d", idx_cap, n_budget);
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < step_ws(dims, idx_cap))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", step_ws(dims, idx_cap),
+                ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  char* w = static_cast<char*>(ws);
+  void* score_part = w;
+  void* dec_part = w + align256(score_ws(dims));
+  hipError_t err = prhs::launch_score(*dims, q, k, scores, nullptr, score_part, stream);
+  if (err == hipSuccess)
+    err = prhs::launch_select(*dims, scores, lse_all, score_part, mode, n_budget, delta_target,
+                              idx, idx_cap, count, cap_hit, stream);
+  if (err == hipSuccess)
+    err = prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, scores, lse_all, out, lse_sel,
+                              delta, tau, dec_part, stream);
+  return finish(err, stream, "prhs_anchor_step");
 }
 
 int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* lse_all,

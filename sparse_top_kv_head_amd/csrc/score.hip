@@ -17,19 +17,19 @@ namespace prhs {
 namespace {
 
 constexpr int kScoreThreads = 256;
+constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int CHUNK = kScoreChunk, int UMAX = kScoreLoads>
 __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
     float2* __restrict__ part, int Hq, int Hkv, int t, long long sb, long long sh, long long st,
     int ld, int nchunks, int g_off, float scale) {
   constexpr int NW = kScoreThreads / kWave;
-  constexpr int CHUNK = kScoreChunk;
   constexpr int E = Elem<T>::kPer16B;
   constexpr int LPR = D / E;
   constexpr int RPW = kWave / LPR;
-  constexpr int U = 8;
   constexpr int RW = CHUNK / NW;
+  constexpr int U = RW / RPW < UMAX ? RW / RPW : UMAX;
   constexpr int ITERS = RW / (U * RPW);
   static_assert(G <= LPR, "one lane per head in a row group");
   static_assert(RW % (U * RPW) == 0, "chunk tiling");
@@ -107,18 +107,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   }
 }
 
-// Merge the per-chunk partials of each head into its dense log-sum-exp.
+// Merge the per-chunk partials of each head into its dense log-sum-exp: one
+// wave per head, the lanes reading the partials in parallel.
 __global__ __launch_bounds__(256) void lse_merge_kernel(const float2* __restrict__ part,
                                                         float* __restrict__ lse_all, int nheads,
                                                         int nchunks) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.x * (256 / kWave) + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
   if (h >= nheads) return;
   float m = -INFINITY, l = 0.f;
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = lane; c < nchunks; c += kWave) {
     const float2 p = part[(size_t)h * nchunks + c];
     ml_combine(m, l, p.x, p.y);
   }
-  lse_all[h] = (l > 0.f) ? m + __logf(l) : -INFINITY;
+  wave_ml(m, l);
+  if (lane == 0) lse_all[h] = (l > 0.f) ? m + __logf(l) : -INFINITY;
 }
 
 template <typename T, int D, int G>
@@ -155,7 +158,7 @@ void launch_scan_group(const prhs_dims& d, const void* q, const void* k, float* 
 
 hipError_t launch_score(const prhs_dims& d, const void* q, const void* k, float* scores,
                         float* lse_all, void* ws, hipStream_t stream) {
-  float2* part = lse_all ? static_cast<float2*>(ws) : nullptr;
+  float2* part = static_cast<float2*>(ws);
   const int G = d.n_q_heads / d.n_kv_heads;
   if (d.dtype == PRHS_F16) {
     if (d.head_dim == 128) launch_scan_group<__half, 128>(d, q, k, scores, part, G, stream);
@@ -166,7 +169,7 @@ hipError_t launch_score(const prhs_dims& d, const void* q, const void* k, float*
   }
   if (lse_all) {
     const int nheads = d.batch * d.n_q_heads;
-    hipLaunchKernelGGL(lse_merge_kernel, dim3((nheads + 255) / 256), dim3(256), 0, stream, part,
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((nheads + 3) / 4), dim3(256), 0, stream, part,
                        lse_all, nheads, score_nchunks(d));
   }
   return hipGetLastError();

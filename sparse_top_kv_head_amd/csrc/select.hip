@@ -86,6 +86,7 @@ struct SelShared {
   uint32_t wtot[NT / kWave];
   uint32_t wtot2[NT / kWave];
   unsigned long long wmass[NT / kWave];
+  float lse;                      // dense log-sum-exp merged from the scan partials
   uint32_t ncand;                 // fast-path list length
   uint32_t ncand_r;               // register-path list length
   uint32_t kmax;
@@ -638,16 +639,33 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
   }
 }
 
+// lse_all is read (DELTA) unless `part` is given: then the head's per-chunk
+// (max, sum) partials of the score scan are merged here, the result used and
+// written to lse_all.
 template <int KPT, int NT, int MODE>
 __global__ __launch_bounds__(NT) void select_kernel(
-    const float* __restrict__ scores, const float* __restrict__ lse_all, int t, int ld,
-    int n_budget, float delta_target, int* __restrict__ idx, int idx_cap,
-    int* __restrict__ count, int* __restrict__ cap_hit) {
+    const float* __restrict__ scores, float* __restrict__ lse_all,
+    const float2* __restrict__ part, int nchunks, int t, int ld, int n_budget,
+    float delta_target, int* __restrict__ idx, int idx_cap, int* __restrict__ count,
+    int* __restrict__ cap_hit) {
   constexpr bool MASS = MODE == PRHS_DELTA;
   __shared__ SelShared<NT, MASS> sh;
 
   const int head = blockIdx.x;
   const float* row = scores + (size_t)head * ld;
+  if (part != nullptr && threadIdx.x < kWave) {
+    float m = -INFINITY, l = 0.f;
+    for (int c = threadIdx.x; c < nchunks; c += kWave) {
+      const float2 pc = part[(size_t)head * nchunks + c];
+      ml_combine(m, l, pc.x, pc.y);
+    }
+    wave_ml(m, l);
+    if (threadIdx.x == 0) {
+      const float lse = l > 0.f ? m + __logf(l) : -INFINITY;
+      sh.lse = lse;
+      lse_all[head] = lse;
+    }
+  }
 
   for (int i = threadIdx.x; i < kBins * kRep1; i += NT) sh.hist[i] = 0;
   if constexpr (MASS)
@@ -666,7 +684,7 @@ __global__ __launch_bounds__(NT) void select_kernel(
   int n_sel = n_budget;
   int hit = 0;
   if constexpr (MASS) {
-    const float lse = lse_all[head];
+    const float lse = part != nullptr ? sh.lse : lse_all[head];
     const unsigned long long budget = (unsigned long long)((double)delta_target * kMassScale);
     uint32_t n_above = 0, take_T = 0;
     const bool found = mass_search<KPT, NT>(K, lse, budget, T, n_above, take_T, sh);
@@ -698,13 +716,13 @@ __global__ __launch_bounds__(NT) void select_kernel(
 constexpr int kSelThreads = 1024;
 
 template <int MODE>
-void launch_mode(int kpt, int nheads, const float* scores, const float* lse_all, int t, int ld,
-                 int n_budget, float delta_target, int* idx, int idx_cap, int* count, int* cap_hit,
-                 hipStream_t stream) {
+void launch_mode(int kpt, int nheads, const float* scores, float* lse_all, const float2* part,
+                 int nchunks, int t, int ld, int n_budget, float delta_target, int* idx,
+                 int idx_cap, int* count, int* cap_hit, hipStream_t stream) {
 #define PRHS_SEL(K)                                                                          \
   hipLaunchKernelGGL((select_kernel<K, kSelThreads, MODE>), dim3(nheads), dim3(kSelThreads), 0, \
-                     stream, scores, lse_all, t, ld, n_budget, delta_target, idx, idx_cap, count, \
-                     cap_hit)
+                     stream, scores, lse_all, part, nchunks, t, ld, n_budget, delta_target, idx, \
+                     idx_cap, count, cap_hit)
   switch (kpt) {
     case 1: PRHS_SEL(1); break;
     case 2: PRHS_SEL(2); break;
@@ -719,18 +737,20 @@ void launch_mode(int kpt, int nheads, const float* scores, const float* lse_all,
 
 }  // namespace
 
-hipError_t launch_select(const prhs_dims& d, const float* scores, const float* lse_all, int mode,
-                         int n_budget, float delta_target, int* idx, int idx_cap, int* count,
-                         int* cap_hit, hipStream_t stream) {
+hipError_t launch_select(const prhs_dims& d, const float* scores, float* lse_all,
+                         const void* score_ws, int mode, int n_budget, float delta_target,
+                         int* idx, int idx_cap, int* count, int* cap_hit, hipStream_t stream) {
   int kpt = 1;
   while (kpt * kSelThreads < d.ctx_len) kpt *= 2;
   const int nheads = d.batch * d.n_q_heads;
+  const float2* part = static_cast<const float2*>(score_ws);
+  const int nch = score_nchunks(d);
   if (mode == PRHS_DELTA)
-    launch_mode<PRHS_DELTA>(kpt, nheads, scores, lse_all, d.ctx_len, d.scores_ld, n_budget,
-                            delta_target, idx, idx_cap, count, cap_hit, stream);
+    launch_mode<PRHS_DELTA>(kpt, nheads, scores, lse_all, part, nch, d.ctx_len, d.scores_ld,
+                            n_budget, delta_target, idx, idx_cap, count, cap_hit, stream);
   else
-    launch_mode<PRHS_TOPN>(kpt, nheads, scores, lse_all, d.ctx_len, d.scores_ld, n_budget,
-                           delta_target, idx, idx_cap, count, cap_hit, stream);
+    launch_mode<PRHS_TOPN>(kpt, nheads, scores, lse_all, part, nch, d.ctx_len, d.scores_ld,
+                           n_budget, delta_target, idx, idx_cap, count, cap_hit, stream);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ class DecodeEngine:
         self.tau = torch.empty((d.batch, d.n_q_heads), **f32)
         self.reuse_ok = torch.empty((d.batch, d.n_q_heads), **i32)
         ws = max(P.prhs_workspace_bytes(d, P.PRHS_OP_SCORE),
-                 P.prhs_workspace_bytes(d, P.PRHS_OP_DECODE, cap))
+                 P.prhs_workspace_bytes(d, P.PRHS_OP_DECODE, cap),
+                 P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, cap))
         self.ws = torch.empty(((ws + 15) // 16 * 16,), dtype=torch.uint8, device=dev)
 
     def score(self, q, K, stream=None):
@@ -57,17 +58,19 @@ class DecodeEngine:
                              self.delta if use_scores else None, self.tau if use_scores else None,
                              self.ws, stream=stream)
 
+    def anchor_step(self, q, K, V, mode, n_budget, delta_target=0.0, stream=None):
+        """One fused call: score scan, selection, sparse attention with delta/tau."""
+        P.prhs_anchor_step(self.dims, mode, n_budget, delta_target, q, K, V, self.scores,
+                           self.lse_all, self.idx, self.cap, self.count, self.cap_hit, self.out,
+                           self.lse_sel, self.delta, self.tau, self.ws, stream=stream)
+
     def topn_step(self, q, K, V, N, stream=None):
         """Anchor step: exact top-N over fresh scores, then attention over it."""
-        self.score(q, K, stream)
-        self.select(P.PRHS_TOPN, N, stream=stream)
-        self.decode(q, K, V, True, stream=stream)
+        self.anchor_step(q, K, V, P.PRHS_TOPN, N, stream=stream)
 
     def delta_step(self, q, K, V, cap, delta_target, stream=None):
         """Smallest set with dropped mass <= delta_target (capped), then attention."""
-        self.score(q, K, stream)
-        self.select(P.PRHS_DELTA, cap, delta_target, stream=stream)
-        self.decode(q, K, V, True, stream=stream)
+        self.anchor_step(q, K, V, P.PRHS_DELTA, cap, delta_target, stream=stream)
 
     def reuse_step(self, q, K, V, anchor_idx, anchor_count, anchor_cap, radius,
                    q_anchor=None, sim_tau=0.0, stream=None):
@@ -79,3 +82,15 @@ class DecodeEngine:
 
     def dropped_mass(self, stream=None):
         P.prhs_dropped_mass(self.dims, self.lse_sel, self.lse_all, self.delta, self.tau, stream=stream)
+
+    def capture(self, steps, mode, n_budget, delta_target=0.0):
+        """Capture a sequence of anchor steps [(q, K, V), ...] into one HIP graph.
+
+        The graph replays the same kernels on the same buffers; inputs must stay
+        at the captured addresses. Returns the torch CUDAGraph (call .replay()).
+        """
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for (q, K, V) in steps:
+                self.anchor_step(q, K, V, mode, n_budget, delta_target)
+        return g

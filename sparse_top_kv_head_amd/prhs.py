@@ -35,11 +35,13 @@ PRHS_DELTA = 1
 PRHS_OP_SCORE = 0
 PRHS_OP_SELECT = 1
 PRHS_OP_DECODE = 2
+PRHS_OP_ANCHOR_STEP = 3
 PRHS_MAX_SELECT_CTX = 65536
 
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-    "prhs_dropped_mass", "prhs_workspace_bytes", "prhs_status_string", "prhs_last_error",
+    "prhs_dropped_mass", "prhs_anchor_step", "prhs_workspace_bytes", "prhs_status_string",
+    "prhs_last_error",
 )
 
 
@@ -82,6 +84,8 @@ def lib():
         L.prhs_cis_reuse.argtypes = [dp, vp, i32, vp, i32, vp, vp, f32, vp, i32, vp, vp, vp]
         L.prhs_sparse_decode.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
+        L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                       vp, vp, vp, vp, sz, vp]
         L.prhs_workspace_bytes.argtypes = [dp, i32, i32]
         L.prhs_workspace_bytes.restype = sz
         L.prhs_status_string.argtypes = [ctypes.c_int]
@@ -89,7 +93,7 @@ def lib():
         L.prhs_last_error.argtypes = []
         L.prhs_last_error.restype = ctypes.c_char_p
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-                     "prhs_dropped_mass"):
+                     "prhs_dropped_mass", "prhs_anchor_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -173,3 +177,14 @@ def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
 def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):
     _check(lib().prhs_dropped_mass(ctypes.byref(dims), _p(lse_sel), _p(lse_all), _p(delta),
                                    _p(tau), _stream(stream)))
+
+
+def prhs_anchor_step(dims, mode, n_budget, delta_target, q, k, v, scores, lse_all, idx, idx_cap,
+                     count, cap_hit, out, lse_sel, delta=None, tau=None, ws=None, ws_bytes=None,
+                     stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(lib().prhs_anchor_step(ctypes.byref(dims), mode, n_budget, delta_target, _p(q), _p(k),
+                                  _p(v), _p(scores), _p(lse_all), _p(idx), idx_cap, _p(count),
+                                  _p(cap_hit), _p(out), _p(lse_sel), _p(delta), _p(tau), _p(ws),
+                                  ws_bytes, _stream(stream)))

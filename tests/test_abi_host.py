@@ -167,6 +167,35 @@ def test_decode_argument_checks(L):
     assert L.prhs_dropped_mass(ctypes.byref(d), None, FAKE, FAKE, None, None) == P.PRHS_E_NULL
 
 
+def _step(L, d, mode=P.PRHS_TOPN, n=64, dt=0.05, q=FAKE, k=FAKE, v=FAKE, s=FAKE, lse=FAKE,
+          idx=FAKE, cap=64, cnt=FAKE, out=FAKE, lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_anchor_step(ctypes.byref(d) if d is not None else None, mode, n, dt, q, k, v, s,
+                              lse, idx, cap, cnt, None, out, lsel, dl, tau, ws, wsb, None)
+
+
+def test_anchor_step_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_ANCHOR_STEP, 64)
+    part = 2 * 8 * 1 * 8
+    assert need == (part + 255) // 256 * 256 + 2 * 8 * 1 * (128 + 2) * 4
+    assert _step(L, None) == P.PRHS_E_NULL
+    assert _step(L, _dims(head_dim=96)) == P.PRHS_E_DIMS
+    assert _step(L, _dims(ctx_len=P.PRHS_MAX_SELECT_CTX + 1, scores_ld=P.PRHS_MAX_SELECT_CTX + 4)) == P.PRHS_E_DIMS
+    for kw in ("q", "k", "v", "s", "lse", "idx", "cnt", "out", "lsel"):
+        assert _step(L, d, **{kw: None}) == P.PRHS_E_NULL, kw
+    assert _step(L, d, dl=None) == P.PRHS_E_NULL            # tau without delta
+    assert _step(L, d, v=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert _step(L, d, mode=9) == P.PRHS_E_BUDGET
+    assert _step(L, d, n=0) == P.PRHS_E_BUDGET
+    assert _step(L, d, mode=P.PRHS_DELTA, dt=2.0) == P.PRHS_E_BUDGET
+    assert _step(L, d, n=65) == P.PRHS_E_CAPACITY
+    assert _step(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _step(L, d, wsb=need - 1) == P.PRHS_E_WORKSPACE
+    assert _step(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
+
+
 def test_status_strings(L):
     codes = [P.PRHS_OK, P.PRHS_E_NULL, P.PRHS_E_DIMS, P.PRHS_E_DTYPE, P.PRHS_E_BUDGET,
              P.PRHS_E_CAPACITY, P.PRHS_E_WORKSPACE, P.PRHS_E_HIP, P.PRHS_E_ALIGN]

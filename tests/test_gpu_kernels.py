@@ -386,3 +386,61 @@ def test_engine_topn_step_small():
             o_ref = r["out"] if exact else O.sparse_attention(r["scores"], V64[b, h], gidx)[0]
             assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL
             assert abs(eng.delta[b, h].item() - r["delta"]) <= DELTA_TOL
+
+
+# ---------------------------------------------------------------------------
+# prhs_anchor_step: one call, same results as the three calls in sequence.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [P.PRHS_TOPN, P.PRHS_DELTA])
+def test_anchor_step_matches_separate_calls(mode):
+    dev = _dev()
+    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+    cfg = CONFIGS["llama2_4k"].replace(steps=2, n_q_heads=8, n_kv_heads=2)
+    w = make_workload(cfg, device=dev)
+    a = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    b = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    q = w.q[1]
+    ds = 0.3
+    a.anchor_step(q, w.K, w.V, mode, cfg.budget, ds)
+    b.score(q, w.K)
+    b.select(mode, cfg.budget, ds)
+    b.decode(q, w.K, w.V, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.scores[..., :cfg.ctx_len], b.scores[..., :cfg.ctx_len])
+    assert torch.equal(a.lse_all, b.lse_all)
+    assert torch.equal(a.count, b.count)
+    for h in range(cfg.n_q_heads):
+        n = int(a.count[0, h])
+        assert torch.equal(a.idx[0, h, :n], b.idx[0, h, :n])
+    for name in ("out", "lse_sel", "delta", "tau"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    if mode == P.PRHS_DELTA:
+        assert torch.equal(a.cap_hit, b.cap_hit)
+
+
+def test_anchor_step_graph_replay_matches_eager():
+    """A captured step replays to the eager results, replay after replay, with
+    eager work and synchronisations between the replays."""
+    dev = _dev()
+    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=1, ctx_len=8192, budget=512, steps=3,
+                                             n_clusters=(64, 64))
+    w = make_workload(cfg, device=dev)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    other = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    names = ("scores", "lse_all", "idx", "count", "out", "lse_sel", "delta", "tau")
+    eng.anchor_step(w.q[1], w.K, w.V, P.PRHS_TOPN, cfg.budget)
+    torch.cuda.synchronize()
+    ref = {n: getattr(eng, n).clone() for n in names}
+    eng.anchor_step(w.q[0], w.K, w.V, P.PRHS_TOPN, cfg.budget)      # overwrite before capture
+    g = eng.capture([(w.q[1], w.K, w.V)], P.PRHS_TOPN, cfg.budget)
+    for r in range(4):
+        other.anchor_step(w.q[r % 3], w.K, w.V, P.PRHS_TOPN, cfg.budget)   # eager work in between
+        for n in names:
+            getattr(eng, n).fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(eng, n), ref[n]), (r, n)
