@@ -1,0 +1,191 @@
+"""End-to-end parity of the decode hot path on the configured workloads.
+
+Every workload runs at its full configured size in the launch configuration
+the benchmark uses (DecodeEngine.anchor_step / reuse_step); the oracle checks
+a sample of heads and steps (each oracle head costs one fp64 pass over its
+KV head). Inputs are the seeded synthetic workloads; expected values come only
+from the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prhs_oracle as O
+from sparse_top_kv_head_amd import prhs as P
+from sparse_top_kv_head_amd.engine import DecodeEngine
+from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+from tests.parity_util import DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()
+    return torch.device("cuda:0")
+
+
+def _np(x):
+    return x.detach().double().cpu().numpy()
+
+
+def _sample_heads(cfg, n, seed):
+    rng = np.random.default_rng(seed)
+    allh = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_q_heads)]
+    pick = rng.choice(len(allh), size=min(n, len(allh)), replace=False)
+    return sorted(allh[i] for i in pick)
+
+
+class _KVCache:
+    """fp64 host copies of the KV heads the oracle needs, fetched on demand."""
+
+    def __init__(self, w):
+        self.w = w
+        self.k = {}
+        self.v = {}
+
+    def kv(self, b, g):
+        if (b, g) not in self.k:
+            self.k[(b, g)] = _np(self.w.K[b, g])
+            self.v[(b, g)] = _np(self.w.V[b, g])
+        return self.k[(b, g)], self.v[(b, g)]
+
+
+def _oracle_scores(cache, q64, b, h, G):
+    K, V = cache.kv(b, h // G)
+    s = O.attention_scores(q64[b:b + 1, h:h + 1], K[None, None])[0, 0]
+    return s, V
+
+
+def _check_topn_heads(eng, w, cfg, step, heads, cache):
+    q64 = _np(w.q[step])
+    G = cfg.group
+    exact_heads = 0
+    for (b, h) in heads:
+        s, V = _oracle_scores(cache, q64, b, h, G)
+        n = int(eng.count[b, h])
+        gidx = eng.idx[b, h, :n].cpu().numpy()
+        exact = check_set_band(gidx, s, cfg.budget)
+        exact_heads += exact
+        S_ref = O.topn_select(s, cfg.budget) if exact else gidx
+        o_ref, lse_ref = O.sparse_attention(s, V, S_ref)
+        d_ref, _ = O.dropped_mass(s, S_ref)
+        assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL
+        assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL
+        assert abs(eng.tau[b, h].item() - (1 - d_ref)) <= DELTA_TOL
+        _, lse_all = O.dense_softmax(s)
+        assert abs(eng.lse_all[b, h].item() - lse_all) <= 1e-3
+    return exact_heads
+
+
+def test_llama2_4k_full():
+    """LLaMA2-7B-shaped layer: every head of three of the 64 steps."""
+    dev = _dev()
+    cfg = CONFIGS["llama2_4k"]
+    w = make_workload(cfg, device=dev)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    cache = _KVCache(w)
+    heads = [(0, h) for h in range(cfg.n_q_heads)]
+    for step in (0, 31, cfg.steps - 1):
+        eng.topn_step(w.q[step], w.K, w.V, cfg.budget)
+        torch.cuda.synchronize()
+        assert _check_topn_heads(eng, w, cfg, step, heads, cache) >= len(heads) - 2
+
+
+def test_mistral_gqa_32k_sampled():
+    """Mistral-7B-shaped GQA layer at 32K: 16 sampled heads at three steps, plus
+    run-to-run determinism of every head's indices and outputs."""
+    dev = _dev()
+    cfg = CONFIGS["mistral_gqa_32k"]
+    w = make_workload(cfg, device=dev)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    cache = _KVCache(w)
+    for step in (0, 13, cfg.steps - 1):
+        eng.topn_step(w.q[step], w.K, w.V, cfg.budget)
+        torch.cuda.synchronize()
+        heads = _sample_heads(cfg, 16, step)
+        assert _check_topn_heads(eng, w, cfg, step, heads, cache) >= len(heads) - 2
+        assert torch.all(eng.count == cfg.budget)
+    first = (eng.idx.clone(), eng.count.clone(), eng.out.clone(), eng.delta.clone())
+    eng.topn_step(w.q[cfg.steps - 1], w.K, w.V, cfg.budget)
+    torch.cuda.synchronize()
+    for a, b in zip(first, (eng.idx, eng.count, eng.out, eng.delta)):
+        assert torch.equal(a, b)
+
+
+def test_llama2_cis_8k_schedule():
+    """CIS reuse at full size: exact retrieval every 4th step, +-2 dilation of the
+    anchor's set otherwise (not chained), attention over the reused set with
+    gathered K and V rows; delta of the reused set against the oracle."""
+    dev = _dev()
+    cfg = CONFIGS["llama2_cis_8k"]
+    w = make_workload(cfg, device=dev)
+    r = cfg.radius
+    dil_cap = min(cfg.ctx_len, (2 * r + 1) * cfg.budget)
+    anchor = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    reuse = DecodeEngine(w.K, cfg.n_q_heads, dil_cap)
+    cache = _KVCache(w)
+    heads = _sample_heads(cfg, 12, 3)
+    sched = O.cis_schedule(8, cfg.refresh_period)
+    anchor_sets = {}
+    for step, (is_anchor, a_step) in enumerate(sched):
+        q64 = _np(w.q[step])
+        if is_anchor:
+            anchor.topn_step(w.q[step], w.K, w.V, cfg.budget)
+            torch.cuda.synchronize()
+            _check_topn_heads(anchor, w, cfg, step, heads, cache)
+            anchor_sets = {bh: anchor.idx[bh[0], bh[1], :int(anchor.count[bh])].cpu().numpy() for bh in heads}
+            a_idx, a_cnt = anchor.idx.clone(), anchor.count.clone()
+            continue
+        reuse.reuse_step(w.q[step], w.K, w.V, a_idx, a_cnt, cfg.budget, r)
+        # diagnostic pass: dense lse of this step for the reused set's delta
+        reuse.score(w.q[step], w.K)
+        reuse.dropped_mass()
+        torch.cuda.synchronize()
+        for (b, h) in heads:
+            s, V = _oracle_scores(cache, q64, b, h, cfg.group)
+            D_ref = O.cis_dilate(anchor_sets[(b, h)], r, cfg.ctx_len)
+            n = int(reuse.count[b, h])
+            assert np.array_equal(reuse.idx[b, h, :n].cpu().numpy(), D_ref)
+            o_ref, lse_ref = O.sparse_attention(s, V, D_ref)
+            d_ref, _ = O.dropped_mass(s, D_ref)
+            assert np.max(np.abs(_np(reuse.out[b, h]) - o_ref)) <= OUT_TOL
+            assert abs(reuse.lse_sel[b, h].item() - lse_ref) <= 1e-3
+            assert abs(reuse.delta[b, h].item() - d_ref) <= DELTA_TOL
+            # the reused set keeps at most the oracle's mass at its own size
+            assert O.beta_emp(s, D_ref) >= -1e-12
+
+
+@pytest.mark.parametrize("variant", ["literal", "sharp"])
+def test_delta_16k_layer_sampled(variant):
+    """Delta-budgeted layer at full size (one of the 32 layers; each layer is an
+    independent KV cache): smallest N with delta <= 0.05, capped at 2048. The
+    "sharp" variant draws a per-layer query scale in [1, 4] so that N* varies."""
+    dev = _dev()
+    cfg = CONFIGS["delta_16k"]
+    if variant == "sharp":
+        cfg = cfg.replace(q_scale=(1.0, 4.0))
+    layer = 7
+    w = make_workload(cfg, device=dev, layer=layer)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    cache = _KVCache(w)
+    for step in (0, cfg.steps - 1):
+        eng.delta_step(w.q[step], w.K, w.V, cfg.budget, cfg.delta_star)
+        torch.cuda.synchronize()
+        q64 = _np(w.q[step])
+        for (b, h) in _sample_heads(cfg, 12, 100 * layer + step):
+            s, V = _oracle_scores(cache, q64, b, h, cfg.group)
+            _, lse = O.dense_softmax(s)
+            n = int(eng.count[b, h])
+            gidx = eng.idx[b, h, :n].cpu().numpy()
+            exact = check_delta_choice(gidx, n, s, float(lse), cfg.budget, cfg.delta_star,
+                                       cap_hit=int(eng.cap_hit[b, h]))
+            S_ref = O.topn_select(s, n) if exact else gidx
+            o_ref, _ = O.sparse_attention(s, V, S_ref)
+            d_ref, _ = O.dropped_mass(s, S_ref)
+            assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL
+            assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL
+            if not int(eng.cap_hit[b, h]):
+                assert eng.delta[b, h].item() <= cfg.delta_star + DELTA_TOL
