@@ -27,6 +27,28 @@ import numpy as np
 import torch
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_scan_mistral_gqa_32k_hbm_traffic.md")
+SCAN_SOURCES = ["sparse_top_kv_head_amd/csrc/score.hip", "sparse_top_kv_head_amd/csrc/prhs_device.hpp",
+                "sparse_top_kv_head_amd/csrc/prhs_launch.hpp"]
+
+
+def scan_traffic_bytes():
+    """HBM bytes per scan launch from the committed counter profile, or None when
+    the scan kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    rec = dict(line.split(": ", 1) for line in text.splitlines()
+               if line.startswith(("scan_traffic_bytes_per_launch:", "scan_source_hash:")))
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("scan_source_hash", "").strip() != h.hexdigest()[:16]:
+        return None
+    return float(rec["scan_traffic_bytes_per_launch"])
 
 
 def _parse():
@@ -38,6 +60,8 @@ def _parse():
     ap.add_argument("--rotate", type=int, default=4, help="independent KV copies cycled over steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -125,17 +149,15 @@ def main():
     total_ms = ev0.elapsed_time(ev1)
 
     # The scan kernel alone, same inputs and launch configuration as inside the
-    # step (per-chunk partials on, no separate log-sum-exp merge), timed with
-    # events on the launch stream.
+    # step (per-chunk partials on, no separate log-sum-exp merge): K launches
+    # back to back between two events on the launch stream.
     part = torch.empty(P.prhs_workspace_bytes(eng.dims, P.PRHS_OP_SCORE), dtype=torch.uint8, device=dev)
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
+    ev0.record(stream)
     for i in range(a.steps):
-        r = i % a.rotate
-        sev[i][0].record(stream)
-        P.prhs_score(eng.dims, w.q[i % cfg.steps], Ks[r], eng.scores, None, part, stream=stream)
-        sev[i][1].record(stream)
+        P.prhs_score(eng.dims, w.q[i % cfg.steps], Ks[i % a.rotate], eng.scores, None, part, stream=stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    scan_ms = np.array([e[0].elapsed_time(e[1]) for e in sev])
+    scan_ms = np.array([ev0.elapsed_time(ev1) / a.steps])
 
     B, Hq, Hkv, d, t, eb = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.elem_bytes
     heads = B * Hq
@@ -151,6 +173,8 @@ def main():
             rows += np.unique(np.concatenate([idx[b, h, :cnt[b, h]] for h in range(g * G, (g + 1) * G)])).size
     step_bytes = scan_bytes + rows * d * eb
     scan_gbs = scan_bytes / (scan_ms.mean() / 1e3) / 1e9
+    traffic_bytes = scan_traffic_bytes()
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (scan_ms.mean() / 1e3) / 1e9, 1)
     res = {
         "metric": "sparse decode attn heads*steps/s at 32K ctx + achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -167,9 +191,10 @@ def main():
         "config": {"workload": f"{cfg.name}: Mistral-7B-shaped GQA decode layer, B={B}, H_q={Hq}, "
                                f"H_kv={Hkv}, d={d}, t={t}, top-N={N}, fp16 K/V",
                    "batch": B, "ctx_len": t, "budget": N, "kv_copies_rotated": a.rotate},
-        "roofline": {"bound": "hbm", "kernel": "score_scan_kernel<__half,128,4> (K scan GEMV, timed in its own loop)",
+        "roofline": {"bound": "hbm", "kernel": "score_scan_kernel<__half,128,4,256,16> (K scan GEMV, timed in its own loop)",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_bytes_per_launch": traffic_bytes,
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "mean_launch_ms": round(float(scan_ms.mean()), 5)},
         "step": {"hbm_alg_bytes": int(step_bytes), "hbm_alg_gbs": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
@@ -179,6 +204,13 @@ def main():
                  "mean_selected_rows_per_head": float(cnt.mean()),
                  "wall_s": round(wall, 4)},
     }
+    if a.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = src.numel()
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, cfg.steps, a.cpu_seconds)
     print(json.dumps(res), flush=True)
