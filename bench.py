@@ -151,7 +151,7 @@ def main():
     # The scan kernel alone, same inputs and launch configuration as inside the
     # step (per-chunk partials on, no separate log-sum-exp merge): K launches
     # back to back between two events on the launch stream.
-    part = torch.empty(P.prhs_workspace_bytes(eng.dims, P.PRHS_OP_SCORE), dtype=torch.uint8, device=dev)
+    part = P.alloc_workspace(eng.dims, P.PRHS_OP_SCORE, device=dev)
     ev0.record(stream)
     for i in range(a.steps):
         P.prhs_score(eng.dims, w.q[i % cfg.steps], Ks[i % a.rotate], eng.scores, None, part, stream=stream)

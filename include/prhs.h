@@ -32,6 +32,9 @@
  *    tau) are fp32 [B, H_q].
  *  - Query head h reads KV head h / G with G = H_q / H_kv (grouped-query
  *    attention).
+ *  - Workspaces: a call that takes `ws` needs at least prhs_workspace_bytes()
+ *    bytes, 16-byte aligned; their contents on entry do not matter. Calls
+ *    that share a workspace must not run concurrently.
  *  - Alignment: q, K, V and scores base pointers must be 16-byte aligned;
  *    kv_stride_t * element size, kv_stride_h and kv_stride_b must keep every
  *    row 16-byte aligned; scores_ld must be a multiple of 4.
@@ -96,8 +99,8 @@ typedef struct prhs_dims {
  *
  * Products are accumulated in fp32. The K row of every key is read once for
  * all G query heads of its group. lse_all may be NULL (then ws may be NULL).
- * ws: device workspace of at least prhs_workspace_bytes(dims, PRHS_OP_SCORE, 0)
- * bytes (per-chunk partial maxima and sums); its contents on entry do not matter.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_SCORE, 0) bytes (per-chunk
+ * partial maxima and sums).
  */
 int prhs_score(const prhs_dims* dims, const void* q, const void* k, float* scores,
                float* lse_all, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -116,13 +119,16 @@ int prhs_score(const prhs_dims* dims, const void* q, const void* k, float* score
  *   depend on the order of accumulation.
  *
  * Output: idx[b,h,0:count) ascending; count[b,h] = N (TOPN) or N* (DELTA).
+ * sel_scores (nullable, fp32 [B, H_q, idx_cap]): the scores of the selected
+ * keys in the same order as idx, for prhs_sparse_decode.
  * Requires 1 <= n_budget <= t, n_budget <= idx_cap, 0 <= delta_target <= 1,
  * t <= PRHS_MAX_SELECT_CTX. Scores must be finite or -inf (NaN is outside
  * the contract); -0.0 and +0.0 compare equal. lse_all may be NULL in TOPN mode.
  */
 int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* lse_all,
                      int32_t mode, int32_t n_budget, float delta_target, int32_t* idx,
-                     int32_t idx_cap, int32_t* count, int32_t* cap_hit, hipStream_t stream);
+                     int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* sel_scores,
+                     hipStream_t stream);
 
 /*
  * prhs_cis_reuse -- critical-index-set sharing with dilation (Fig. 4: the set
@@ -152,10 +158,12 @@ int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anc
  *   m_S = max_{i in S} s_i,  out = sum_{i in S} e^{s_i - m_S} v_i / sum_{i in S} e^{s_i - m_S}
  *   lse_sel = m_S + log sum_{i in S} e^{s_i - m_S}
  *
- * S = idx[b,h,0:count[b,h]). s_i is read from `scores` when it is non-NULL
- * (the scores of the same step from prhs_score); otherwise the K rows at S
- * are gathered and scored (k must then be non-NULL). The set is split over
- * workgroups and the partial (max, sum, output) triples are merged exactly.
+ * S = idx[b,h,0:count[b,h]). s_i is read from sel_scores when it is non-NULL
+ * (fp32 [B, H_q, idx_cap] in idx order, as prhs_select_topk writes it), else
+ * gathered from `scores` when that is non-NULL (the scores of the same step
+ * from prhs_score); otherwise the K rows at S are gathered and scored (q and
+ * k must then be non-NULL). The set is split over workgroups and the partial
+ * (max, sum, output) triples are merged exactly.
  * Indices outside [0, t) are skipped; counts are clamped to [0, idx_cap]; an
  * empty set gives out = 0, lse_sel = -inf.
  * Fused dropped mass: when lse_all and delta are non-NULL,
@@ -165,9 +173,9 @@ int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anc
  */
 int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
                        const int32_t* idx, int32_t idx_cap, const int32_t* count,
-                       const float* scores, const float* lse_all, float* out, float* lse_sel,
-                       float* delta, float* tau, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+                       const float* sel_scores, const float* scores, const float* lse_all,
+                       float* out, float* lse_sel, float* delta, float* tau, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * prhs_anchor_step -- one exact-retrieval decode step in a single call: the
@@ -181,13 +189,22 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
  * needs delta). The dense log-sum-exp is merged inside the selection kernel
  * from the scan's per-chunk partials, so no separate merge runs. Argument
  * rules are the union of the three calls' rules.
+ *
+ * theta (nullable, fp32 [B, H_q], in/out; TOPN only): a per-head score
+ * threshold hint. The scan also hands the keys whose score is >= theta to
+ * the selection, which selects among them alone when they include the top
+ * n_budget (at least n_budget of them and at most a few thousand) and
+ * otherwise searches all keys, so the result never depends on the hint. NaN
+ * means no hint. On return theta holds a hint for the next step of the same
+ * heads: this step's boundary score less a margin (adjacent decode queries
+ * are highly similar: Fig. 2, Fig. 10). Initialise it to NaN.
  * ws: at least prhs_workspace_bytes(dims, PRHS_OP_ANCHOR_STEP, idx_cap) bytes.
  */
 int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,
                      const void* q, const void* k, const void* v, float* scores, float* lse_all,
                      int32_t* idx, int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* out,
-                     float* lse_sel, float* delta, float* tau, void* ws, size_t ws_bytes,
-                     hipStream_t stream);
+                     float* lse_sel, float* delta, float* tau, float* theta, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /*
  * prhs_dropped_mass -- dropped and retained attention mass of the selected

@@ -4,14 +4,14 @@
 //
 // Split-budget decode: the selected list of a head is cut into splits of
 // kDecodeRows entries, one 256-thread workgroup each, so even a few heads fill
-// the chip. A workgroup gathers its entries' scores (stored by the score scan,
-// or recomputed from gathered K rows on steps without a scan), takes their
-// maximum, turns them into weights in LDS, then streams the V rows at those
-// indices with 16-byte lane loads (LPR lanes per row, several rows in flight
-// per lane) and accumulates weight * v in fp32. Each split leaves a partial
-// (max, sum, output) triple; the merge kernel combines them exactly as the
-// online softmax does and, when the dense log-sum-exp is given, writes the
-// dropped mass delta and the retained mass tau of the set.
+// the chip. A workgroup reads its entries' scores (compact from the selection,
+// gathered from the score scan, or recomputed from gathered K rows on steps
+// without a scan), requests all of its V rows with 16-byte lane loads (LPR
+// lanes per row, up to 16 rows in flight per lane) while it turns the scores
+// into weights, and accumulates weight * v in fp32. Each split leaves a
+// partial (max, sum, output) triple; the merge kernel combines them exactly
+// as the online softmax does and, when the dense log-sum-exp is given, writes
+// the dropped mass delta and the retained mass tau of the set.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
@@ -20,149 +20,14 @@ namespace {
 
 constexpr int kDecThreads = 256;
 
-template <typename T, int D, bool HAS_SCORES>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int* __restrict__ idx, int idx_cap, const int* __restrict__ count,
-    const float* __restrict__ scores, int Hq, int Hkv, int t, long long sb, long long sh,
-    long long st, int ld, float scale, float* __restrict__ part, int nsplit) {
-  constexpr int NW = kDecThreads / kWave;
-  constexpr int ROWS = kDecodeRows;
-  constexpr int E = Elem<T>::kPer16B;
-  constexpr int LPR = D / E;
-  constexpr int RPW = kWave / LPR;
-  constexpr int U = 4;
-
-  __shared__ int sidx[ROWS];
-  __shared__ float sp[ROWS];
-  __shared__ float sred[NW];
-  __shared__ __align__(16) float so[NW][D];
-
-  const int split = blockIdx.x;
-  const int head = blockIdx.y;
-  const int b = head / Hq;
-  const int h = head - b * Hq;
-  const int g = h / (Hq / Hkv);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
-  const int c = lane % LPR;
-  const int rr = lane / LPR;
-
-  const int n = max(0, min(count[head], idx_cap));
-  const int beg = split * ROWS;
-  const int nr = max(0, min(ROWS, n - beg));
-  const int* irow = idx + (size_t)head * idx_cap + beg;
-
-  for (int i = tid; i < nr; i += kDecThreads) {
-    const int id = irow[i];
-    const bool ok = id >= 0 && id < t;
-    sidx[i] = ok ? id : -1;
-    if constexpr (HAS_SCORES) sp[i] = ok ? scores[(size_t)head * ld + id] : -INFINITY;
-  }
-  __syncthreads();
-
-  const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
-  if constexpr (!HAS_SCORES) {
-    const uint4 qv = load16(q + (size_t)head * D + c * E);
-    const char* kbase = reinterpret_cast<const char*>(k + kv_off) + c * 16;
-    for (int i0 = w * RPW * U; i0 < nr; i0 += NW * RPW * U) {
-      uint4 kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * RPW + rr;
-        const int id = i < nr ? sidx[i] : -1;
-        kv[u] = id >= 0 ? load16(kbase + (size_t)id * st * sizeof(T)) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * RPW + rr;
-        const float s = group_sum<LPR>(dot16(kv[u], qv, 0.f, T()));
-        if (c == 0 && i < nr) sp[i] = sidx[i] >= 0 ? s * scale : -INFINITY;
-      }
-    }
-    __syncthreads();
-  }
-
-  // split maximum
-  float m = -INFINITY;
-  for (int i = tid; i < nr; i += kDecThreads) m = fmaxf(m, sp[i]);
-  m = wave_max(m);
-  if (lane == 0) sred[w] = m;
-  __syncthreads();
-  m = sred[0];
-#pragma unroll
-  for (int k2 = 1; k2 < NW; ++k2) m = fmaxf(m, sred[k2]);
-  __syncthreads();
-  // weights and their sum
-  float l = 0.f;
-  for (int i = tid; i < nr; i += kDecThreads) {
-    const float p = (m == -INFINITY) ? 0.f : __expf(sp[i] - m);
-    sp[i] = p;
-    l += p;
-  }
-  l = wave_sum(l);
-  if (lane == 0) sred[w] = l;
-  __syncthreads();
-  l = 0.f;
-#pragma unroll
-  for (int k2 = 0; k2 < NW; ++k2) l += sred[k2];
-
-  // weighted V rows
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  const char* vbase = reinterpret_cast<const char*>(v + kv_off) + c * 16;
-  for (int i0 = w * RPW * U; i0 < nr; i0 += NW * RPW * U) {
-    uint4 vv[U];
-    float pw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * RPW + rr;
-      const int id = i < nr ? sidx[i] : -1;
-      pw[u] = id >= 0 ? sp[i] : 0.f;
-      vv[u] = id >= 0 ? load16(vbase + (size_t)id * st * sizeof(T)) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) axpy16(pw[u], vv[u], acc, T());
-  }
-  // sum the RPW row slots of the wave (lanes c, c+LPR, ...)
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-#pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
-  }
-  if (rr == 0) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) so[w][c * E + e] = acc[e];
-  }
-  __syncthreads();
-  float* dst = part + ((size_t)head * nsplit + split) * (D + 2);
-  for (int col = tid; col < D; col += kDecThreads) {
-    float s = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < NW; ++k2) s += so[k2][col];
-    dst[col] = s;
-  }
-  if (tid == 0) {
-    dst[D] = m;
-    dst[D + 1] = l;
-  }
-}
-
-// Merge the split partials of one head: thread `col` owns one output column.
-// Splits are taken eight at a time with all their loads issued together, so
-// the merge costs about one memory round trip per eight splits.
+// Merge the split partials of one head (thread `col` owns output column col):
+// splits are taken eight at a time with all their loads issued together.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part, int nsplit,
-                                                         float* __restrict__ out,
-                                                         float* __restrict__ lse_sel,
-                                                         const float* __restrict__ lse_all,
-                                                         float* __restrict__ delta,
-                                                         float* __restrict__ tau) {
-  const int head = blockIdx.x;
-  const int col = threadIdx.x;
-  const float* p = part + (size_t)head * nsplit * (D + 2);
+__device__ __forceinline__ void merge_head(const float* __restrict__ p, int nsplit, int col,
+                                           float* __restrict__ out, float* __restrict__ lse_sel,
+                                           const float* __restrict__ lse_all,
+                                           float* __restrict__ delta, float* __restrict__ tau,
+                                           int head) {
   float m = -INFINITY, l = 0.f, o = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += 8) {
     float ms[8], ls[8], os[8];
@@ -209,6 +74,179 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   }
 }
 
+// One split of one head. HAS_SCORES: the scores of the selected rows are read,
+// from sel_scores (compact, in idx order) when it is given, else gathered from
+// `scores`; otherwise they are computed from gathered K rows. Each wave owns
+// 64 consecutive rows of the split; their V rows are requested as soon as the
+// indices are known, before the split's weights are formed. The split leaves
+// (max, sum, o[D]) for the merge kernel. (Merging in the last split to arrive
+// needs a device-scope fence per workgroup, which costs far more on this chip
+// than the separate merge launch.)
+template <typename T, int D, bool HAS_SCORES>
+__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int* __restrict__ idx, int idx_cap, const int* __restrict__ count,
+    const float* __restrict__ sel_scores, const float* __restrict__ scores, int Hq, int Hkv,
+    int t, long long sb, long long sh, long long st, int ld, float scale,
+    float* __restrict__ part, int nsplit) {
+  constexpr int NW = kDecThreads / kWave;
+  constexpr int ROWS = kDecodeRows;
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  constexpr int RPW = kWave / LPR;
+  constexpr int RW = ROWS / NW;                    // rows per wave
+  constexpr int U = RW / RPW < 16 ? RW / RPW : 16;  // loads in flight per lane
+  constexpr int IT = RW / (U * RPW);
+  static_assert(RW % (U * RPW) == 0, "split tiling");
+
+  __shared__ int sidx[ROWS];
+  __shared__ float sp[ROWS];
+  __shared__ float sred[NW];
+  __shared__ __align__(16) float so[NW][D];
+
+  const int split = blockIdx.x;
+  const int head = blockIdx.y;
+  const int b = head / Hq;
+  const int h = head - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int c = lane % LPR;
+  const int rr = lane / LPR;
+
+  const int n = max(0, min(count[head], idx_cap));
+  const int beg = split * ROWS;
+  const int nr = max(0, min(ROWS, n - beg));
+  const int* irow = idx + (size_t)head * idx_cap + beg;
+
+  for (int i = tid; i < nr; i += kDecThreads) {
+    const int id = irow[i];
+    const bool ok = id >= 0 && id < t;
+    sidx[i] = ok ? id : -1;
+    if constexpr (HAS_SCORES)
+      sp[i] = !ok ? -INFINITY
+                  : sel_scores ? sel_scores[(size_t)head * idx_cap + beg + i]
+                               : scores[(size_t)head * ld + id];
+  }
+  __syncthreads();
+
+  const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
+  const size_t row_bytes = (size_t)st * sizeof(T);
+  if constexpr (!HAS_SCORES) {
+    const uint4 qv = load16(q + (size_t)head * D + c * E);
+    const char* kbase = reinterpret_cast<const char*>(k + kv_off) + c * 16;
+#pragma unroll 1
+    for (int it = 0; it < IT; ++it) {
+      uint4 kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = w * RW + (it * U + u) * RPW + rr;
+        const int id = i < nr ? sidx[i] : -1;
+        kv[u] = id >= 0 ? load16(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = w * RW + (it * U + u) * RPW + rr;
+        const float s = group_sum<LPR>(dot16(kv[u], qv, 0.f, T()));
+        if (c == 0 && i < nr) sp[i] = sidx[i] >= 0 ? s * scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+  }
+
+  // request the first batch of V rows before the weights are formed
+  const char* vbase = reinterpret_cast<const char*>(v + kv_off) + c * 16;
+  uint4 vv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = w * RW + u * RPW + rr;
+    const int id = i < nr ? sidx[i] : -1;
+    vv[u] = id >= 0 ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+  }
+
+  // split maximum
+  float m = -INFINITY;
+  for (int i = tid; i < nr; i += kDecThreads) m = fmaxf(m, sp[i]);
+  m = wave_max(m);
+  if (lane == 0) sred[w] = m;
+  __syncthreads();
+  m = sred[0];
+#pragma unroll
+  for (int k2 = 1; k2 < NW; ++k2) m = fmaxf(m, sred[k2]);
+  __syncthreads();
+  // weights and their sum
+  float l = 0.f;
+  for (int i = tid; i < nr; i += kDecThreads) {
+    const float p = (m == -INFINITY) ? 0.f : __expf(sp[i] - m);
+    sp[i] = p;
+    l += p;
+  }
+  l = wave_sum(l);
+  if (lane == 0) sred[w] = l;
+  __syncthreads();
+  l = 0.f;
+#pragma unroll
+  for (int k2 = 0; k2 < NW; ++k2) l += sred[k2];
+
+  // weighted V rows
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll 1
+  for (int it = 0; it < IT; ++it) {
+    if (it > 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = w * RW + (it * U + u) * RPW + rr;
+        const int id = i < nr ? sidx[i] : -1;
+        vv[u] = id >= 0 ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = w * RW + (it * U + u) * RPW + rr;
+      const float pw = (i < nr && sidx[i] >= 0) ? sp[i] : 0.f;
+      axpy16(pw, vv[u], acc, T());
+    }
+  }
+  // sum the RPW row slots of the wave (lanes c, c+LPR, ...)
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (rr == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) so[w][c * E + e] = acc[e];
+  }
+  __syncthreads();
+  float* dst = part + ((size_t)head * nsplit + split) * (D + 2);
+  for (int col = tid; col < D; col += kDecThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < NW; ++k2) s += so[k2][col];
+    dst[col] = s;
+  }
+  if (tid == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+
+// Merge of one head's split partials: thread `col` owns one output column.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part, int nsplit,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ lse_sel,
+                                                         const float* __restrict__ lse_all,
+                                                         float* __restrict__ delta,
+                                                         float* __restrict__ tau) {
+  const int head = blockIdx.x;
+  merge_head<D>(part + (size_t)head * nsplit * (D + 2), nsplit, threadIdx.x, out, lse_sel,
+                lse_all, delta, tau, head);
+}
+
 __global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restrict__ lse_sel,
                                                            const float* __restrict__ lse_all,
                                                            float* __restrict__ delta,
@@ -222,21 +260,21 @@ __global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restri
 
 template <typename T, int D>
 void launch_split(const prhs_dims& d, const void* q, const void* k, const void* v, const int* idx,
-                  int idx_cap, const int* count, const float* scores, float* part, int nsplit,
-                  hipStream_t stream) {
+                  int idx_cap, const int* count, const float* sel_scores, const float* scores,
+                  float* part, int nsplit, hipStream_t stream) {
   dim3 grid(nsplit, d.batch * d.n_q_heads);
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
-  if (scores)
+  if (scores || sel_scores)
     hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(kDecThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, idx_cap, count, scores, d.n_q_heads,
+                       static_cast<const T*>(v), idx, idx_cap, count, sel_scores, scores, d.n_q_heads,
                        d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
                        (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
                        part, nsplit);
   else
     hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(kDecThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, idx_cap, count, scores, d.n_q_heads,
+                       static_cast<const T*>(v), idx, idx_cap, count, sel_scores, scores, d.n_q_heads,
                        d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
                        (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
                        part, nsplit);
@@ -245,17 +283,17 @@ void launch_split(const prhs_dims& d, const void* q, const void* k, const void* 
 }  // namespace
 
 hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const void* v,
-                         const int* idx, int idx_cap, const int* count, const float* scores,
-                         const float* lse_all, float* out, float* lse_sel, float* delta, float* tau,
-                         void* ws, hipStream_t stream) {
+                         const int* idx, int idx_cap, const int* count, const float* sel_scores,
+                         const float* scores, const float* lse_all, float* out, float* lse_sel,
+                         float* delta, float* tau, void* ws, hipStream_t stream) {
   const int nsplit = decode_nsplit(idx_cap);
   float* part = static_cast<float*>(ws);
   if (d.dtype == PRHS_F16) {
-    if (d.head_dim == 128) launch_split<__half, 128>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
-    else launch_split<__half, 64>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+    if (d.head_dim == 128) launch_split<__half, 128>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
+    else launch_split<__half, 64>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
   } else {
-    if (d.head_dim == 128) launch_split<float, 128>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
-    else launch_split<float, 64>(d, q, k, v, idx, idx_cap, count, scores, part, nsplit, stream);
+    if (d.head_dim == 128) launch_split<float, 128>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
+    else launch_split<float, 64>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
   }
   const int nheads = d.batch * d.n_q_heads;
   if (d.head_dim == 128)

@@ -75,18 +75,41 @@ int check_dims(const prhs_dims* d) {
   return PRHS_OK;
 }
 
-size_t score_ws(const prhs_dims* d) {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t score_part_bytes(const prhs_dims* d) {
   return (size_t)d->batch * d->n_q_heads * prhs::score_nchunks(*d) * 2 * sizeof(float);
 }
 
-size_t decode_ws(const prhs_dims* d, int cap) {
+size_t decode_part_bytes(const prhs_dims* d, int cap) {
   return (size_t)d->batch * d->n_q_heads * prhs::decode_nsplit(cap) * (d->head_dim + 2) *
          sizeof(float);
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t score_ws(const prhs_dims* d) { return score_part_bytes(d); }
 
-size_t step_ws(const prhs_dims* d, int cap) { return align256(score_ws(d)) + decode_ws(d, cap); }
+size_t decode_ws(const prhs_dims* d, int cap) { return decode_part_bytes(d, cap); }
+
+// Anchor-step workspace: scan partials | candidate counts | candidates |
+// selected scores | decode partials, each part 256-byte aligned.
+struct StepWs {
+  size_t part, cnt, cand, sel, dec, total;
+};
+
+StepWs step_ws_layout(const prhs_dims* d, int cap) {
+  const size_t heads = (size_t)d->batch * d->n_q_heads;
+  const size_t nch = (size_t)prhs::score_nchunks(*d);
+  StepWs w;
+  w.part = 0;
+  w.cnt = w.part + align256(score_part_bytes(d));
+  w.cand = w.cnt + align256(heads * nch * sizeof(uint32_t));
+  w.sel = w.cand + align256(heads * nch * prhs::kScoreChunk * sizeof(uint2));
+  w.dec = w.sel + align256(heads * (size_t)cap * sizeof(float));
+  w.total = w.dec + decode_part_bytes(d, cap);
+  return w;
+}
+
+size_t step_ws(const prhs_dims* d, int cap) { return step_ws_layout(d, cap).total; }
 
 }  // namespace
 
@@ -138,7 +161,7 @@ int prhs_score(const prhs_dims* dims, const void* q, const void* k, float* score
 
 int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* lse_all, int32_t mode,
                      int32_t n_budget, float delta_target, int32_t* idx, int32_t idx_cap,
-                     int32_t* count, int32_t* cap_hit, hipStream_t stream) {
+                     int32_t* count, int32_t* cap_hit, float* sel_scores, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
@@ -153,9 +176,18 @@ int prhs_select_topk(const prhs_dims* dims, const float* scores, const float* ls
     return fail(PRHS_E_BUDGET, "delta_target must lie in [0, 1]");
   if (idx_cap < n_budget)
     return fail(PRHS_E_CAPACITY, "idx_cap %d < n_budget %d", idx_cap, n_budget);
-  return finish(prhs::launch_select(*dims, scores, const_cast<float*>(lse_all), nullptr, mode,
-                                    n_budget, delta_target, idx, idx_cap, count, cap_hit, stream),
-                stream, "prhs_select_topk");
+  prhs::SelectArgs a;
+  a.scores = scores;
+  a.lse_all = const_cast<float*>(lse_all);  // read only: no partials are given
+  a.mode = mode;
+  a.n_budget = n_budget;
+  a.delta_target = delta_target;
+  a.idx = idx;
+  a.idx_cap = idx_cap;
+  a.count = count;
+  a.cap_hit = cap_hit;
+  a.sel_scores = sel_scores;
+  return finish(prhs::launch_select(*dims, a, stream), stream, "prhs_select_topk");
 }
 
 int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
@@ -182,13 +214,15 @@ int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anc
 
 int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
                        const int32_t* idx, int32_t idx_cap, const int32_t* count,
-                       const float* scores, const float* lse_all, float* out, float* lse_sel,
-                       float* delta, float* tau, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       const float* sel_scores, const float* scores, const float* lse_all,
+                       float* out, float* lse_sel, float* delta, float* tau, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!v || !idx || !count || !out || !lse_sel)
     return fail(PRHS_E_NULL, "v, idx, count, out and lse_sel are required");
-  if (!scores && (!q || !k)) return fail(PRHS_E_NULL, "without scores, q and k are required");
+  if (!scores && !sel_scores && (!q || !k))
+    return fail(PRHS_E_NULL, "without scores or sel_scores, q and k are required");
   if (delta && !lse_all) return fail(PRHS_E_NULL, "delta needs lse_all");
   if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
   if (!aligned16(v) || (k && !aligned16(k)) || (q && !aligned16(q)))
@@ -199,16 +233,16 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
     return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", decode_ws(dims, idx_cap),
                 ws_bytes);
   if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
-  return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
-                                    lse_sel, delta, tau, ws, stream),
+  return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel_scores, scores,
+                                    lse_all, out, lse_sel, delta, tau, ws, stream),
                 stream, "prhs_sparse_decode");
 }
 
 int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,
                      const void* q, const void* k, const void* v, float* scores, float* lse_all,
                      int32_t* idx, int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* out,
-                     float* lse_sel, float* delta, float* tau, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+                     float* lse_sel, float* delta, float* tau, float* theta, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
@@ -231,15 +265,38 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
                 ws_bytes);
   if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
   char* w = static_cast<char*>(ws);
-  void* score_part = w;
-  void* dec_part = w + align256(score_ws(dims));
-  hipError_t err = prhs::launch_score(*dims, q, k, scores, nullptr, score_part, stream);
+  const StepWs L = step_ws_layout(dims, idx_cap);
+  float2* part = reinterpret_cast<float2*>(w + L.part);
+  float* sel = reinterpret_cast<float*>(w + L.sel);
+  prhs::ScanCand cd;
+  const bool hint = theta != nullptr && mode == PRHS_TOPN;
+  if (hint) {
+    cd.theta = theta;
+    cd.cand = reinterpret_cast<uint2*>(w + L.cand);
+    cd.cand_cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+  }
+  hipError_t err = prhs::launch_score(*dims, q, k, scores, nullptr, part, stream, &cd);
+  if (err == hipSuccess) {
+    prhs::SelectArgs a;
+    a.scores = scores;
+    a.lse_all = lse_all;
+    a.part = part;
+    a.mode = mode;
+    a.n_budget = n_budget;
+    a.delta_target = delta_target;
+    a.idx = idx;
+    a.idx_cap = idx_cap;
+    a.count = count;
+    a.cap_hit = cap_hit;
+    a.sel_scores = sel;
+    a.cand = cd.cand;
+    a.cand_cnt = cd.cand_cnt;
+    a.theta_out = hint ? theta : nullptr;
+    err = prhs::launch_select(*dims, a, stream);
+  }
   if (err == hipSuccess)
-    err = prhs::launch_select(*dims, scores, lse_all, score_part, mode, n_budget, delta_target,
-                              idx, idx_cap, count, cap_hit, stream);
-  if (err == hipSuccess)
-    err = prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, scores, lse_all, out, lse_sel,
-                              delta, tau, dec_part, stream);
+    err = prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel, nullptr, lse_all, out,
+                              lse_sel, delta, tau, w + L.dec, stream);
   return finish(err, stream, "prhs_anchor_step");
 }
 

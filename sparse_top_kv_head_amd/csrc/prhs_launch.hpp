@@ -15,25 +15,58 @@ constexpr int kDecodeRows = 256;
 inline int score_nchunks(const prhs_dims& d) { return (d.ctx_len + kScoreChunk - 1) / kScoreChunk; }
 inline int decode_nsplit(int cap) { return (cap + kDecodeRows - 1) / kDecodeRows; }
 
+// Count marking a (head, chunk) for which no candidates were written.
+constexpr uint32_t kNoCand = 0xFFFFFFFFu;
+
+// Candidate output of the scan: keys whose score >= theta[head] (theta not
+// finite: none), as (score bits, index) in cand[head][chunk][0:kScoreChunk],
+// counts in cand_cnt[head][chunk]. All NULL: no candidate output.
+struct ScanCand {
+  const float* theta = nullptr;
+  uint2* cand = nullptr;
+  uint32_t* cand_cnt = nullptr;
+};
+
 // Writes scores; with ws, also the per-chunk (max, sum) partials of the dense
 // softmax; with lse_all (needs ws), also merges them into lse_all.
 hipError_t launch_score(const prhs_dims& d, const void* q, const void* k, float* scores,
-                        float* lse_all, void* ws, hipStream_t stream);
+                        float* lse_all, void* ws, hipStream_t stream,
+                        const ScanCand* cand = nullptr);
 
-// score_ws: when non-NULL, the per-chunk partials that launch_score left in
-// that workspace; the select kernel then merges them and writes lse_all
-// itself. Otherwise lse_all is an input (read in DELTA mode only).
-hipError_t launch_select(const prhs_dims& d, const float* scores, float* lse_all,
-                         const void* score_ws, int mode, int n_budget, float delta_target,
-                         int* idx, int idx_cap, int* count, int* cap_hit, hipStream_t stream);
+// Arguments of the selection kernel (t, ld and nchunks are filled in by
+// launch_select from the dims).
+struct SelectArgs {
+  const float* scores = nullptr;
+  float* lse_all = nullptr;       // read in DELTA mode unless part is given
+  const float2* part = nullptr;   // scan partials: merged into lse_all by the kernel
+  int mode = PRHS_TOPN;
+  int n_budget = 0;
+  float delta_target = 0.f;
+  int* idx = nullptr;
+  int idx_cap = 0;
+  int* count = nullptr;
+  int* cap_hit = nullptr;
+  float* sel_scores = nullptr;    // scores of the selected keys, in idx order
+  const uint2* cand = nullptr;    // scan candidates (TOPN)
+  const uint32_t* cand_cnt = nullptr;
+  float* theta_out = nullptr;     // next-step threshold hint (TOPN)
+  int t = 0;
+  int ld = 0;
+  int nchunks = 0;
+};
+
+hipError_t launch_select(const prhs_dims& d, const SelectArgs& a, hipStream_t stream);
 
 hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                       const int* anchor_count, int radius, const void* q_cur, const void* q_anchor,
                       float sim_tau, int* out_idx, int out_cap, int* out_count, int* reuse_ok,
                       hipStream_t stream);
 
+// Scores of the selected rows come from sel_scores (compact, in idx order) if
+// given, else are gathered from scores, else computed from gathered K rows.
 hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const void* v,
-                         const int* idx, int idx_cap, const int* count, const float* scores,
+                         const int* idx, int idx_cap, const int* count, const float* sel_scores,
+                         const float* scores,
                          const float* lse_all, float* out, float* lse_sel, float* delta, float* tau,
                          void* ws, hipStream_t stream);
 

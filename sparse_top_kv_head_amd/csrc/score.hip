@@ -19,11 +19,16 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
+// With `theta` (a per-head score threshold), the chunk's keys whose score is
+// >= theta are also written, in index order, as (score bits, index) pairs to
+// cand[head][chunk][0:n] with n in cand_cnt[head][chunk]; a head whose theta is
+// not finite gets the count kNoCand.
 template <typename T, int D, int G, int CHUNK = kScoreChunk, int UMAX = kScoreLoads>
 __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
-    float2* __restrict__ part, int Hq, int Hkv, int t, long long sb, long long sh, long long st,
-    int ld, int nchunks, int g_off, float scale) {
+    float2* __restrict__ part, const float* __restrict__ theta, uint2* __restrict__ cand,
+    uint32_t* __restrict__ cand_cnt, int Hq, int Hkv, int t, long long sb, long long sh,
+    long long st, int ld, int nchunks, int g_off, float scale) {
   constexpr int NW = kScoreThreads / kWave;
   constexpr int E = Elem<T>::kPer16B;
   constexpr int LPR = D / E;
@@ -33,8 +38,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   constexpr int ITERS = RW / (U * RPW);
   static_assert(G <= LPR, "one lane per head in a row group");
   static_assert(RW % (U * RPW) == 0, "chunk tiling");
+  static_assert(CHUNK == kScoreThreads, "candidate compaction maps one row per thread");
 
   __shared__ __align__(16) float sc[G][CHUNK];
+  __shared__ uint32_t wcnt[G][NW];
 
   const int chunk = blockIdx.x;
   const int unit = blockIdx.y;
@@ -93,6 +100,42 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
       }
     }
   }
+  if (theta != nullptr) {
+    // index-ordered compaction of the keys >= theta: ballot per wave, then
+    // the waves' counts give each wave its offset in the chunk's slot range
+    uint64_t hits[G];
+    float th[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      th[j] = theta[b * Hq + h0 + j];
+      const int r = w * kWave + lane;
+      const bool hit = __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
+      hits[j] = __ballot(hit);
+      if (lane == 0) wcnt[j][w] = (uint32_t)__popcll(hits[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
+      if (!__builtin_isfinite(th[j])) {
+        if (threadIdx.x == 0) cand_cnt[hc] = kNoCand;
+        continue;
+      }
+      uint32_t base = 0, total = 0;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        const uint32_t c = wcnt[j][u];
+        base += u < w ? c : 0u;
+        total += c;
+      }
+      const int r = w * kWave + lane;
+      if ((hits[j] >> lane) & 1ull) {
+        const uint32_t pos = base + (uint32_t)__popcll(hits[j] & ((1ull << lane) - 1ull));
+        cand[hc * CHUNK + pos] = make_uint2(__float_as_uint(sc[j][r]), (uint32_t)(base_row + r));
+      }
+      if (threadIdx.x == 0) cand_cnt[hc] = total;
+    }
+  }
   if (part != nullptr) {
     for (int j = w; j < G; j += NW) {
       float m = -INFINITY;
@@ -126,29 +169,29 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float2* __restrict
 
 template <typename T, int D, int G>
 void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores, float2* part,
-                 int g_off, hipStream_t stream) {
+                 const ScanCand& cd, int g_off, hipStream_t stream) {
   const int nchunks = score_nchunks(d);
   dim3 grid(nchunks, d.batch * d.n_kv_heads);
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
   hipLaunchKernelGGL((score_scan_kernel<T, D, G>), grid, dim3(kScoreThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), scores, part, d.n_q_heads,
-                     d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
+                     static_cast<const T*>(q), static_cast<const T*>(k), scores, part, cd.theta,
+                     cd.cand, cd.cand_cnt, d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
                      (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
 }
 
 template <typename T, int D>
 void launch_scan_group(const prhs_dims& d, const void* q, const void* k, float* scores,
-                       float2* part, int G, hipStream_t stream) {
+                       float2* part, const ScanCand& cd, int G, hipStream_t stream) {
   // Power-of-two sub-groups of the query heads that share one KV head.
   int off = 0;
   while (off < G) {
     const int rest = G - off;
     const int sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
     switch (sub) {
-      case 8: launch_scan<T, D, 8>(d, q, k, scores, part, off, stream); break;
-      case 4: launch_scan<T, D, 4>(d, q, k, scores, part, off, stream); break;
-      case 2: launch_scan<T, D, 2>(d, q, k, scores, part, off, stream); break;
-      default: launch_scan<T, D, 1>(d, q, k, scores, part, off, stream); break;
+      case 8: launch_scan<T, D, 8>(d, q, k, scores, part, cd, off, stream); break;
+      case 4: launch_scan<T, D, 4>(d, q, k, scores, part, cd, off, stream); break;
+      case 2: launch_scan<T, D, 2>(d, q, k, scores, part, cd, off, stream); break;
+      default: launch_scan<T, D, 1>(d, q, k, scores, part, cd, off, stream); break;
     }
     off += sub;
   }
@@ -157,15 +200,16 @@ void launch_scan_group(const prhs_dims& d, const void* q, const void* k, float* 
 }  // namespace
 
 hipError_t launch_score(const prhs_dims& d, const void* q, const void* k, float* scores,
-                        float* lse_all, void* ws, hipStream_t stream) {
+                        float* lse_all, void* ws, hipStream_t stream, const ScanCand* cand) {
   float2* part = static_cast<float2*>(ws);
+  const ScanCand cd = cand ? *cand : ScanCand{};
   const int G = d.n_q_heads / d.n_kv_heads;
   if (d.dtype == PRHS_F16) {
-    if (d.head_dim == 128) launch_scan_group<__half, 128>(d, q, k, scores, part, G, stream);
-    else launch_scan_group<__half, 64>(d, q, k, scores, part, G, stream);
+    if (d.head_dim == 128) launch_scan_group<__half, 128>(d, q, k, scores, part, cd, G, stream);
+    else launch_scan_group<__half, 64>(d, q, k, scores, part, cd, G, stream);
   } else {
-    if (d.head_dim == 128) launch_scan_group<float, 128>(d, q, k, scores, part, G, stream);
-    else launch_scan_group<float, 64>(d, q, k, scores, part, G, stream);
+    if (d.head_dim == 128) launch_scan_group<float, 128>(d, q, k, scores, part, cd, G, stream);
+    else launch_scan_group<float, 64>(d, q, k, scores, part, cd, G, stream);
   }
   if (lse_all) {
     const int nheads = d.batch * d.n_q_heads;

@@ -83,6 +83,7 @@ struct SelShared {
   uint2 cand[kCandCap + kWave];   // (key, index) of the fast path; key only otherwise; + dummies
   uint32_t gt_bits[kMaxWords];
   uint32_t eq_bits[kMaxWords];
+  uint32_t coff[kMaxWords / 8 + 1];   // candidate-chunk offsets (t / 256 chunks)
   uint32_t wtot[NT / kWave];
   uint32_t wtot2[NT / kWave];
   unsigned long long wmass[NT / kWave];
@@ -90,6 +91,7 @@ struct SelShared {
   uint32_t ncand;                 // fast-path list length
   uint32_t ncand_r;               // register-path list length
   uint32_t kmax;
+  uint32_t kmin;
   uint32_t digit;
   uint32_t above;
   uint32_t cT;
@@ -376,7 +378,9 @@ __device__ __forceinline__ void mark_from_regs(const Keys<KPT>& K, uint32_t T,
 // ascending index order: thread i owns WPT consecutive bitmap words.
 template <int NT, bool MASS>
 __device__ __forceinline__ void emit_bitmaps(int t, uint32_t take_eq, int* __restrict__ out,
-                                             uint32_t cap, SelShared<NT, MASS>& sh) {
+                                             float* __restrict__ out_s,
+                                             const float* __restrict__ row, uint32_t cap,
+                                             SelShared<NT, MASS>& sh) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -423,7 +427,10 @@ __device__ __forceinline__ void emit_bitmaps(int t, uint32_t take_eq, int* __res
     while (sel) {
       const int b = __builtin_ctz(sel);
       sel &= sel - 1;
-      if (pos < cap) out[pos] = base_i + b;
+      if (pos < cap) {
+        out[pos] = base_i + b;
+        if (out_s) out_s[pos] = row[base_i + b];
+      }
       ++pos;
     }
   }
@@ -501,6 +508,36 @@ __device__ __forceinline__ void find_count_w0(uint32_t krem, SelShared<NT, MASS>
   __syncthreads();
 }
 
+// Exact N-th largest key among the C candidate keys in sh.cand[].x, all of
+// them in [lo, hi]: radix passes with 12-bit digits of key - lo. Returns the
+// boundary key T and take_eq, the number of keys equal to T that are taken.
+template <int NT, bool MASS>
+__device__ __forceinline__ void cand_radix(uint32_t lo, uint32_t hi, uint32_t C, uint32_t N,
+                                           uint32_t& T, uint32_t& take_eq,
+                                           SelShared<NT, MASS>& sh) {
+  const uint32_t range = hi - lo;
+  int shift = range ? 32 - __builtin_clz(range) - 12 : 0;
+  shift = shift > 0 ? shift : 0;
+  uint32_t pre = 0, pmask = 0, krem = N;
+#pragma unroll 1
+  while (true) {
+    if (threadIdx.x == 0) sh.digit = 0;
+    for (int c = threadIdx.x; c < (int)C; c += NT) {
+      const uint32_t o = sh.cand[c].x - lo;
+      if ((o & pmask) == pre) atomicAdd(&sh.hist[swz_slot<4096, 1>((o >> shift) & 4095u, 0)], 1u);
+    }
+    __syncthreads();
+    find_count_w0<4096, 1, NT, MASS>(krem, sh);
+    krem -= sh.above;
+    pre |= sh.digit << shift;
+    pmask |= 4095u << shift;
+    if (shift == 0) break;
+    shift = shift > 12 ? shift - 12 : 0;
+  }
+  T = lo + pre;
+  take_eq = krem;
+}
+
 // Try the sampled-threshold path. Returns false (nothing written to the
 // output) when the threshold does not leave between N and kCandCap keys;
 // otherwise T and take_eq describe the result and the bitmaps are marked.
@@ -574,28 +611,7 @@ __device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N,
   const uint32_t C = sh.ncand;
   if (C < N || C > (uint32_t)kCandCap) return false;
 
-  // exact N-th largest among the candidates: 12-bit digits of key - theta
-  const uint32_t range = sh.kmax - theta;
-  int shift = range ? 32 - __builtin_clz(range) - 12 : 0;
-  shift = shift > 0 ? shift : 0;
-  uint32_t pre = 0, pmask = 0, krem = N;
-#pragma unroll 1
-  while (true) {
-    if (threadIdx.x == 0) sh.digit = 0;
-    for (int c = threadIdx.x; c < (int)C; c += NT) {
-      const uint32_t o = sh.cand[c].x - theta;
-      if ((o & pmask) == pre) atomicAdd(&sh.hist[swz_slot<4096, 1>((o >> shift) & 4095u, 0)], 1u);
-    }
-    __syncthreads();
-    find_count_w0<4096, 1, NT, MASS>(krem, sh);
-    krem -= sh.above;
-    pre |= sh.digit << shift;
-    pmask |= 4095u << shift;
-    if (shift == 0) break;
-    shift = shift > 12 ? shift - 12 : 0;
-  }
-  T = theta + pre;
-  take_eq = krem;
+  cand_radix<NT, MASS>(theta, sh.kmax, C, N, T, take_eq, sh);
   // mark the result bits from the candidate list
   for (int c = threadIdx.x; c < (int)C; c += NT) {
     const uint2 ki = sh.cand[c];
@@ -604,6 +620,135 @@ __device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N,
   }
   __syncthreads();
   return true;
+}
+
+// ---------------------------------------------------------------------------
+// TOPN from the scan's candidates (keys >= a per-head threshold hint).
+// ---------------------------------------------------------------------------
+
+// Write the candidates above T and the first take_eq equal to T, in the list's
+// (index) order, with their scores. Thread i owns a contiguous block of the list.
+template <int NT, bool MASS>
+__device__ __forceinline__ void emit_list(uint32_t C, uint32_t T, uint32_t take_eq,
+                                          int* __restrict__ out, float* __restrict__ out_s,
+                                          uint32_t cap, SelShared<NT, MASS>& sh) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const uint32_t cpt = (C + NT - 1) / NT;
+  const uint32_t beg = threadIdx.x * cpt;
+  const uint32_t end = beg + cpt < C ? beg + cpt : C;
+  uint32_t ng = 0, ne = 0;
+  for (uint32_t c = beg; c < end; ++c) {
+    const uint32_t key = sh.cand[c].x;
+    ng += key > T;
+    ne += key == T;
+  }
+  const uint32_t ginc = wave_scan_u32(ng);
+  const uint32_t einc = wave_scan_u32(ne);
+  if (lane == kWave - 1) {
+    sh.wtot[w] = ginc;
+    sh.wtot2[w] = einc;
+  }
+  __syncthreads();
+  uint32_t gb = ginc - ng, eb = einc - ne;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    if (u < w) {
+      gb += sh.wtot[u];
+      eb += sh.wtot2[u];
+    }
+  }
+  uint32_t pos = gb + (eb < take_eq ? eb : take_eq);
+  uint32_t eq_left = take_eq > eb ? take_eq - eb : 0u;
+  for (uint32_t c = beg; c < end; ++c) {
+    const uint2 ki = sh.cand[c];
+    bool sel = ki.x > T;
+    if (ki.x == T && eq_left) {
+      sel = true;
+      --eq_left;
+    }
+    if (sel) {
+      if (pos < cap) {
+        out[pos] = (int)ki.y;
+        if (out_s) out_s[pos] = key_to_score(ki.x);
+      }
+      ++pos;
+    }
+  }
+}
+
+// Gather the head's scan candidates (chunk by chunk, so in index order) into
+// sh.cand as (key, index). Returns false, with nothing written, when a chunk
+// carries no candidates or the total is outside [N, kCandCap].
+template <int NT, bool MASS>
+__device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand,
+                                                  const uint32_t* __restrict__ cand_cnt,
+                                                  int head, int nch, uint32_t N, uint32_t& C,
+                                                  SelShared<NT, MASS>& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t c = (int)threadIdx.x < nch ? cand_cnt[(size_t)head * nch + threadIdx.x] : 0u;
+  if (__syncthreads_or(c == kNoCand)) return false;
+  uint32_t total;
+  const uint32_t ex = block_exclusive_scan<NT>(c, sh.wtot, total);
+  if ((int)threadIdx.x < nch) sh.coff[threadIdx.x] = ex;
+  if (threadIdx.x == 0) {
+    sh.coff[nch] = total;
+    sh.kmax = 0;
+    sh.kmin = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  C = total;
+  if (C < N || C > (uint32_t)kCandCap) return false;
+  // all of a thread's loads are issued before any is used
+  constexpr int PER = (kCandCap + NT - 1) / NT;
+  uint2 e[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t p = threadIdx.x + (uint32_t)j * NT;
+    e[j] = make_uint2(0, 0);
+    if (p < C) {
+      int a = 0, b = nch - 1;  // last chunk whose offset <= p
+      while (a < b) {
+        const int mid = (a + b + 1) >> 1;
+        if (sh.coff[mid] <= p) a = mid;
+        else b = mid - 1;
+      }
+      e[j] = cand[((size_t)head * nch + a) * kScoreChunk + (p - sh.coff[a])];
+    }
+  }
+  uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t p = threadIdx.x + (uint32_t)j * NT;
+    if (p < C) {
+      const uint32_t key = score_key(__uint_as_float(e[j].x));
+      sh.cand[p] = make_uint2(key, e[j].y);
+      kmx = key > kmx ? key : kmx;
+      kmn = key < kmn ? key : kmn;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(kmx, o);
+    const uint32_t z = __shfl_xor(kmn, o);
+    kmx = y > kmx ? y : kmx;
+    kmn = z < kmn ? z : kmn;
+  }
+  if (lane == 0) {
+    atomicMax(&sh.kmax, kmx);
+    atomicMin(&sh.kmin, kmn);
+  }
+  __syncthreads();
+  return true;
+}
+
+// Threshold hint for the next step of the same head: the boundary score less
+// a margin that grows with the spread between the top score and the boundary.
+__device__ __forceinline__ float next_theta(uint32_t T, uint32_t kmax) {
+  const float ts = key_to_score(T), ms = key_to_score(kmax);
+  const float spread = ms - ts;
+  return ts - (0.1f * (spread > 0.f ? spread : 0.f) + 0.05f);
 }
 
 // Load the head's scores as keys: wave w owns [w*64*KPT, (w+1)*64*KPT), lane
@@ -641,29 +786,29 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
 
 // lse_all is read (DELTA) unless `part` is given: then the head's per-chunk
 // (max, sum) partials of the score scan are merged here, the result used and
-// written to lse_all.
+// written to lse_all. TOPN with scan candidates (cand != NULL) selects from
+// them when they hold the answer and otherwise falls back to the full path.
 template <int KPT, int NT, int MODE>
-__global__ __launch_bounds__(NT) void select_kernel(
-    const float* __restrict__ scores, float* __restrict__ lse_all,
-    const float2* __restrict__ part, int nchunks, int t, int ld, int n_budget,
-    float delta_target, int* __restrict__ idx, int idx_cap, int* __restrict__ count,
-    int* __restrict__ cap_hit) {
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr bool MASS = MODE == PRHS_DELTA;
   __shared__ SelShared<NT, MASS> sh;
 
   const int head = blockIdx.x;
-  const float* row = scores + (size_t)head * ld;
-  if (part != nullptr && threadIdx.x < kWave) {
+  const int t = a.t;
+  const float* row = a.scores + (size_t)head * a.ld;
+  int* out = a.idx + (size_t)head * a.idx_cap;
+  float* out_s = a.sel_scores ? a.sel_scores + (size_t)head * a.idx_cap : nullptr;
+  if (a.part != nullptr && threadIdx.x < kWave) {
     float m = -INFINITY, l = 0.f;
-    for (int c = threadIdx.x; c < nchunks; c += kWave) {
-      const float2 pc = part[(size_t)head * nchunks + c];
+    for (int c = threadIdx.x; c < a.nchunks; c += kWave) {
+      const float2 pc = a.part[(size_t)head * a.nchunks + c];
       ml_combine(m, l, pc.x, pc.y);
     }
     wave_ml(m, l);
     if (threadIdx.x == 0) {
       const float lse = l > 0.f ? m + __logf(l) : -INFINITY;
       sh.lse = lse;
-      lse_all[head] = lse;
+      a.lse_all[head] = lse;
     }
   }
 
@@ -676,53 +821,86 @@ __global__ __launch_bounds__(NT) void select_kernel(
     sh.eq_bits[i] = 0;
   }
 
+  if constexpr (!MASS) {
+    uint32_t C = 0;
+    if (a.cand != nullptr &&
+        gather_candidates<NT, MASS>(a.cand, a.cand_cnt, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
+      uint32_t T, take;
+      cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
+      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh);
+      if (threadIdx.x == 0) {
+        a.count[head] = a.n_budget;
+        if (a.cap_hit) a.cap_hit[head] = 0;
+        if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+      }
+      return;
+    }
+  }
+
   Keys<KPT> K;
   load_keys<KPT>(K, row, t);
   __syncthreads();
 
   uint32_t T = 0, take = 0;
-  int n_sel = n_budget;
+  int n_sel = a.n_budget;
   int hit = 0;
   if constexpr (MASS) {
-    const float lse = part != nullptr ? sh.lse : lse_all[head];
-    const unsigned long long budget = (unsigned long long)((double)delta_target * kMassScale);
+    const float lse = a.part != nullptr ? sh.lse : a.lse_all[head];
+    const unsigned long long budget = (unsigned long long)((double)a.delta_target * kMassScale);
     uint32_t n_above = 0, take_T = 0;
     const bool found = mass_search<KPT, NT>(K, lse, budget, T, n_above, take_T, sh);
-    if (found && (int)(n_above + take_T) <= n_budget) {
+    if (found && (int)(n_above + take_T) <= a.n_budget) {
       n_sel = (int)(n_above + take_T);
       take = take_T;
     } else {
       hit = found ? 1 : 0;
-      n_sel = found ? n_budget : 1;
+      n_sel = found ? a.n_budget : 1;
       take = (uint32_t)n_sel;
       T = count_search<KPT, NT, MASS>(K, take, sh);
     }
     mark_from_regs<KPT, NT, MASS>(K, T, sh);
   } else {
-    if (!topn_fast<KPT, NT, MASS>(K, t, (uint32_t)n_budget, T, take, sh)) {
+    if (!topn_fast<KPT, NT, MASS>(K, t, (uint32_t)a.n_budget, T, take, sh)) {
       load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die
-      take = (uint32_t)n_budget;
+      take = (uint32_t)a.n_budget;
       T = count_search<KPT, NT, MASS>(K, take, sh);
       mark_from_regs<KPT, NT, MASS>(K, T, sh);
     }
   }
-  emit_bitmaps<NT, MASS>(t, take, idx + (size_t)head * idx_cap, (uint32_t)idx_cap, sh);
+  emit_bitmaps<NT, MASS>(t, take, out, out_s, row, (uint32_t)a.idx_cap, sh);
   if (threadIdx.x == 0) {
-    count[head] = n_sel;
-    if (cap_hit) cap_hit[head] = hit;
+    a.count[head] = n_sel;
+    if (a.cap_hit) a.cap_hit[head] = hit;
+  }
+  if constexpr (!MASS) {
+    if (a.theta_out) {
+      // the head's top key, for the next step's threshold hint
+      uint32_t kmx = 0;
+      for (int i = threadIdx.x; i < t; i += NT) {
+        const uint32_t key = score_key(row[i]);
+        kmx = key > kmx ? key : kmx;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t y = __shfl_xor(kmx, o);
+        kmx = y > kmx ? y : kmx;
+      }
+      if (threadIdx.x == 0) sh.kmax = 0;
+      __syncthreads();
+      if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh.kmax, kmx);
+      __syncthreads();
+      if (threadIdx.x == 0) a.theta_out[head] = next_theta(T, sh.kmax);
+    }
   }
 }
 
 constexpr int kSelThreads = 1024;
 
 template <int MODE>
-void launch_mode(int kpt, int nheads, const float* scores, float* lse_all, const float2* part,
-                 int nchunks, int t, int ld, int n_budget, float delta_target, int* idx,
-                 int idx_cap, int* count, int* cap_hit, hipStream_t stream) {
+void launch_mode(int kpt, int nheads, const SelectArgs& a, hipStream_t stream) {
 #define PRHS_SEL(K)                                                                          \
   hipLaunchKernelGGL((select_kernel<K, kSelThreads, MODE>), dim3(nheads), dim3(kSelThreads), 0, \
-                     stream, scores, lse_all, part, nchunks, t, ld, n_budget, delta_target, idx, \
-                     idx_cap, count, cap_hit)
+                     stream, a)
   switch (kpt) {
     case 1: PRHS_SEL(1); break;
     case 2: PRHS_SEL(2); break;
@@ -737,20 +915,16 @@ void launch_mode(int kpt, int nheads, const float* scores, float* lse_all, const
 
 }  // namespace
 
-hipError_t launch_select(const prhs_dims& d, const float* scores, float* lse_all,
-                         const void* score_ws, int mode, int n_budget, float delta_target,
-                         int* idx, int idx_cap, int* count, int* cap_hit, hipStream_t stream) {
+hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t stream) {
   int kpt = 1;
   while (kpt * kSelThreads < d.ctx_len) kpt *= 2;
   const int nheads = d.batch * d.n_q_heads;
-  const float2* part = static_cast<const float2*>(score_ws);
-  const int nch = score_nchunks(d);
-  if (mode == PRHS_DELTA)
-    launch_mode<PRHS_DELTA>(kpt, nheads, scores, lse_all, part, nch, d.ctx_len, d.scores_ld,
-                            n_budget, delta_target, idx, idx_cap, count, cap_hit, stream);
-  else
-    launch_mode<PRHS_TOPN>(kpt, nheads, scores, lse_all, part, nch, d.ctx_len, d.scores_ld,
-                           n_budget, delta_target, idx, idx_cap, count, cap_hit, stream);
+  SelectArgs a = args;
+  a.t = d.ctx_len;
+  a.ld = d.scores_ld;
+  a.nchunks = score_nchunks(d);
+  if (a.mode == PRHS_DELTA) launch_mode<PRHS_DELTA>(kpt, nheads, a, stream);
+  else launch_mode<PRHS_TOPN>(kpt, nheads, a, stream);
   return hipGetLastError();
 }
 

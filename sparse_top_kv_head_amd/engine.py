@@ -36,6 +36,9 @@ class DecodeEngine:
         self.delta = torch.empty((d.batch, d.n_q_heads), **f32)
         self.tau = torch.empty((d.batch, d.n_q_heads), **f32)
         self.reuse_ok = torch.empty((d.batch, d.n_q_heads), **i32)
+        self.sel_scores = torch.empty((d.batch, d.n_q_heads, cap), **f32)
+        # per-head score threshold hint carried from one anchor step to the next
+        self.theta = torch.full((d.batch, d.n_q_heads), float("nan"), **f32)
         ws = max(P.prhs_workspace_bytes(d, P.PRHS_OP_SCORE),
                  P.prhs_workspace_bytes(d, P.PRHS_OP_DECODE, cap),
                  P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, cap))
@@ -46,7 +49,8 @@ class DecodeEngine:
 
     def select(self, mode, n_budget, delta_target=0.0, stream=None):
         P.prhs_select_topk(self.dims, self.scores, self.lse_all, mode, n_budget, delta_target,
-                           self.idx, self.cap, self.count, self.cap_hit, stream=stream)
+                           self.idx, self.cap, self.count, self.cap_hit, self.sel_scores,
+                           stream=stream)
 
     def decode(self, q, K, V, use_scores=True, idx=None, count=None, cap=None, stream=None):
         idx = self.idx if idx is None else idx
@@ -58,11 +62,15 @@ class DecodeEngine:
                              self.delta if use_scores else None, self.tau if use_scores else None,
                              self.ws, stream=stream)
 
-    def anchor_step(self, q, K, V, mode, n_budget, delta_target=0.0, stream=None):
-        """One fused call: score scan, selection, sparse attention with delta/tau."""
+    def anchor_step(self, q, K, V, mode, n_budget, delta_target=0.0, stream=None, hint=True):
+        """One fused call: score scan, selection, sparse attention with delta/tau.
+
+        hint: carry the per-head threshold hint between anchor steps (TOPN).
+        """
         P.prhs_anchor_step(self.dims, mode, n_budget, delta_target, q, K, V, self.scores,
                            self.lse_all, self.idx, self.cap, self.count, self.cap_hit, self.out,
-                           self.lse_sel, self.delta, self.tau, self.ws, stream=stream)
+                           self.lse_sel, self.delta, self.tau, self.theta if hint else None,
+                           self.ws, stream=stream)
 
     def topn_step(self, q, K, V, N, stream=None):
         """Anchor step: exact top-N over fresh scores, then attention over it."""

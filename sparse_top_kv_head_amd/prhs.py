@@ -80,12 +80,13 @@ def lib():
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         dp = ctypes.POINTER(PrhsDims)
         L.prhs_score.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
-        L.prhs_select_topk.argtypes = [dp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp]
+        L.prhs_select_topk.argtypes = [dp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp]
         L.prhs_cis_reuse.argtypes = [dp, vp, i32, vp, i32, vp, vp, f32, vp, i32, vp, vp, vp]
-        L.prhs_sparse_decode.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.prhs_sparse_decode.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
-                                       vp, vp, vp, vp, sz, vp]
+                                       vp, vp, vp, vp, vp, sz, vp]
         L.prhs_workspace_bytes.argtypes = [dp, i32, i32]
         L.prhs_workspace_bytes.restype = sz
         L.prhs_status_string.argtypes = [ctypes.c_int]
@@ -140,6 +141,12 @@ def prhs_workspace_bytes(dims: PrhsDims, op: int, cap: int = 0) -> int:
     return int(lib().prhs_workspace_bytes(ctypes.byref(dims), op, cap))
 
 
+def alloc_workspace(dims, op, cap=0, device="cuda"):
+    """A workspace of the size `op` needs (16-byte aligned)."""
+    n = prhs_workspace_bytes(dims, op, cap)
+    return torch.empty(((n + 15) // 16 * 16,), dtype=torch.uint8, device=device)
+
+
 def prhs_status_string(status: int) -> str:
     return lib().prhs_status_string(status).decode()
 
@@ -152,10 +159,10 @@ def prhs_score(dims, q, k, scores, lse_all=None, ws=None, ws_bytes=None, stream=
 
 
 def prhs_select_topk(dims, scores, lse_all, mode, n_budget, delta_target, idx, idx_cap, count,
-                     cap_hit=None, stream=None):
+                     cap_hit=None, sel_scores=None, stream=None):
     _check(lib().prhs_select_topk(ctypes.byref(dims), _p(scores), _p(lse_all), mode, n_budget,
                                   delta_target, _p(idx), idx_cap, _p(count), _p(cap_hit),
-                                  _stream(stream)))
+                                  _p(sel_scores), _stream(stream)))
 
 
 def prhs_cis_reuse(dims, anchor_idx, anchor_cap, anchor_count, radius, q_cur, q_anchor, sim_tau,
@@ -166,12 +173,13 @@ def prhs_cis_reuse(dims, anchor_idx, anchor_cap, anchor_count, radius, q_cur, q_
 
 
 def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out, lse_sel,
-                       delta=None, tau=None, ws=None, ws_bytes=None, stream=None):
+                       delta=None, tau=None, ws=None, ws_bytes=None, sel_scores=None, stream=None):
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
     _check(lib().prhs_sparse_decode(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(idx), idx_cap,
-                                    _p(count), _p(scores), _p(lse_all), _p(out), _p(lse_sel),
-                                    _p(delta), _p(tau), _p(ws), ws_bytes, _stream(stream)))
+                                    _p(count), _p(sel_scores), _p(scores), _p(lse_all), _p(out),
+                                    _p(lse_sel), _p(delta), _p(tau), _p(ws), ws_bytes,
+                                    _stream(stream)))
 
 
 def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):
@@ -180,11 +188,11 @@ def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):
 
 
 def prhs_anchor_step(dims, mode, n_budget, delta_target, q, k, v, scores, lse_all, idx, idx_cap,
-                     count, cap_hit, out, lse_sel, delta=None, tau=None, ws=None, ws_bytes=None,
-                     stream=None):
+                     count, cap_hit, out, lse_sel, delta=None, tau=None, theta=None, ws=None,
+                     ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
     _check(lib().prhs_anchor_step(ctypes.byref(dims), mode, n_budget, delta_target, _p(q), _p(k),
                                   _p(v), _p(scores), _p(lse_all), _p(idx), idx_cap, _p(count),
-                                  _p(cap_hit), _p(out), _p(lse_sel), _p(delta), _p(tau), _p(ws),
-                                  ws_bytes, _stream(stream)))
+                                  _p(cap_hit), _p(out), _p(lse_sel), _p(delta), _p(tau),
+                                  _p(theta), _p(ws), ws_bytes, _stream(stream)))

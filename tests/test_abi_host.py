@@ -50,7 +50,7 @@ def _score(L, d, q=FAKE, k=FAKE, s=FAKE, lse=None, ws=None, wsb=0):
 
 def _select(L, d, scores=FAKE, lse=FAKE, mode=P.PRHS_TOPN, n=64, dt=0.05, idx=FAKE, cap=64, cnt=FAKE):
     return L.prhs_select_topk(ctypes.byref(d) if d is not None else None, scores, lse, mode, n, dt,
-                              idx, cap, cnt, None, None)
+                              idx, cap, cnt, None, None, None)
 
 
 def _cis(L, d, a=FAKE, acap=64, acnt=FAKE, r=2, qc=None, qa=None, tau=0.8, o=FAKE, ocap=320,
@@ -60,11 +60,11 @@ def _cis(L, d, a=FAKE, acap=64, acnt=FAKE, r=2, qc=None, qa=None, tau=0.8, o=FAK
 
 
 def _decode(L, d, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cap=64, cnt=FAKE, s=FAKE, lse=FAKE, out=FAKE,
-            lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None):
+            lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None, sel=None):
     if wsb is None:
         wsb = 1 << 30
     return L.prhs_sparse_decode(ctypes.byref(d) if d is not None else None, q, k, v, idx, cap, cnt,
-                                s, lse, out, lsel, dl, tau, ws, wsb, None)
+                                sel, s, lse, out, lsel, dl, tau, ws, wsb, None)
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -104,7 +104,7 @@ def test_null_dims(L):
 def test_score_argument_checks(L):
     d = _dims()
     need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0)
-    assert need == 2 * 8 * 1 * 8          # B*H_q*chunks*(max, sum)
+    assert need == 2 * 8 * 4 * 8          # B*H_q*chunks(256 keys)*(max, sum)
     assert _score(L, d, q=None) == P.PRHS_E_NULL
     assert _score(L, d, k=None) == P.PRHS_E_NULL
     assert _score(L, d, s=None) == P.PRHS_E_NULL
@@ -157,6 +157,7 @@ def test_decode_argument_checks(L):
     assert _decode(L, d, lsel=None) == P.PRHS_E_NULL
     assert _decode(L, d, s=None, k=None) == P.PRHS_E_NULL
     assert _decode(L, d, s=None, q=None) == P.PRHS_E_NULL
+    assert _decode(L, d, s=None, q=None, k=None, cap=0, sel=FAKE) == P.PRHS_E_CAPACITY  # sel_scores suffice
     assert _decode(L, d, lse=None) == P.PRHS_E_NULL              # delta without lse_all
     assert _decode(L, d, dl=None) == P.PRHS_E_NULL               # tau without delta
     assert _decode(L, d, cap=0) == P.PRHS_E_CAPACITY
@@ -168,18 +169,21 @@ def test_decode_argument_checks(L):
 
 
 def _step(L, d, mode=P.PRHS_TOPN, n=64, dt=0.05, q=FAKE, k=FAKE, v=FAKE, s=FAKE, lse=FAKE,
-          idx=FAKE, cap=64, cnt=FAKE, out=FAKE, lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None):
+          idx=FAKE, cap=64, cnt=FAKE, out=FAKE, lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None,
+          theta=None):
     if wsb is None:
         wsb = 1 << 30
     return L.prhs_anchor_step(ctypes.byref(d) if d is not None else None, mode, n, dt, q, k, v, s,
-                              lse, idx, cap, cnt, None, out, lsel, dl, tau, ws, wsb, None)
+                              lse, idx, cap, cnt, None, out, lsel, dl, tau, theta, ws, wsb, None)
 
 
 def test_anchor_step_argument_checks(L):
     d = _dims()
     need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_ANCHOR_STEP, 64)
-    part = 2 * 8 * 1 * 8
-    assert need == (part + 255) // 256 * 256 + 2 * 8 * 1 * (128 + 2) * 4
+    heads, nch = 2 * 8, (1000 + 255) // 256
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert need == (a256(heads * nch * 8) + a256(heads * nch * 4) + a256(heads * nch * 256 * 8)
+                    + a256(heads * 64 * 4) + heads * 1 * (128 + 2) * 4)
     assert _step(L, None) == P.PRHS_E_NULL
     assert _step(L, _dims(head_dim=96)) == P.PRHS_E_DIMS
     assert _step(L, _dims(ctx_len=P.PRHS_MAX_SELECT_CTX + 1, scores_ld=P.PRHS_MAX_SELECT_CTX + 4)) == P.PRHS_E_DIMS

@@ -66,7 +66,7 @@ def test_score_and_lse(B, Hq, Hkv, d, t, dtype, pad):
     dims = P.make_dims(K, Hq)
     scores = torch.full((B, Hq, dims.scores_ld), float("nan"), device=dev)
     lse = torch.empty((B, Hq), device=dev)
-    ws = torch.empty(P.prhs_workspace_bytes(dims, P.PRHS_OP_SCORE), dtype=torch.uint8, device=dev)
+    ws = P.alloc_workspace(dims, P.PRHS_OP_SCORE, device=dev)
     P.prhs_score(dims, q, K, scores, lse, ws)
     torch.cuda.synchronize()
     bound, s_ref = score_bound(_np(q), _np(K))
@@ -316,7 +316,7 @@ def test_sparse_decode(B, Hq, Hkv, d, t, dtype, N, with_scores):
     delta = torch.empty((B, Hq), device=dev)
     tau = torch.empty((B, Hq), device=dev)
     lse_all = torch.from_numpy(lse.astype(np.float32)).to(dev)
-    ws = torch.empty(P.prhs_workspace_bytes(dims, P.PRHS_OP_DECODE, cap), dtype=torch.uint8, device=dev)
+    ws = P.alloc_workspace(dims, P.PRHS_OP_DECODE, cap, device=dev)
     P.prhs_sparse_decode(dims, q, K, V, idx.to(dev), cap, cnt.to(dev),
                          scores.to(dev) if with_scores else None, lse_all, out, lse_sel, delta, tau, ws)
     torch.cuda.synchronize()
@@ -351,7 +351,7 @@ def test_sparse_decode_edge_counts():
     dims = P.make_dims(K, H)
     out = torch.empty((B, H, d), device=dev)
     lse_sel = torch.empty((B, H), device=dev)
-    ws = torch.empty(P.prhs_workspace_bytes(dims, P.PRHS_OP_DECODE, cap), dtype=torch.uint8, device=dev)
+    ws = P.alloc_workspace(dims, P.PRHS_OP_DECODE, cap, device=dev)
     P.prhs_sparse_decode(dims, q, K, V, idx.to(dev), cap, cnt.to(dev), None, None, out, lse_sel,
                          None, None, ws)
     torch.cuda.synchronize()
@@ -444,3 +444,37 @@ def test_anchor_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for n in names:
             assert torch.equal(getattr(eng, n), ref[n]), (r, n)
+
+
+# ---------------------------------------------------------------------------
+# Threshold hints: results never depend on the hint.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ctx", [32768, 4096])
+def test_anchor_step_hint_exact(ctx):
+    """Steps with the carried hint, and with hints forced too high, too low and
+    absent, give the same indices, scores and outputs as steps without a hint."""
+    dev = _dev()
+    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=1, ctx_len=ctx, budget=min(2048, ctx // 8),
+                                             steps=4, n_clusters=(64, 64))
+    w = make_workload(cfg, device=dev)
+    hinted = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    plain = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    names = ("idx", "count", "out", "lse_sel", "delta", "tau", "lse_all")
+    forced = {2: 1e30, 3: -1e30}
+    for step in range(cfg.steps):
+        if step in forced:
+            hinted.theta.fill_(forced[step])
+        hinted.anchor_step(w.q[step], w.K, w.V, P.PRHS_TOPN, cfg.budget)
+        plain.anchor_step(w.q[step], w.K, w.V, P.PRHS_TOPN, cfg.budget, hint=False)
+        torch.cuda.synchronize()
+        assert torch.isfinite(hinted.theta).all()
+        for n in names:
+            a, b = getattr(hinted, n), getattr(plain, n)
+            if n == "idx":
+                for h in range(cfg.n_q_heads):
+                    c = int(plain.count[0, h])
+                    assert torch.equal(a[0, h, :c], b[0, h, :c]), (step, h)
+            else:
+                assert torch.equal(a, b), (step, n)
