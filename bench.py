@@ -2,17 +2,23 @@
 
 One step = one pass of the whole hot path over one decode query batch:
 score (K scan) -> exact top-N select -> sparse attention over the selected
-rows with the fused dropped mass, on the Mistral-7B-shaped GQA layer with a
-32K context (batch 4, 32 query heads on 8 KV heads, d = 128, fp16, N = 2048).
+rows with the fused dropped mass. The headline workload is the
+Mistral-7B-shaped GQA layer with a 32K context (batch 4, 32 query heads on 8
+KV heads, d = 128, fp16, N = 2048).
 
 Prints one JSON line. ``value`` is heads*steps/s over the timed steps with
 inputs resident in HBM; the timed steps are captured once as a HIP graph and
-replayed (the eager per-call rate is reported beside it). Independent copies of K and V are rotated so that no
-step finds its KV cache in the 256 MB Infinity Cache left by the previous
-one. ``roofline`` reports the scan kernel (the dominant kernel): algorithmic
-bytes (the K cache it must read) over its mean duration from HIP events on
-the launch stream. ``cpu_baseline`` times the fp64 numpy oracle on a bounded
-sample of the same workload.
+replayed (the eager per-step times, from events between steps, give the
+p10/p50/p90). Independent copies of K and V are rotated so that no step finds
+its KV cache in the 256 MB Infinity Cache left by the previous one.
+``roofline`` reports the scan kernel (the dominant kernel): algorithmic bytes
+(the K cache it must read) over its mean duration from HIP events on the
+launch stream. ``stream_read_ceiling`` is a plain read of 4 GiB with the
+library's probe kernel. ``configs`` reports the other workloads the same way:
+the LLaMA2-7B-shaped layer (top-256 of 4K), the CIS-reuse decode (anchor,
+reuse and amortised steps), the delta-budgeted layers (literal and sharp
+query scale) and the toy. ``cpu_baseline`` times the fp64 numpy oracle on a
+bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -60,9 +66,71 @@ def _parse():
     ap.add_argument("--rotate", type=int, default=4, help="independent KV copies cycled over steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def pct(a):
+    return [round(float(np.percentile(a, p)), 5) for p in (10, 50, 90)]
+
+
+def timed_steps(step_fns, stream):
+    """Run the steps eagerly with events between them, then capture the same
+    sequence once as a HIP graph and replay it.
+
+    Returns (per-step eager ms, graph replay ms for the whole sequence)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(step_fns) + 1)]
+    evs[0].record(stream)
+    for i, f in enumerate(step_fns):
+        f()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(len(step_fns))])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in step_fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return per, a.elapsed_time(b)
+
+
+def distinct_rows(idx, cnt, G):
+    """Distinct (b, kv head, row) triples over the selected sets."""
+    idx = idx.cpu().numpy()
+    cnt = cnt.cpu().numpy()
+    B, Hq = cnt.shape
+    rows = 0
+    for b in range(B):
+        for g in range(Hq // G):
+            sets = [idx[b, h, :cnt[b, h]] for h in range(g * G, (g + 1) * G)]
+            rows += sets[0].size if G == 1 else np.unique(np.concatenate(sets)).size
+    return rows
+
+
+def stream_read_ceiling(P, dev, stream, nbytes=4 << 30, reps=5):
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    P.prhs_probe_stream_read(buf, sink, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        P.prhs_probe_stream_read(buf, sink, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del buf
+    return {"bytes": nbytes, "ms": round(ms, 4), "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "prhs_probe_stream_read (16-byte non-temporal loads, 16384 x 256 threads, 8 in flight)"}
 
 
 def cpu_baseline(w, n_steps, budget_s):
@@ -95,6 +163,128 @@ def cpu_baseline(w, n_steps, budget_s):
                       f"of the {cfg.name} workload in {el:.1f} s"}
 
 
+def _rotated(w, copies):
+    Ks = [w.K] + [w.K.clone() for _ in range(copies - 1)]
+    Vs = [w.V] + [w.V.clone() for _ in range(copies - 1)]
+    return Ks, Vs
+
+
+def _summary(cfg, per_ms, graph_ms, n_steps, step_bytes, extra=None):
+    heads = cfg.batch * cfg.n_q_heads
+    mean_ms = graph_ms / n_steps
+    out = {"heads_steps_per_s": round(heads * n_steps / (graph_ms / 1e3), 1),
+           "ms_per_step": round(mean_ms, 5), "step_ms_p10_p50_p90": pct(per_ms),
+           "hbm_alg_bytes_per_step": int(step_bytes),
+           "hbm_alg_gbs": round(step_bytes / (mean_ms / 1e3) / 1e9, 1),
+           "frac_of_peak": round(step_bytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "steps": n_steps}
+    if extra:
+        out.update(extra)
+    return out
+
+
+def bench_topn(P, cfg, dev, stream, warmup, copies):
+    """A plain top-N workload (anchor step every step)."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import make_workload
+    w = make_workload(cfg, device=dev)
+    Ks, Vs = _rotated(w, copies)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    N = cfg.budget
+
+    def mk(i):
+        return lambda: eng.anchor_step(w.q[i % cfg.steps], Ks[i % copies], Vs[i % copies], P.PRHS_TOPN, N)
+
+    for i in range(warmup):
+        mk(i)()
+    per, gms = timed_steps([mk(warmup + i) for i in range(cfg.steps)], stream)
+    e = cfg.elem_bytes
+    rows = distinct_rows(eng.idx, eng.count, cfg.group)
+    scan = cfg.batch * cfg.n_kv_heads * cfg.ctx_len * cfg.head_dim * e
+    res = _summary(cfg, per, gms, cfg.steps, scan + rows * cfg.head_dim * e,
+                   {"kv_copies_rotated": copies, "budget": N})
+    del w, Ks, Vs, eng
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
+    """CIS reuse: exact top-N every refresh_period-th step, the anchor's set
+    dilated by +-radius otherwise (K and V rows gathered, no scan)."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import make_workload
+    w = make_workload(cfg, device=dev)
+    Ks, Vs = _rotated(w, copies)
+    N, r, Pd = cfg.budget, cfg.radius, cfg.refresh_period
+    dil_cap = min(cfg.ctx_len, (2 * r + 1) * N)
+    anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
+    reuse = DecodeEngine(w.K, cfg.n_q_heads, dil_cap)
+
+    def mk(i):
+        q, K, V = w.q[i % cfg.steps], Ks[i % copies], Vs[i % copies]
+        if i % Pd == 0:
+            return lambda: anchor.anchor_step(q, K, V, P.PRHS_TOPN, N)
+        return lambda: reuse.reuse_step(q, K, V, anchor.idx, anchor.count, N, r)
+
+    for i in range(warmup * Pd):
+        mk(i)()
+    per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
+    e, d = cfg.elem_bytes, cfg.head_dim
+    heads = cfg.batch * cfg.n_q_heads
+    a_rows = distinct_rows(anchor.idx, anchor.count, cfg.group)
+    r_rows = distinct_rows(reuse.idx, reuse.count, cfg.group)
+    scan = cfg.batch * cfg.n_kv_heads * cfg.ctx_len * d * e
+    a_bytes = scan + a_rows * d * e
+    r_bytes = 2 * r_rows * d * e
+    is_a = np.array([i % Pd == 0 for i in range(n_steps)])
+    a_ms, r_ms = per[is_a], per[~is_a]
+    mean_bytes = (a_bytes * is_a.sum() + r_bytes * (~is_a).sum()) / n_steps
+    res = _summary(cfg, per, gms, n_steps, mean_bytes, {
+        "kv_copies_rotated": copies, "budget": N, "radius": r, "refresh_period": Pd,
+        "anchor": {"ms_p10_p50_p90": pct(a_ms), "hbm_alg_bytes": int(a_bytes),
+                   "hbm_alg_gbs_p50": round(a_bytes / (np.median(a_ms) / 1e3) / 1e9, 1)},
+        "reuse": {"ms_p10_p50_p90": pct(r_ms), "hbm_alg_bytes": int(r_bytes),
+                  "hbm_alg_gbs_p50": round(r_bytes / (np.median(r_ms) / 1e3) / 1e9, 1),
+                  "mean_dilated_rows_per_head": round(float(reuse.count.float().mean()), 1),
+                  "heads_steps_per_s_p50": round(heads / (np.median(r_ms) / 1e3), 1)},
+        "note": "step time is the amortised mean over anchor and reuse steps"})
+    del w, Ks, Vs, anchor, reuse
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_delta(P, cfg, dev, stream, warmup, layers, steps_per_layer):
+    """Delta-budgeted decode, one layer-step per step, cycling over `layers`
+    independent KV caches (each larger than the Infinity Cache)."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import make_workload
+    ws = [make_workload(cfg, device=dev, layer=l) for l in range(layers)]
+    engs = [DecodeEngine(w.K, cfg.n_q_heads, cfg.budget) for w in ws]
+
+    def mk(i):
+        l, s = i % layers, (i // layers) % cfg.steps
+        w, eng = ws[l], engs[l]
+        return lambda: eng.delta_step(w.q[s], w.K, w.V, cfg.budget, cfg.delta_star)
+
+    for i in range(warmup * layers):
+        mk(i)()
+    n_steps = layers * steps_per_layer
+    per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
+    e, d = cfg.elem_bytes, cfg.head_dim
+    scan = cfg.batch * cfg.n_kv_heads * cfg.ctx_len * d * e
+    rows = np.mean([distinct_rows(eng.idx, eng.count, cfg.group) for eng in engs])
+    counts = torch.stack([eng.count for eng in engs]).float()
+    caps = torch.stack([eng.cap_hit for eng in engs]).float()
+    res = _summary(cfg, per, gms, n_steps, scan + rows * d * e, {
+        "unit_of_step": "layer-step", "layers_cycled": layers, "delta_star": cfg.delta_star,
+        "cap": cfg.budget, "mean_n_star": round(float(counts.mean()), 1),
+        "min_n_star": int(counts.min()), "cap_hit_fraction": round(float(caps.mean()), 4),
+        "q_scale": list(cfg.q_scale)})
+    del ws, engs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     a = _parse()
     if a.gpus != 1:
@@ -110,71 +300,49 @@ def main():
     dev = torch.device("cuda:0")
     cfg = CONFIGS[a.config]
     w = make_workload(cfg, device=dev)
-    Ks = [w.K] + [w.K.clone() for _ in range(a.rotate - 1)]
-    Vs = [w.V] + [w.V.clone() for _ in range(a.rotate - 1)]
+    Ks, Vs = _rotated(w, a.rotate)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
     stream = torch.cuda.current_stream()
     N = cfg.budget
+    print(f"[bench] {cfg.name}: warmup", file=sys.stderr, flush=True)
 
-    def step(i):
+    def mk(i):
         r = i % a.rotate
-        eng.anchor_step(w.q[i % cfg.steps], Ks[r], Vs[r], P.PRHS_TOPN, N)
+        return lambda: eng.anchor_step(w.q[i % cfg.steps], Ks[r], Vs[r], P.PRHS_TOPN, N)
 
     for i in range(a.warmup):
-        step(i)
+        mk(i)()
     torch.cuda.synchronize()
 
-    # Eager: one library call per step (host launch overhead included).
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(a.steps):
-        step(a.warmup + i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = ev0.elapsed_time(ev1)
-
-    # Timed: the same K steps captured once as a HIP graph and replayed, so the
-    # kernels run back to back without host launch gaps.
-    seq = [(w.q[(a.warmup + i) % cfg.steps], Ks[(a.warmup + i) % a.rotate], Vs[(a.warmup + i) % a.rotate])
-           for i in range(a.steps)]
-    graph = eng.capture(seq, P.PRHS_TOPN, N)
-    graph.replay()  # one untimed replay
-    torch.cuda.synchronize()
+    # Timed: K steps, eager with events between steps (host launch overhead
+    # included), then the same K steps captured once as a HIP graph and
+    # replayed, so the kernels run back to back without host launch gaps.
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    graph.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    per_ms, total_ms = timed_steps([mk(a.warmup + i) for i in range(a.steps)], stream)
     wall = time.perf_counter() - wall0
-    total_ms = ev0.elapsed_time(ev1)
 
     # The scan kernel alone, same inputs and launch configuration as inside the
     # step (per-chunk partials on, no separate log-sum-exp merge): K launches
     # back to back between two events on the launch stream.
     part = P.alloc_workspace(eng.dims, P.PRHS_OP_SCORE, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for i in range(a.steps):
         P.prhs_score(eng.dims, w.q[i % cfg.steps], Ks[i % a.rotate], eng.scores, None, part, stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
-    scan_ms = np.array([ev0.elapsed_time(ev1) / a.steps])
+    scan_ms = ev0.elapsed_time(ev1) / a.steps
 
     B, Hq, Hkv, d, t, eb = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len, cfg.elem_bytes
     heads = B * Hq
     value = heads * a.steps / (total_ms / 1e3)
     scan_bytes = B * Hkv * t * d * eb
-    # distinct V rows per (b, kv head) selected at the last timed step (algorithmic gather bytes)
-    idx = eng.idx.cpu().numpy()
+    rows = distinct_rows(eng.idx, eng.count, cfg.group)
     cnt = eng.count.cpu().numpy()
-    G = Hq // Hkv
-    rows = 0
-    for b in range(B):
-        for g in range(Hkv):
-            rows += np.unique(np.concatenate([idx[b, h, :cnt[b, h]] for h in range(g * G, (g + 1) * G)])).size
     step_bytes = scan_bytes + rows * d * eb
-    scan_gbs = scan_bytes / (scan_ms.mean() / 1e3) / 1e9
+    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
     traffic_bytes = scan_traffic_bytes()
-    traffic = None if traffic_bytes is None else round(traffic_bytes / (scan_ms.mean() / 1e3) / 1e9, 1)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / (scan_ms / 1e3) / 1e9, 1)
     res = {
         "metric": "sparse decode attn heads*steps/s at 32K ctx + achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -196,14 +364,31 @@ def main():
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,
                      "algorithmic_bytes_per_launch": scan_bytes,
-                     "mean_launch_ms": round(float(scan_ms.mean()), 5)},
+                     "mean_launch_ms": round(scan_ms, 5)},
         "step": {"hbm_alg_bytes": int(step_bytes), "hbm_alg_gbs": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "eager_ms_per_step": round(eager_ms / a.steps, 5),
-                 "scan_ms_p50": round(float(np.median(scan_ms)), 5),
+                 "eager_step_ms_p10_p50_p90": pct(per_ms),
+                 "eager_ms_per_step": round(float(per_ms.mean()), 5),
                  "mean_selected_rows_per_head": float(cnt.mean()),
                  "wall_s": round(wall, 4)},
     }
+    del Ks, Vs, eng, part
+    torch.cuda.empty_cache()
+    print("[bench] stream-read ceiling", file=sys.stderr, flush=True)
+    ceil = stream_read_ceiling(P, dev, stream)
+    res["stream_read_ceiling"] = ceil
+    res["roofline"]["frac_of_stream_ceiling"] = round(scan_gbs / ceil["gbs"], 4)
+    if not a.no_extra_configs:
+        other = {}
+        for name, fn in (("toy", lambda: bench_topn(P, CONFIGS["toy"], dev, stream, 2, 1)),
+                         ("llama2_4k", lambda: bench_topn(P, CONFIGS["llama2_4k"], dev, stream, 2, 16)),
+                         ("llama2_cis_8k", lambda: bench_cis(P, CONFIGS["llama2_cis_8k"], dev, stream, 1, 2, 32)),
+                         ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 1, 2, 8)),
+                         ("delta_16k_sharp", lambda: bench_delta(
+                             P, CONFIGS["delta_16k"].replace(q_scale=(1.0, 4.0)), dev, stream, 1, 2, 8))):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            other[name] = fn()
+        res["configs"] = other
     if a.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -212,6 +397,7 @@ def main():
         torch.cuda.synchronize()
         res["calibration_copy_bytes"] = src.numel()
     if not a.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, cfg.steps, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "prhs.h"
+#include "prhs_probe.h"
 #include "prhs_launch.hpp"
 
 namespace {
@@ -307,6 +308,13 @@ int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* 
   if (!lse_sel || !lse_all || !delta) return fail(PRHS_E_NULL, "lse_sel, lse_all and delta are required");
   return finish(prhs::launch_dropped_mass(*dims, lse_sel, lse_all, delta, tau, stream), stream,
                 "prhs_dropped_mass");
+}
+
+int prhs_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (buf == nullptr || sink == nullptr) return fail(PRHS_E_NULL, "buf and sink must be non-NULL");
+  if (!aligned16(buf)) return fail(PRHS_E_ALIGN, "buf must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16) return fail(PRHS_E_DIMS, "bytes must be a positive multiple of 16");
+  return finish(prhs::launch_stream_read(buf, bytes, sink, stream), stream, "prhs_probe_stream_read");
 }
 
 }  // extern "C"

@@ -70,6 +70,9 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
                          const float* lse_all, float* out, float* lse_sel, float* delta, float* tau,
                          void* ws, hipStream_t stream);
 
+// Read `bytes` (a multiple of 16) of device memory once (HBM ceiling probe).
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 hipError_t launch_dropped_mass(const prhs_dims& d, const float* lse_sel, const float* lse_all,
                                float* delta, float* tau, hipStream_t stream);
 

@@ -25,11 +25,13 @@
 // position; one workgroup scan over the bitmap words then gives each thread
 // its output offset, and the indices are written in ascending order.
 //
-// DELTA mode runs the full search on attention mass: each bin also sums the
-// dense weights exp(s - lse) in 2^-40 fixed point and the search walks up
-// from the smallest keys to the first position whose suffix mass exceeds the
-// target. That gives the smallest N whose dropped mass is within the target;
-// when it exceeds the cap, a count search for the cap follows.
+// DELTA mode first finds the cap-th largest key Tc as above and sums the
+// dense weights exp(s - lse) of the keys outside the top-cap set, in 2^-40
+// fixed point (exact, order-free integer sums). If that dropped mass exceeds
+// the target the cap binds. Otherwise the smallest N lies within the top-cap
+// set: a radix search on mass over the keys >= Tc (each bin also sums their
+// weights) walks up from the smallest of them, with the mass below Tc already
+// spent, to the first position whose suffix mass exceeds the target.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
@@ -121,7 +123,7 @@ __device__ __forceinline__ uint32_t take_bin(uint32_t* hist, int p, int b) {
 // registers (FROM_LDS false) or from the compacted candidate list.
 template <int KPT, int NT, bool MASS, bool FROM_LDS>
 __device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pre, uint32_t pmask,
-                                          float lse, SelShared<NT, MASS>& sh) {
+                                          float lse, SelShared<NT, MASS>& sh, uint32_t klo = 0) {
   const int shift = kPasses[p].shift;
   const uint32_t dmask = (1u << kPasses[p].bits) - 1u;
   const int lane = threadIdx.x & (kWave - 1);
@@ -129,7 +131,7 @@ __device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pr
     const int n = (int)sh.ncand_r;
     for (int c = threadIdx.x; c < n; c += NT) {
       const uint32_t key = sh.cand[c].x;
-      if ((key & pmask) == pre) {
+      if ((key & pmask) == pre && key >= klo) {
         const uint32_t dig = (key >> shift) & dmask;
         atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
         if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
@@ -139,7 +141,7 @@ __device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pr
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint32_t key = K.k[j];
-      if (((K.valid >> j) & 1ull) && (key & pmask) == pre) {
+      if (((K.valid >> j) & 1ull) && (key & pmask) == pre && key >= klo) {
         const uint32_t dig = (key >> shift) & dmask;
         atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
         if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
@@ -270,12 +272,12 @@ __device__ __forceinline__ void find_mass(int p, unsigned long long drem, SelSha
 // Copy the register keys matching (pre, pmask) into the LDS candidate list.
 template <int KPT, int NT, bool MASS>
 __device__ __forceinline__ void compact(const Keys<KPT>& K, uint32_t pre, uint32_t pmask,
-                                        SelShared<NT, MASS>& sh) {
+                                        SelShared<NT, MASS>& sh, uint32_t klo = 0) {
   const int lane = threadIdx.x & (kWave - 1);
   unsigned long long hit = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    if (((K.valid >> j) & 1ull) && (K.k[j] & pmask) == pre) hit |= 1ull << j;
+    if (((K.valid >> j) & 1ull) && (K.k[j] & pmask) == pre && K.k[j] >= klo) hit |= 1ull << j;
   const uint32_t cnt = (uint32_t)__popcll(hit);
   const uint32_t incl = wave_scan_u32(cnt);
   const uint32_t wtotal = lane_read(incl, kWave - 1);
@@ -315,35 +317,34 @@ __device__ __forceinline__ uint32_t count_search(const Keys<KPT>& K, uint32_t& k
   return pre;
 }
 
-// Mass search (DELTA): the boundary key T where the suffix mass (a key and
-// everything ranked below it) first exceeds the budget, walking up from the
-// smallest key. Returns false when the total mass is within the budget.
+// Mass search (DELTA) over the keys >= klo: the boundary key T where the
+// suffix mass (a key and everything ranked below it, down to klo) first
+// exceeds drem, walking up from the smallest key. The keys come from the
+// registers, or (FROM_LIST) from the first sh.ncand_r entries of the LDS
+// list. Returns false when the mass of all keys >= klo is within drem.
 // Otherwise n_above is the number of keys above T and take_T the number of
 // keys equal to T that are taken.
-template <int KPT, int NT>
-__device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse,
-                                            unsigned long long budget, uint32_t& T,
-                                            uint32_t& n_above, uint32_t& take_T,
-                                            SelShared<NT, true>& sh) {
+template <int KPT, int NT, bool FROM_LIST>
+__device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse, unsigned long long drem,
+                                            uint32_t klo, uint32_t& T, uint32_t& n_above,
+                                            uint32_t& take_T, SelShared<NT, true>& sh) {
   uint32_t pre = 0, pmask = 0;
-  unsigned long long drem = budget;
   n_above = 0;
-  bool lds = false;
-  if (threadIdx.x == 0) sh.ncand_r = 0;
+  bool lds = FROM_LIST;
+  if (!FROM_LIST && threadIdx.x == 0) sh.ncand_r = 0;
 #pragma unroll 1
   for (int p = 0; p < 3; ++p) {
-    if (p == 0) hist_pass<KPT, NT, true, false>(K, 0, pre, pmask, lse, sh);
-    else if (lds) hist_pass<KPT, NT, true, true>(K, p, pre, pmask, lse, sh);
-    else hist_pass<KPT, NT, true, false>(K, p, pre, pmask, lse, sh);
+    if (lds) hist_pass<KPT, NT, true, true>(K, p, pre, pmask, lse, sh, klo);
+    else hist_pass<KPT, NT, true, false>(K, p, pre, pmask, lse, sh, klo);
     find_mass<NT>(p, drem, sh);
     if (!sh.found) return false;
     drem -= sh.below;
     n_above += sh.above;
     pre |= sh.digit << kPasses[p].shift;
     pmask |= (uint32_t)((1 << kPasses[p].bits) - 1) << kPasses[p].shift;
-    if (p == 0) {
+    if (!FROM_LIST && p == 0) {
       lds = sh.cT <= (uint32_t)kCandCap;
-      if (lds) compact<KPT, NT, true>(K, pre, pmask, sh);
+      if (lds) compact<KPT, NT, true>(K, pre, pmask, sh, klo);
     }
   }
   // Boundary key T = pre: its c_T keys carry identical mass a each. The key
@@ -355,6 +356,43 @@ __device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse,
   take_T = cT - (keep_out < cT ? (uint32_t)keep_out : cT);
   T = pre;
   return true;
+}
+
+// Mass of the register keys below T, and the number of keys equal to T.
+template <int KPT, int NT>
+__device__ __forceinline__ void mass_below(const Keys<KPT>& K, uint32_t T, float lse,
+                                           unsigned long long& below, uint32_t& n_eq,
+                                           SelShared<NT, true>& sh) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  unsigned long long m = 0;
+  uint32_t e = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if ((K.valid >> j) & 1ull) {
+      if (K.k[j] < T) m += mass_fx(K.k[j], lse);
+      e += K.k[j] == T;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    m += __shfl_xor(m, o);
+    e += __shfl_xor(e, o);
+  }
+  if (lane == 0) {
+    sh.wmass[w] = m;
+    sh.wtot[w] = e;
+  }
+  __syncthreads();
+  below = 0;
+  n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    below += sh.wmass[u];
+    n_eq += sh.wtot[u];
+  }
+  __syncthreads();
 }
 
 // Mark the register keys above T and equal to T in the LDS bitmaps.
@@ -538,12 +576,13 @@ __device__ __forceinline__ void cand_radix(uint32_t lo, uint32_t hi, uint32_t C,
   take_eq = krem;
 }
 
-// Try the sampled-threshold path. Returns false (nothing written to the
-// output) when the threshold does not leave between N and kCandCap keys;
-// otherwise T and take_eq describe the result and the bitmaps are marked.
+// Sampled threshold: pick theta so that at least N keys clear it with a wide
+// margin and compact the keys >= theta with their indices into sh.cand
+// (sh.ncand of them, sh.kmax their largest). Returns false when the list does
+// not hold between N and kCandCap keys; theta is returned in `theta`.
 template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N, uint32_t& T,
-                                          uint32_t& take_eq, SelShared<NT, MASS>& sh) {
+__device__ __forceinline__ bool build_candidates(const Keys<KPT>& K, int t, uint32_t N,
+                                                 uint32_t& theta_key, SelShared<NT, MASS>& sh) {
   constexpr int SR = KPT >= 8 ? 8 : 1;  // sample one key in SR
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -608,17 +647,33 @@ __device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N,
     sh.cand[slot] = make_uint2(K.k[j], (uint32_t)(ibase + (j / Keys<KPT>::GR) * kWave * Keys<KPT>::GR + (j % Keys<KPT>::GR)));
   }
   __syncthreads();
+  theta_key = theta;
   const uint32_t C = sh.ncand;
-  if (C < N || C > (uint32_t)kCandCap) return false;
+  return C >= N && C <= (uint32_t)kCandCap;
+}
 
-  cand_radix<NT, MASS>(theta, sh.kmax, C, N, T, take_eq, sh);
-  // mark the result bits from the candidate list
+// Mark the list entries above T and equal to T in the LDS bitmaps.
+template <int NT, bool MASS>
+__device__ __forceinline__ void mark_from_list(uint32_t C, uint32_t T, SelShared<NT, MASS>& sh) {
   for (int c = threadIdx.x; c < (int)C; c += NT) {
     const uint2 ki = sh.cand[c];
     if (ki.x > T) atomicOr(&sh.gt_bits[ki.y >> 5], 1u << (ki.y & 31));
     else if (ki.x == T) atomicOr(&sh.eq_bits[ki.y >> 5], 1u << (ki.y & 31));
   }
   __syncthreads();
+}
+
+// Try the sampled-threshold path. Returns false (nothing written to the
+// output) when the threshold does not leave between N and kCandCap keys;
+// otherwise T and take_eq describe the result and the bitmaps are marked.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N, uint32_t& T,
+                                          uint32_t& take_eq, SelShared<NT, MASS>& sh) {
+  uint32_t theta;
+  if (!build_candidates<KPT, NT, MASS>(K, t, N, theta, sh)) return false;
+  const uint32_t C = sh.ncand;
+  cand_radix<NT, MASS>(theta, sh.kmax, C, N, T, take_eq, sh);
+  mark_from_list<NT, MASS>(C, T, sh);
   return true;
 }
 
@@ -847,18 +902,49 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if constexpr (MASS) {
     const float lse = a.part != nullptr ? sh.lse : a.lse_all[head];
     const unsigned long long budget = (unsigned long long)((double)a.delta_target * kMassScale);
-    uint32_t n_above = 0, take_T = 0;
-    const bool found = mass_search<KPT, NT>(K, lse, budget, T, n_above, take_T, sh);
-    if (found && (int)(n_above + take_T) <= a.n_budget) {
-      n_sel = (int)(n_above + take_T);
-      take = take_T;
+    const uint32_t cap = (uint32_t)a.n_budget;
+    // The cap-th largest key Tc; takec of the keys equal to it are in the
+    // top-cap set. From the sampled candidate list when it holds the answer.
+    uint32_t theta = 0, Tc = 0, takec = cap;
+    const bool list = build_candidates<KPT, NT, MASS>(K, t, cap, theta, sh);
+    const uint32_t C = sh.ncand;
+    if (list) cand_radix<NT, MASS>(theta, sh.kmax, C, cap, Tc, takec, sh);
+    else Tc = count_search<KPT, NT, MASS>(K, takec, sh);
+    // Dropped mass of the top-cap set. Above the target the cap binds;
+    // otherwise the smallest N lies within the top-cap set, and the mass
+    // search runs over the keys >= Tc only, with the mass below Tc spent.
+    unsigned long long below = 0;
+    uint32_t n_eq = 0;
+    mass_below<KPT, NT>(K, Tc, lse, below, n_eq, sh);
+    const unsigned long long drop_cap =
+        below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse);
+    if (drop_cap > budget) {
+      hit = 1;
+      T = Tc;
+      take = takec;
     } else {
-      hit = found ? 1 : 0;
-      n_sel = found ? a.n_budget : 1;
-      take = (uint32_t)n_sel;
-      T = count_search<KPT, NT, MASS>(K, take, sh);
+      uint32_t n_above = 0, take_T = 0;
+      bool found;
+      if (list) {
+        if (threadIdx.x == 0) sh.ncand_r = C;
+        __syncthreads();
+        found = mass_search<KPT, NT, true>(K, lse, budget - below, Tc, T, n_above, take_T, sh);
+      } else {
+        found = mass_search<KPT, NT, false>(K, lse, budget - below, Tc, T, n_above, take_T, sh);
+      }
+      if (found) {
+        n_sel = (int)(n_above + take_T);
+        take = take_T;
+      } else {
+        // all of the mass is within the target: the single top key
+        n_sel = 1;
+        take = 1;
+        if (list) T = sh.kmax;
+        else T = count_search<KPT, NT, MASS>(K, take, sh);
+      }
     }
-    mark_from_regs<KPT, NT, MASS>(K, T, sh);
+    if (list) mark_from_list<NT, MASS>(C, T, sh);
+    else mark_from_regs<KPT, NT, MASS>(K, T, sh);
   } else {
     if (!topn_fast<KPT, NT, MASS>(K, t, (uint32_t)a.n_budget, T, take, sh)) {
       load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die

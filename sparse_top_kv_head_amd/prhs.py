@@ -43,6 +43,8 @@ EXPORTED = (
     "prhs_dropped_mass", "prhs_anchor_step", "prhs_workspace_bytes", "prhs_status_string",
     "prhs_last_error",
 )
+# measurement aid (include/prhs_probe.h)
+PROBE_EXPORTED = ("prhs_probe_stream_read",)
 
 
 class PrhsDims(ctypes.Structure):
@@ -87,6 +89,8 @@ def lib():
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
+        L.prhs_probe_stream_read.argtypes = [vp, sz, vp, vp]
+        L.prhs_probe_stream_read.restype = ctypes.c_int
         L.prhs_workspace_bytes.argtypes = [dp, i32, i32]
         L.prhs_workspace_bytes.restype = sz
         L.prhs_status_string.argtypes = [ctypes.c_int]
@@ -196,3 +200,10 @@ def prhs_anchor_step(dims, mode, n_budget, delta_target, q, k, v, scores, lse_al
                                   _p(v), _p(scores), _p(lse_all), _p(idx), idx_cap, _p(count),
                                   _p(cap_hit), _p(out), _p(lse_sel), _p(delta), _p(tau),
                                   _p(theta), _p(ws), ws_bytes, _stream(stream)))
+
+
+def prhs_probe_stream_read(buf, sink, nbytes=None, stream=None):
+    """Read every byte of `buf` once (HBM read-ceiling probe)."""
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    _check(lib().prhs_probe_stream_read(_p(buf), nbytes, _p(sink), _stream(stream)))

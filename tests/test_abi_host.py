@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol prhs.h declares, and rejects
+"""The C-ABI library loads, exports every symbol include/*.h declares, and rejects
 invalid arguments on the host before any HIP call (CPU only: every call here
 fails validation, so nothing is ever launched)."""
 
@@ -13,6 +13,7 @@ from sparse_top_kv_head_amd import prhs as P
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "prhs.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "prhs_probe.h")
 
 FAKE = 0x100000          # 16-byte aligned, never dereferenced: every call below is invalid
 FAKE_MIS = 0x100008      # 8-byte aligned only
@@ -33,11 +34,16 @@ def _dims(**kw):
     return P.PrhsDims(**base)
 
 
+def _declared(path):
+    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(prhs_\w+)\s*\(", open(path).read(), re.M))
+
+
 def test_header_symbols_are_exported(L):
     text = open(HEADER).read()
-    declared = set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(prhs_\w+)\s*\(", text, re.M))
+    declared = _declared(HEADER)
     assert declared == set(P.EXPORTED)
-    for name in declared:
+    assert _declared(PROBE_HEADER) == set(P.PROBE_EXPORTED)
+    for name in declared | _declared(PROBE_HEADER):
         assert hasattr(L, name), name
     assert P.PRHS_MAX_SELECT_CTX == int(re.search(r"PRHS_MAX_SELECT_CTX\s+(\d+)", text).group(1))
     for const, value in re.findall(r"^\s*(PRHS_\w+)\s*=\s*(-?\d+)", text, re.M):
@@ -214,3 +220,12 @@ def test_python_binding_raises(L):
         P.prhs_select_topk(d, FAKE, FAKE, P.PRHS_TOPN, 0, 0.0, FAKE, 64, FAKE, stream=0)
     assert e.value.code == P.PRHS_E_BUDGET
     assert "n_budget" in str(e.value)
+
+
+def test_probe_argument_checks(L):
+    sink = FAKE
+    assert L.prhs_probe_stream_read(None, 64, sink, None) == P.PRHS_E_NULL
+    assert L.prhs_probe_stream_read(FAKE, 64, None, None) == P.PRHS_E_NULL
+    assert L.prhs_probe_stream_read(FAKE_MIS, 64, sink, None) == P.PRHS_E_ALIGN
+    assert L.prhs_probe_stream_read(FAKE, 0, sink, None) == P.PRHS_E_DIMS
+    assert L.prhs_probe_stream_read(FAKE, 40, sink, None) == P.PRHS_E_DIMS

@@ -163,20 +163,24 @@ def test_select_deterministic_and_in_place():
 # ---------------------------------------------------------------------------
 
 DELTA_CASES = [
-    # scale of the scores, t, cap, delta*
-    (4.0, 4096, 2048, 0.05), (8.0, 16384, 2048, 0.05), (1.0, 16384, 2048, 0.05),
-    (3.0, 1000, 1000, 0.0), (3.0, 1000, 1000, 1.0), (6.0, 777, 50, 0.2), (2.0, 32768, 4096, 0.1),
-    (12.0, 65536, 512, 0.01),
+    # scale of the scores, t, cap, delta*, quantum (0: continuous scores)
+    (4.0, 4096, 2048, 0.05, 0), (8.0, 16384, 2048, 0.05, 0), (1.0, 16384, 2048, 0.05, 0),
+    (3.0, 1000, 1000, 0.0, 0), (3.0, 1000, 1000, 1.0, 0), (6.0, 777, 50, 0.2, 0),
+    (2.0, 32768, 4096, 0.1, 0), (12.0, 65536, 512, 0.01, 0), (3.0, 8192, 1024, 0.3, 0),
+    # coarse score grids: many keys tie with the boundary key
+    (4.0, 16384, 2048, 0.05, 0.5), (1.0, 6000, 3000, 0.2, 0.25), (6.0, 20000, 800, 0.1, 1.0),
 ]
 
 
-@pytest.mark.parametrize("scale,t,cap,ds", DELTA_CASES)
-def test_select_delta(scale, t, cap, ds):
+@pytest.mark.parametrize("scale,t,cap,ds,quant", DELTA_CASES)
+def test_select_delta(scale, t, cap, ds, quant):
     dev = _dev()
     H = 4
     rng = np.random.default_rng(int(scale * 100) + t)
     s = (rng.standard_normal((H, t)) * scale).astype(np.float32)
     s[:, rng.integers(0, t, 5)] += 3 * scale   # a few sinks
+    if quant:
+        s = (np.round(s / quant) * quant).astype(np.float32)
     _, lse = O.dense_softmax(s.astype(np.float64))
     ld = (t + 3) // 4 * 4
     buf = torch.zeros((1, H, ld), dtype=torch.float32)
