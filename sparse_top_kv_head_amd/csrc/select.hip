@@ -146,6 +146,9 @@ __device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pr
         atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
         if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
       }
+      // one key's 64-bit mass at a time: keeps the unrolled loop within the
+      // register budget
+      if constexpr (MASS) __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
@@ -358,6 +361,42 @@ __device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse, unsig
   return true;
 }
 
+// Mass of the list keys >= T and the number of keys equal to T (the list
+// holds every key >= T).
+template <int NT>
+__device__ __forceinline__ void mass_list_at_or_above(uint32_t C, uint32_t T, float lse,
+                                                      unsigned long long& top, uint32_t& n_eq,
+                                                      SelShared<NT, true>& sh) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  unsigned long long m = 0;
+  uint32_t e = 0;
+  for (int c = threadIdx.x; c < (int)C; c += NT) {
+    const uint32_t key = sh.cand[c].x;
+    if (key >= T) m += mass_fx(key, lse);
+    e += key == T;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    m += __shfl_xor(m, o);
+    e += __shfl_xor(e, o);
+  }
+  if (lane == 0) {
+    sh.wmass[w] = m;
+    sh.wtot[w] = e;
+  }
+  __syncthreads();
+  top = 0;
+  n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    top += sh.wmass[u];
+    n_eq += sh.wtot[u];
+  }
+  __syncthreads();
+}
+
 // Mass of the register keys below T, and the number of keys equal to T.
 template <int KPT, int NT>
 __device__ __forceinline__ void mass_below(const Keys<KPT>& K, uint32_t T, float lse,
@@ -412,13 +451,12 @@ __device__ __forceinline__ void mark_from_regs(const Keys<KPT>& K, uint32_t T,
   __syncthreads();
 }
 
-// Write the marked keys above T and the first take_eq keys equal to T in
-// ascending index order: thread i owns WPT consecutive bitmap words.
+// Final selection of every bitmap word -- the keys above T plus the first
+// take_eq keys equal to T in index order -- and the word's exclusive output
+// offset, stored in place of gt_bits and eq_bits. Thread i owns WPT
+// consecutive words.
 template <int NT, bool MASS>
-__device__ __forceinline__ void emit_bitmaps(int t, uint32_t take_eq, int* __restrict__ out,
-                                             float* __restrict__ out_s,
-                                             const float* __restrict__ row, uint32_t cap,
-                                             SelShared<NT, MASS>& sh) {
+__device__ __forceinline__ void emit_offsets(int t, uint32_t take_eq, SelShared<NT, MASS>& sh) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -461,15 +499,56 @@ __device__ __forceinline__ void emit_bitmaps(int t, uint32_t take_eq, int* __res
       ew ^= low;
       --eq_left;
     }
-    const int base_i = ((int)threadIdx.x * WPT + q) << 5;
-    while (sel) {
-      const int b = __builtin_ctz(sel);
-      sel &= sel - 1;
-      if (pos < cap) {
-        out[pos] = base_i + b;
-        if (out_s) out_s[pos] = row[base_i + b];
+    const int wi = (int)threadIdx.x * WPT + q;
+    if (wi < nwords) {
+      sh.gt_bits[wi] = sel;
+      sh.eq_bits[wi] = pos;
+    }
+    pos += __popc(sel);
+  }
+  __syncthreads();
+}
+
+// Output slot of key index i, or -1 when it is not selected (after emit_offsets).
+template <int NT, bool MASS>
+__device__ __forceinline__ int out_slot(uint32_t i, const SelShared<NT, MASS>& sh) {
+  const uint32_t m = sh.gt_bits[i >> 5];
+  const uint32_t bit = i & 31u;
+  if (!((m >> bit) & 1u)) return -1;
+  return (int)(sh.eq_bits[i >> 5] + __popc(m & ((1u << bit) - 1u)));
+}
+
+// Write the selected entries of the LDS list (key, index) to their slots.
+template <int NT, bool MASS>
+__device__ __forceinline__ void scatter_list(uint32_t C, int* __restrict__ out,
+                                             float* __restrict__ out_s, uint32_t cap,
+                                             const SelShared<NT, MASS>& sh) {
+  for (int c = threadIdx.x; c < (int)C; c += NT) {
+    const uint2 ki = sh.cand[c];
+    const int pos = out_slot<NT, MASS>(ki.y, sh);
+    if (pos >= 0 && (uint32_t)pos < cap) {
+      out[pos] = (int)ki.y;
+      if (out_s) out_s[pos] = key_to_score(ki.x);
+    }
+  }
+}
+
+// Write the selected register keys to their slots.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ void scatter_regs(const Keys<KPT>& K, int* __restrict__ out,
+                                             float* __restrict__ out_s, uint32_t cap,
+                                             const SelShared<NT, MASS>& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if ((K.valid >> j) & 1ull) {
+      const int i = key_index<KPT>(w, lane, j);
+      const int pos = out_slot<NT, MASS>((uint32_t)i, sh);
+      if (pos >= 0 && (uint32_t)pos < cap) {
+        out[pos] = i;
+        if (out_s) out_s[pos] = key_to_score(K.k[j]);
       }
-      ++pos;
     }
   }
 }
@@ -806,10 +885,12 @@ __device__ __forceinline__ float next_theta(uint32_t T, uint32_t kmax) {
   return ts - (0.1f * (spread > 0.f ? spread : 0.f) + 0.05f);
 }
 
-// Load the head's scores as keys: wave w owns [w*64*KPT, (w+1)*64*KPT), lane
-// `lane` the granules at w*64*KPT + v*64*GR + lane*GR.
+// Load the head's scores (raw fp32 bits; finish_keys turns them into keys):
+// wave w owns [w*64*KPT, (w+1)*64*KPT), lane `lane` the granules at
+// w*64*KPT + v*64*GR + lane*GR. Split in two so that the loads stay in flight
+// across unrelated work.
 template <int KPT>
-__device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict__ row, int t) {
+__device__ __forceinline__ void load_keys_raw(Keys<KPT>& K, const float* __restrict__ row, int t) {
   constexpr int GR = Keys<KPT>::GR, NV = Keys<KPT>::NV;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -817,11 +898,11 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
   if (GR == 4 && (w + 1) * kWave * KPT <= t) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const float4 x = *reinterpret_cast<const float4*>(row + base + v * kWave * GR);
-      K.k[GR * v] = score_key(x.x);
-      K.k[GR * v + 1 % GR] = score_key(x.y);
-      K.k[GR * v + 2 % GR] = score_key(x.z);
-      K.k[GR * v + 3 % GR] = score_key(x.w);
+      const uint4 x = *reinterpret_cast<const uint4*>(row + base + v * kWave * GR);
+      K.k[GR * v] = x.x;
+      K.k[GR * v + 1 % GR] = x.y;
+      K.k[GR * v + 2 % GR] = x.z;
+      K.k[GR * v + 3 % GR] = x.w;
     }
     K.valid = KPT == 64 ? ~0ull : ((1ull << KPT) - 1ull);
     return;
@@ -833,9 +914,47 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
 #pragma unroll
     for (int e = 0; e < GR; ++e) {
       const bool ok = i + e < t;
-      K.k[v * GR + e] = ok ? score_key(row[i + e]) : 0u;
+      K.k[v * GR + e] = ok ? __float_as_uint(row[i + e]) : 0u;
       if (ok) K.valid |= 1ull << (v * GR + e);
     }
+  }
+}
+
+template <int KPT>
+__device__ __forceinline__ void finish_keys(Keys<KPT>& K) {
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    K.k[j] = ((K.valid >> j) & 1ull) ? score_key(__uint_as_float(K.k[j])) : 0u;
+}
+
+template <int KPT>
+__device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict__ row, int t) {
+  load_keys_raw<KPT>(K, row, t);
+  finish_keys<KPT>(K);
+}
+
+// Write the selection once T and take are known and the bitmaps are marked:
+// indices and scores in ascending index order (scattered from the LDS list,
+// or from the register keys, reloaded), then the count, the cap flag and the
+// threshold hint.
+template <int KPT, int NT, bool MASS>
+__device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const float* row,
+                                            int* out, float* out_s, bool list, uint32_t C,
+                                            uint32_t T, uint32_t take, int n_sel, int hit,
+                                            SelShared<NT, MASS>& sh) {
+  const uint32_t cap = (uint32_t)a.idx_cap;
+  emit_offsets<NT, MASS>(a.t, take, sh);
+  if (list) {
+    scatter_list<NT, MASS>(C, out, out_s, cap, sh);
+  } else {
+    Keys<KPT> K;
+    load_keys<KPT>(K, row, a.t);
+    scatter_regs<KPT, NT, MASS>(K, out, out_s, cap, sh);
+  }
+  if (threadIdx.x == 0) {
+    a.count[head] = n_sel;
+    if (a.cap_hit) a.cap_hit[head] = hit;
+    if (!MASS && a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
   }
 }
 
@@ -853,6 +972,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const float* row = a.scores + (size_t)head * a.ld;
   int* out = a.idx + (size_t)head * a.idx_cap;
   float* out_s = a.sel_scores ? a.sel_scores + (size_t)head * a.idx_cap : nullptr;
+  const uint32_t cap = (uint32_t)a.idx_cap;
+  // Without scan candidates the scores are needed in registers: their loads
+  // go out first and complete under the partial merge and the LDS clearing.
+  const bool from_scan = !MASS && a.cand != nullptr;
+  Keys<KPT> K;
+  if (!from_scan) load_keys_raw<KPT>(K, row, t);
   if (a.part != nullptr && threadIdx.x < kWave) {
     float m = -INFINITY, l = 0.f;
     for (int c = threadIdx.x; c < a.nchunks; c += kWave) {
@@ -878,11 +1003,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 
   if constexpr (!MASS) {
     uint32_t C = 0;
-    if (a.cand != nullptr &&
+    if (from_scan &&
         gather_candidates<NT, MASS>(a.cand, a.cand_cnt, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
       uint32_t T, take;
       cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
-      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh);
+      emit_list<NT, MASS>(C, T, take, out, out_s, cap, sh);
       if (threadIdx.x == 0) {
         a.count[head] = a.n_budget;
         if (a.cap_hit) a.cap_hit[head] = 0;
@@ -892,80 +1017,90 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   }
 
-  Keys<KPT> K;
-  load_keys<KPT>(K, row, t);
+  if (from_scan) load_keys_raw<KPT>(K, row, t);
+  finish_keys<KPT>(K);
   __syncthreads();
 
-  uint32_t T = 0, take = 0;
-  int n_sel = a.n_budget;
-  int hit = 0;
   if constexpr (MASS) {
     const float lse = a.part != nullptr ? sh.lse : a.lse_all[head];
     const unsigned long long budget = (unsigned long long)((double)a.delta_target * kMassScale);
-    const uint32_t cap = (uint32_t)a.n_budget;
-    // The cap-th largest key Tc; takec of the keys equal to it are in the
-    // top-cap set. From the sampled candidate list when it holds the answer.
-    uint32_t theta = 0, Tc = 0, takec = cap;
-    const bool list = build_candidates<KPT, NT, MASS>(K, t, cap, theta, sh);
-    const uint32_t C = sh.ncand;
-    if (list) cand_radix<NT, MASS>(theta, sh.kmax, C, cap, Tc, takec, sh);
-    else Tc = count_search<KPT, NT, MASS>(K, takec, sh);
-    // Dropped mass of the top-cap set. Above the target the cap binds;
-    // otherwise the smallest N lies within the top-cap set, and the mass
-    // search runs over the keys >= Tc only, with the mass below Tc spent.
+    const uint32_t ncap = (uint32_t)a.n_budget;
+    // The ncap-th largest key Tc; takec of the keys equal to it are in the
+    // top-ncap set. Then the dropped mass of the top-ncap set: above the
+    // target the cap binds; otherwise the smallest N lies within the top-ncap
+    // set, and the mass search runs over the keys >= Tc only, with the mass
+    // below Tc spent.
+    uint32_t theta = 0;
+    if (build_candidates<KPT, NT, MASS>(K, t, ncap, theta, sh)) {
+      // From the sampled list, which holds every key >= Tc. The mass below Tc
+      // is the whole (the dense weights sum to one) less the listed keys >= Tc,
+      // which avoids weighing every key.
+      const uint32_t C = sh.ncand;
+      uint32_t Tc = 0, takec = ncap;
+      cand_radix<NT, MASS>(theta, sh.kmax, C, ncap, Tc, takec, sh);
+      unsigned long long top = 0;
+      uint32_t n_eq = 0;
+      mass_list_at_or_above<NT>(C, Tc, lse, top, n_eq, sh);
+      const unsigned long long one = (unsigned long long)kMassScale;
+      const unsigned long long below = top < one ? one - top : 0ull;
+      uint32_t T = Tc, take = takec;
+      int n_sel = (int)ncap, hit = 1;
+      if (below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse) <= budget) {
+        hit = 0;
+        if (threadIdx.x == 0) sh.ncand_r = C;
+        __syncthreads();
+        uint32_t n_above = 0, take_T = 0;
+        if (mass_search<KPT, NT, true>(K, lse, budget - below, Tc, T, n_above, take_T, sh)) {
+          n_sel = (int)(n_above + take_T);
+          take = take_T;
+        } else {
+          // all of the mass is within the target: the single top key
+          n_sel = 1;
+          take = 1;
+          T = sh.kmax;
+        }
+      }
+      mark_from_list<NT, MASS>(C, T, sh);
+      finish_head<KPT, NT, MASS>(a, head, row, out, out_s, true, C, T, take, n_sel, hit, sh);
+      return;
+    }
+    // From the register keys (the sample misled).
+    uint32_t takec = ncap;
+    const uint32_t Tc = count_search<KPT, NT, MASS>(K, takec, sh);
     unsigned long long below = 0;
     uint32_t n_eq = 0;
     mass_below<KPT, NT>(K, Tc, lse, below, n_eq, sh);
-    const unsigned long long drop_cap =
-        below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse);
-    if (drop_cap > budget) {
-      hit = 1;
-      T = Tc;
-      take = takec;
-    } else {
+    uint32_t T = Tc, take = takec;
+    int n_sel = (int)ncap, hit = 1;
+    if (below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse) <= budget) {
+      hit = 0;
       uint32_t n_above = 0, take_T = 0;
-      bool found;
-      if (list) {
-        if (threadIdx.x == 0) sh.ncand_r = C;
-        __syncthreads();
-        found = mass_search<KPT, NT, true>(K, lse, budget - below, Tc, T, n_above, take_T, sh);
-      } else {
-        found = mass_search<KPT, NT, false>(K, lse, budget - below, Tc, T, n_above, take_T, sh);
-      }
-      if (found) {
+      if (mass_search<KPT, NT, false>(K, lse, budget - below, Tc, T, n_above, take_T, sh)) {
         n_sel = (int)(n_above + take_T);
         take = take_T;
       } else {
-        // all of the mass is within the target: the single top key
         n_sel = 1;
         take = 1;
-        if (list) T = sh.kmax;
-        else T = count_search<KPT, NT, MASS>(K, take, sh);
+        T = count_search<KPT, NT, MASS>(K, take, sh);
       }
     }
-    if (list) mark_from_list<NT, MASS>(C, T, sh);
-    else mark_from_regs<KPT, NT, MASS>(K, T, sh);
+    mark_from_regs<KPT, NT, MASS>(K, T, sh);
+    finish_head<KPT, NT, MASS>(a, head, row, out, out_s, false, 0, T, take, n_sel, hit, sh);
   } else {
-    if (!topn_fast<KPT, NT, MASS>(K, t, (uint32_t)a.n_budget, T, take, sh)) {
-      load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die
-      take = (uint32_t)a.n_budget;
-      T = count_search<KPT, NT, MASS>(K, take, sh);
-      mark_from_regs<KPT, NT, MASS>(K, T, sh);
+    uint32_t T = 0, take = 0;
+    if (topn_fast<KPT, NT, MASS>(K, t, (uint32_t)a.n_budget, T, take, sh)) {
+      finish_head<KPT, NT, MASS>(a, head, row, out, out_s, true, sh.ncand, T, take, a.n_budget, 0, sh);
+      return;
     }
-  }
-  emit_bitmaps<NT, MASS>(t, take, out, out_s, row, (uint32_t)a.idx_cap, sh);
-  if (threadIdx.x == 0) {
-    a.count[head] = n_sel;
-    if (a.cap_hit) a.cap_hit[head] = hit;
-  }
-  if constexpr (!MASS) {
+    load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die
+    take = (uint32_t)a.n_budget;
+    T = count_search<KPT, NT, MASS>(K, take, sh);
+    mark_from_regs<KPT, NT, MASS>(K, T, sh);
     if (a.theta_out) {
       // the head's top key, for the next step's threshold hint
       uint32_t kmx = 0;
-      for (int i = threadIdx.x; i < t; i += NT) {
-        const uint32_t key = score_key(row[i]);
-        kmx = key > kmx ? key : kmx;
-      }
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) kmx = ((K.valid >> j) & 1ull) && K.k[j] > kmx ? K.k[j] : kmx;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const uint32_t y = __shfl_xor(kmx, o);
@@ -974,9 +1109,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       if (threadIdx.x == 0) sh.kmax = 0;
       __syncthreads();
       if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh.kmax, kmx);
-      __syncthreads();
-      if (threadIdx.x == 0) a.theta_out[head] = next_theta(T, sh.kmax);
     }
+    finish_head<KPT, NT, MASS>(a, head, row, out, out_s, false, 0, T, take, a.n_budget, 0, sh);
   }
 }
 
