@@ -119,36 +119,32 @@ __device__ __forceinline__ uint32_t take_bin(uint32_t* hist, int p, int b) {
   return c;
 }
 
-// Atomics of pass p over the keys matching (pre, pmask), taken from the
-// registers (FROM_LDS false) or from the compacted candidate list.
-template <int KPT, int NT, bool MASS, bool FROM_LDS>
-__device__ __forceinline__ void hist_pass(const Keys<KPT>& K, int p, uint32_t pre, uint32_t pmask,
+// Where the keys of a search come from: the first n entries of the LDS list
+// (key in .x), or the score row itself, streamed (L2-resident after the
+// first read). Only the fallback paths stream; they then hold no keys in
+// registers, which keeps the kernel free of spills.
+struct Src {
+  const float* row;  // non-NULL: row[0:n]; NULL: the LDS list
+  int n;
+};
+
+__device__ __forceinline__ uint32_t src_key(const Src& src, const uint2* cand, int c) {
+  return src.row != nullptr ? score_key(src.row[c]) : cand[c].x;
+}
+
+// Atomics of pass p over the source keys >= klo matching (pre, pmask).
+template <int NT, bool MASS>
+__device__ __forceinline__ void hist_pass(const Src& src, int p, uint32_t pre, uint32_t pmask,
                                           float lse, SelShared<NT, MASS>& sh, uint32_t klo = 0) {
   const int shift = kPasses[p].shift;
   const uint32_t dmask = (1u << kPasses[p].bits) - 1u;
   const int lane = threadIdx.x & (kWave - 1);
-  if constexpr (FROM_LDS) {
-    const int n = (int)sh.ncand_r;
-    for (int c = threadIdx.x; c < n; c += NT) {
-      const uint32_t key = sh.cand[c].x;
-      if ((key & pmask) == pre && key >= klo) {
-        const uint32_t dig = (key >> shift) & dmask;
-        atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
-        if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint32_t key = K.k[j];
-      if (((K.valid >> j) & 1ull) && (key & pmask) == pre && key >= klo) {
-        const uint32_t dig = (key >> shift) & dmask;
-        atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
-        if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
-      }
-      // one key's 64-bit mass at a time: keeps the unrolled loop within the
-      // register budget
-      if constexpr (MASS) __builtin_amdgcn_sched_barrier(0);
+  for (int c = threadIdx.x; c < src.n; c += NT) {
+    const uint32_t key = src_key(src, sh.cand, c);
+    if ((key & pmask) == pre && key >= klo) {
+      const uint32_t dig = (key >> shift) & dmask;
+      atomicAdd(&sh.hist[hist_slot(p, dig, lane)], 1u);
+      if constexpr (MASS) atomicAdd(&sh.mhist[dig], mass_fx(key, lse));
     }
   }
   __syncthreads();
@@ -272,46 +268,51 @@ __device__ __forceinline__ void find_mass(int p, unsigned long long drem, SelSha
   __syncthreads();
 }
 
-// Copy the register keys matching (pre, pmask) into the LDS candidate list.
-template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ void compact(const Keys<KPT>& K, uint32_t pre, uint32_t pmask,
-                                        SelShared<NT, MASS>& sh, uint32_t klo = 0) {
+// Copy the row's keys >= klo matching (pre, pmask) into the LDS list (keys
+// only, in no particular order); sh.ncand_r becomes their number. The caller
+// knows that they fit.
+template <int NT, bool MASS>
+__device__ __forceinline__ void compact_row(const float* __restrict__ row, int t, uint32_t pre,
+                                            uint32_t pmask, uint32_t klo,
+                                            SelShared<NT, MASS>& sh) {
   const int lane = threadIdx.x & (kWave - 1);
-  unsigned long long hit = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (((K.valid >> j) & 1ull) && (K.k[j] & pmask) == pre && K.k[j] >= klo) hit |= 1ull << j;
-  const uint32_t cnt = (uint32_t)__popcll(hit);
-  const uint32_t incl = wave_scan_u32(cnt);
-  const uint32_t wtotal = lane_read(incl, kWave - 1);
-  uint32_t base = 0;
-  if (lane == 0 && wtotal) base = atomicAdd(&sh.ncand_r, wtotal);
-  base = lane_read(base, 0);
-  uint32_t pos = base + incl - cnt;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if ((hit >> j) & 1ull) sh.cand[pos++].x = K.k[j];
+  if (threadIdx.x == 0) sh.ncand_r = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < t; c0 += NT) {  // whole waves iterate together
+    const int c = c0 + (int)threadIdx.x;
+    const uint32_t key = c < t ? score_key(row[c]) : 0u;
+    const bool h = c < t && (key & pmask) == pre && key >= klo;
+    const unsigned long long m = __ballot(h);
+    if (m) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sh.ncand_r, (uint32_t)__popcll(m));
+      base = lane_read(base, 0);
+      const uint32_t pos = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+      if (h && pos < (uint32_t)kCandCap) sh.cand[pos].x = key;
+    }
+  }
   __syncthreads();
 }
 
-// Exact boundary of the krem-th largest key. Returns T; krem becomes the
-// number of keys equal to T that are taken.
-template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ uint32_t count_search(const Keys<KPT>& K, uint32_t& krem,
-                                                 SelShared<NT, MASS>& sh) {
+// Exact boundary of the krem-th largest key of the row. Returns T; krem
+// becomes the number of keys equal to T that are taken.
+template <int NT, bool MASS>
+__device__ __forceinline__ uint32_t count_search(const float* __restrict__ row, int t,
+                                                 uint32_t& krem, SelShared<NT, MASS>& sh) {
   uint32_t pre = 0, pmask = 0;
-  if (threadIdx.x == 0) sh.ncand_r = 0;
-  hist_pass<KPT, NT, MASS, false>(K, 0, pre, pmask, 0.f, sh);
+  Src src{row, t};
+  hist_pass<NT, MASS>(src, 0, pre, pmask, 0.f, sh);
   find_count<NT, MASS>(0, krem, sh);
   krem -= sh.above;
   pre = sh.digit << kPasses[0].shift;
   pmask = (uint32_t)(kBins - 1) << kPasses[0].shift;
-  const bool lds = sh.cT <= (uint32_t)kCandCap;
-  if (lds) compact<KPT, NT, MASS>(K, pre, pmask, sh);
+  if (sh.cT <= (uint32_t)kCandCap) {
+    compact_row<NT, MASS>(row, t, pre, pmask, 0u, sh);
+    src = Src{nullptr, (int)sh.ncand_r};
+  }
 #pragma unroll 1
   for (int p = 1; p < 3; ++p) {
-    if (lds) hist_pass<KPT, NT, MASS, true>(K, p, pre, pmask, 0.f, sh);
-    else hist_pass<KPT, NT, MASS, false>(K, p, pre, pmask, 0.f, sh);
+    hist_pass<NT, MASS>(src, p, pre, pmask, 0.f, sh);
     find_count<NT, MASS>(p, krem, sh);
     krem -= sh.above;
     pre |= sh.digit << kPasses[p].shift;
@@ -320,34 +321,31 @@ __device__ __forceinline__ uint32_t count_search(const Keys<KPT>& K, uint32_t& k
   return pre;
 }
 
-// Mass search (DELTA) over the keys >= klo: the boundary key T where the
-// suffix mass (a key and everything ranked below it, down to klo) first
-// exceeds drem, walking up from the smallest key. The keys come from the
-// registers, or (FROM_LIST) from the first sh.ncand_r entries of the LDS
-// list. Returns false when the mass of all keys >= klo is within drem.
-// Otherwise n_above is the number of keys above T and take_T the number of
-// keys equal to T that are taken.
-template <int KPT, int NT, bool FROM_LIST>
-__device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse, unsigned long long drem,
+// Mass search (DELTA) over the source keys >= klo: the boundary key T where
+// the suffix mass (a key and everything ranked below it, down to klo) first
+// exceeds drem, walking up from the smallest key. A streamed row is compacted
+// to the LDS list after the first pass when the boundary bin fits. Returns
+// false when the mass of all keys >= klo is within drem. Otherwise n_above is
+// the number of keys above T and take_T the number of keys equal to T that
+// are taken.
+template <int NT>
+__device__ __forceinline__ bool mass_search(Src src, float lse, unsigned long long drem,
                                             uint32_t klo, uint32_t& T, uint32_t& n_above,
                                             uint32_t& take_T, SelShared<NT, true>& sh) {
   uint32_t pre = 0, pmask = 0;
   n_above = 0;
-  bool lds = FROM_LIST;
-  if (!FROM_LIST && threadIdx.x == 0) sh.ncand_r = 0;
 #pragma unroll 1
   for (int p = 0; p < 3; ++p) {
-    if (lds) hist_pass<KPT, NT, true, true>(K, p, pre, pmask, lse, sh, klo);
-    else hist_pass<KPT, NT, true, false>(K, p, pre, pmask, lse, sh, klo);
+    hist_pass<NT, true>(src, p, pre, pmask, lse, sh, klo);
     find_mass<NT>(p, drem, sh);
     if (!sh.found) return false;
     drem -= sh.below;
     n_above += sh.above;
     pre |= sh.digit << kPasses[p].shift;
     pmask |= (uint32_t)((1 << kPasses[p].bits) - 1) << kPasses[p].shift;
-    if (!FROM_LIST && p == 0) {
-      lds = sh.cT <= (uint32_t)kCandCap;
-      if (lds) compact<KPT, NT, true>(K, pre, pmask, sh, klo);
+    if (p == 0 && src.row != nullptr && sh.cT <= (uint32_t)kCandCap) {
+      compact_row<NT, true>(src.row, src.n, pre, pmask, klo, sh);
+      src = Src{nullptr, (int)sh.ncand_r};
     }
   }
   // Boundary key T = pre: its c_T keys carry identical mass a each. The key
@@ -361,20 +359,20 @@ __device__ __forceinline__ bool mass_search(const Keys<KPT>& K, float lse, unsig
   return true;
 }
 
-// Mass of the list keys >= T and the number of keys equal to T (the list
-// holds every key >= T).
-template <int NT>
-__device__ __forceinline__ void mass_list_at_or_above(uint32_t C, uint32_t T, float lse,
-                                                      unsigned long long& top, uint32_t& n_eq,
-                                                      SelShared<NT, true>& sh) {
+// Block sums over the source keys: the mass of the keys below T (BELOW) or at
+// or above T, and the number of keys equal to T.
+template <int NT, bool BELOW>
+__device__ __forceinline__ void mass_split(const Src& src, uint32_t T, float lse,
+                                           unsigned long long& mass, uint32_t& n_eq,
+                                           SelShared<NT, true>& sh) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   unsigned long long m = 0;
   uint32_t e = 0;
-  for (int c = threadIdx.x; c < (int)C; c += NT) {
-    const uint32_t key = sh.cand[c].x;
-    if (key >= T) m += mass_fx(key, lse);
+  for (int c = threadIdx.x; c < src.n; c += NT) {
+    const uint32_t key = src_key(src, sh.cand, c);
+    if (BELOW ? key < T : key >= T) m += mass_fx(key, lse);
     e += key == T;
   }
 #pragma unroll
@@ -387,66 +385,24 @@ __device__ __forceinline__ void mass_list_at_or_above(uint32_t C, uint32_t T, fl
     sh.wtot[w] = e;
   }
   __syncthreads();
-  top = 0;
+  mass = 0;
   n_eq = 0;
 #pragma unroll
   for (int u = 0; u < NW; ++u) {
-    top += sh.wmass[u];
+    mass += sh.wmass[u];
     n_eq += sh.wtot[u];
   }
   __syncthreads();
 }
 
-// Mass of the register keys below T, and the number of keys equal to T.
-template <int KPT, int NT>
-__device__ __forceinline__ void mass_below(const Keys<KPT>& K, uint32_t T, float lse,
-                                           unsigned long long& below, uint32_t& n_eq,
-                                           SelShared<NT, true>& sh) {
-  constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  unsigned long long m = 0;
-  uint32_t e = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if ((K.valid >> j) & 1ull) {
-      if (K.k[j] < T) m += mass_fx(K.k[j], lse);
-      e += K.k[j] == T;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    m += __shfl_xor(m, o);
-    e += __shfl_xor(e, o);
-  }
-  if (lane == 0) {
-    sh.wmass[w] = m;
-    sh.wtot[w] = e;
-  }
-  __syncthreads();
-  below = 0;
-  n_eq = 0;
-#pragma unroll
-  for (int u = 0; u < NW; ++u) {
-    below += sh.wmass[u];
-    n_eq += sh.wtot[u];
-  }
-  __syncthreads();
-}
-
-// Mark the register keys above T and equal to T in the LDS bitmaps.
-template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ void mark_from_regs(const Keys<KPT>& K, uint32_t T,
-                                               SelShared<NT, MASS>& sh) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if ((K.valid >> j) & 1ull) {
-      const int i = key_index<KPT>(w, lane, j);
-      if (K.k[j] > T) atomicOr(&sh.gt_bits[i >> 5], 1u << (i & 31));
-      else if (K.k[j] == T) atomicOr(&sh.eq_bits[i >> 5], 1u << (i & 31));
-    }
+// Mark the row's keys above T and equal to T in the LDS bitmaps.
+template <int NT, bool MASS>
+__device__ __forceinline__ void mark_row(const float* __restrict__ row, int t, uint32_t T,
+                                         SelShared<NT, MASS>& sh) {
+  for (int i = threadIdx.x; i < t; i += NT) {
+    const uint32_t key = score_key(row[i]);
+    if (key > T) atomicOr(&sh.gt_bits[i >> 5], 1u << (i & 31));
+    else if (key == T) atomicOr(&sh.eq_bits[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
 }
@@ -533,22 +489,16 @@ __device__ __forceinline__ void scatter_list(uint32_t C, int* __restrict__ out,
   }
 }
 
-// Write the selected register keys to their slots.
-template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ void scatter_regs(const Keys<KPT>& K, int* __restrict__ out,
-                                             float* __restrict__ out_s, uint32_t cap,
-                                             const SelShared<NT, MASS>& sh) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    if ((K.valid >> j) & 1ull) {
-      const int i = key_index<KPT>(w, lane, j);
-      const int pos = out_slot<NT, MASS>((uint32_t)i, sh);
-      if (pos >= 0 && (uint32_t)pos < cap) {
-        out[pos] = i;
-        if (out_s) out_s[pos] = key_to_score(K.k[j]);
-      }
+// Write the row's selected keys to their slots.
+template <int NT, bool MASS>
+__device__ __forceinline__ void scatter_row(const float* __restrict__ row, int t,
+                                            int* __restrict__ out, float* __restrict__ out_s,
+                                            uint32_t cap, const SelShared<NT, MASS>& sh) {
+  for (int i = threadIdx.x; i < t; i += NT) {
+    const int pos = out_slot<NT, MASS>((uint32_t)i, sh);
+    if (pos >= 0 && (uint32_t)pos < cap) {
+      out[pos] = i;
+      if (out_s) out_s[pos] = key_to_score(score_key(row[i]));
     }
   }
 }
@@ -715,15 +665,15 @@ __device__ __forceinline__ bool build_candidates(const Keys<KPT>& K, int t, uint
     base = atomicAdd(&sh.ncand, wtotal);
     atomicMax(&sh.kmax, kmx);
   }
-  base = lane_read(base, 0) + incl - cnt;
+  uint32_t pos = lane_read(base, 0) + incl - cnt;
   const uint32_t dummy = (uint32_t)kCandCap + (uint32_t)lane;
   const int ibase = key_index<KPT>(w, lane, 0);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const uint32_t pos = base + (uint32_t)__builtin_popcountll(hit & (((Mask)1 << j) - 1));
     const bool h = (hit >> j) & 1;
     const uint32_t slot = (h && pos < (uint32_t)kCandCap) ? pos : dummy;
     sh.cand[slot] = make_uint2(K.k[j], (uint32_t)(ibase + (j / Keys<KPT>::GR) * kWave * Keys<KPT>::GR + (j % Keys<KPT>::GR)));
+    pos += h;
   }
   __syncthreads();
   theta_key = theta;
@@ -740,20 +690,6 @@ __device__ __forceinline__ void mark_from_list(uint32_t C, uint32_t T, SelShared
     else if (ki.x == T) atomicOr(&sh.eq_bits[ki.y >> 5], 1u << (ki.y & 31));
   }
   __syncthreads();
-}
-
-// Try the sampled-threshold path. Returns false (nothing written to the
-// output) when the threshold does not leave between N and kCandCap keys;
-// otherwise T and take_eq describe the result and the bitmaps are marked.
-template <int KPT, int NT, bool MASS>
-__device__ __forceinline__ bool topn_fast(const Keys<KPT>& K, int t, uint32_t N, uint32_t& T,
-                                          uint32_t& take_eq, SelShared<NT, MASS>& sh) {
-  uint32_t theta;
-  if (!build_candidates<KPT, NT, MASS>(K, t, N, theta, sh)) return false;
-  const uint32_t C = sh.ncand;
-  cand_radix<NT, MASS>(theta, sh.kmax, C, N, T, take_eq, sh);
-  mark_from_list<NT, MASS>(C, T, sh);
-  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -934,23 +870,18 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
 }
 
 // Write the selection once T and take are known and the bitmaps are marked:
-// indices and scores in ascending index order (scattered from the LDS list,
-// or from the register keys, reloaded), then the count, the cap flag and the
+// indices and scores in ascending index order, scattered from the LDS list
+// (`list`) or from the streamed row, then the count, the cap flag and the
 // threshold hint.
-template <int KPT, int NT, bool MASS>
+template <int NT, bool MASS>
 __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const float* row,
                                             int* out, float* out_s, bool list, uint32_t C,
                                             uint32_t T, uint32_t take, int n_sel, int hit,
                                             SelShared<NT, MASS>& sh) {
   const uint32_t cap = (uint32_t)a.idx_cap;
   emit_offsets<NT, MASS>(a.t, take, sh);
-  if (list) {
-    scatter_list<NT, MASS>(C, out, out_s, cap, sh);
-  } else {
-    Keys<KPT> K;
-    load_keys<KPT>(K, row, a.t);
-    scatter_regs<KPT, NT, MASS>(K, out, out_s, cap, sh);
-  }
+  if (list) scatter_list<NT, MASS>(C, out, out_s, cap, sh);
+  else scatter_row<NT, MASS>(row, a.t, out, out_s, cap, sh);
   if (threadIdx.x == 0) {
     a.count[head] = n_sel;
     if (a.cap_hit) a.cap_hit[head] = hit;
@@ -972,7 +903,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const float* row = a.scores + (size_t)head * a.ld;
   int* out = a.idx + (size_t)head * a.idx_cap;
   float* out_s = a.sel_scores ? a.sel_scores + (size_t)head * a.idx_cap : nullptr;
-  const uint32_t cap = (uint32_t)a.idx_cap;
   // Without scan candidates the scores are needed in registers: their loads
   // go out first and complete under the partial merge and the LDS clearing.
   const bool from_scan = !MASS && a.cand != nullptr;
@@ -1007,7 +937,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         gather_candidates<NT, MASS>(a.cand, a.cand_cnt, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
       uint32_t T, take;
       cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
-      emit_list<NT, MASS>(C, T, take, out, out_s, cap, sh);
+      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh);
       if (threadIdx.x == 0) {
         a.count[head] = a.n_budget;
         if (a.cap_hit) a.cap_hit[head] = 0;
@@ -1021,97 +951,58 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   finish_keys<KPT>(K);
   __syncthreads();
 
+  // The nb-th largest key Tn (TOPN: N; DELTA: the cap), `taken` of the keys
+  // equal to it in the top-nb set: from the sampled candidate list when it
+  // holds them (the register keys die here), else by a radix search that
+  // streams the row. sh.kmax is the top key either way.
+  const uint32_t nb = (uint32_t)a.n_budget;
+  uint32_t theta = 0;
+  const bool list = build_candidates<KPT, NT, MASS>(K, t, nb, theta, sh);
+  const uint32_t C = sh.ncand;
+  uint32_t Tn = 0, taken = nb;
+  if (list) cand_radix<NT, MASS>(theta, sh.kmax, C, nb, Tn, taken, sh);
+  else Tn = count_search<NT, MASS>(row, t, taken, sh);
+  uint32_t T = Tn, take = taken;
+  int n_sel = (int)nb, hit = 0;
   if constexpr (MASS) {
+    // Dropped mass of the top-cap set: above the target the cap binds;
+    // otherwise the smallest N lies within the top-cap set, and the mass
+    // search runs over the keys >= Tn only, with the mass below Tn spent. On
+    // the list path (which holds every key >= Tn) the mass below Tn is the
+    // whole -- the dense weights sum to one -- less the listed keys >= Tn,
+    // which avoids weighing every key.
     const float lse = a.part != nullptr ? sh.lse : a.lse_all[head];
     const unsigned long long budget = (unsigned long long)((double)a.delta_target * kMassScale);
-    const uint32_t ncap = (uint32_t)a.n_budget;
-    // The ncap-th largest key Tc; takec of the keys equal to it are in the
-    // top-ncap set. Then the dropped mass of the top-ncap set: above the
-    // target the cap binds; otherwise the smallest N lies within the top-ncap
-    // set, and the mass search runs over the keys >= Tc only, with the mass
-    // below Tc spent.
-    uint32_t theta = 0;
-    if (build_candidates<KPT, NT, MASS>(K, t, ncap, theta, sh)) {
-      // From the sampled list, which holds every key >= Tc. The mass below Tc
-      // is the whole (the dense weights sum to one) less the listed keys >= Tc,
-      // which avoids weighing every key.
-      const uint32_t C = sh.ncand;
-      uint32_t Tc = 0, takec = ncap;
-      cand_radix<NT, MASS>(theta, sh.kmax, C, ncap, Tc, takec, sh);
-      unsigned long long top = 0;
-      uint32_t n_eq = 0;
-      mass_list_at_or_above<NT>(C, Tc, lse, top, n_eq, sh);
-      const unsigned long long one = (unsigned long long)kMassScale;
-      const unsigned long long below = top < one ? one - top : 0ull;
-      uint32_t T = Tc, take = takec;
-      int n_sel = (int)ncap, hit = 1;
-      if (below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse) <= budget) {
-        hit = 0;
-        if (threadIdx.x == 0) sh.ncand_r = C;
-        __syncthreads();
-        uint32_t n_above = 0, take_T = 0;
-        if (mass_search<KPT, NT, true>(K, lse, budget - below, Tc, T, n_above, take_T, sh)) {
-          n_sel = (int)(n_above + take_T);
-          take = take_T;
-        } else {
-          // all of the mass is within the target: the single top key
-          n_sel = 1;
-          take = 1;
-          T = sh.kmax;
-        }
-      }
-      mark_from_list<NT, MASS>(C, T, sh);
-      finish_head<KPT, NT, MASS>(a, head, row, out, out_s, true, C, T, take, n_sel, hit, sh);
-      return;
-    }
-    // From the register keys (the sample misled).
-    uint32_t takec = ncap;
-    const uint32_t Tc = count_search<KPT, NT, MASS>(K, takec, sh);
+    const Src src = list ? Src{nullptr, (int)C} : Src{row, t};
     unsigned long long below = 0;
     uint32_t n_eq = 0;
-    mass_below<KPT, NT>(K, Tc, lse, below, n_eq, sh);
-    uint32_t T = Tc, take = takec;
-    int n_sel = (int)ncap, hit = 1;
-    if (below + (unsigned long long)(n_eq - takec) * mass_fx(Tc, lse) <= budget) {
+    if (list) {
+      unsigned long long top = 0;
+      mass_split<NT, false>(src, Tn, lse, top, n_eq, sh);
+      const unsigned long long one = (unsigned long long)kMassScale;
+      below = top < one ? one - top : 0ull;
+    } else {
+      mass_split<NT, true>(src, Tn, lse, below, n_eq, sh);
+    }
+    hit = 1;
+    if (below + (unsigned long long)(n_eq - taken) * mass_fx(Tn, lse) <= budget) {
       hit = 0;
       uint32_t n_above = 0, take_T = 0;
-      if (mass_search<KPT, NT, false>(K, lse, budget - below, Tc, T, n_above, take_T, sh)) {
+      if (mass_search<NT>(src, lse, budget - below, Tn, T, n_above, take_T, sh)) {
         n_sel = (int)(n_above + take_T);
         take = take_T;
       } else {
+        // all of the mass is within the target: the single top key (the
+        // lowest index among equal ones)
         n_sel = 1;
         take = 1;
-        T = count_search<KPT, NT, MASS>(K, take, sh);
+        T = sh.kmax;
       }
     }
-    mark_from_regs<KPT, NT, MASS>(K, T, sh);
-    finish_head<KPT, NT, MASS>(a, head, row, out, out_s, false, 0, T, take, n_sel, hit, sh);
-  } else {
-    uint32_t T = 0, take = 0;
-    if (topn_fast<KPT, NT, MASS>(K, t, (uint32_t)a.n_budget, T, take, sh)) {
-      finish_head<KPT, NT, MASS>(a, head, row, out, out_s, true, sh.ncand, T, take, a.n_budget, 0, sh);
-      return;
-    }
-    load_keys<KPT>(K, row, t);  // reload: the fast path lets the keys die
-    take = (uint32_t)a.n_budget;
-    T = count_search<KPT, NT, MASS>(K, take, sh);
-    mark_from_regs<KPT, NT, MASS>(K, T, sh);
-    if (a.theta_out) {
-      // the head's top key, for the next step's threshold hint
-      uint32_t kmx = 0;
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) kmx = ((K.valid >> j) & 1ull) && K.k[j] > kmx ? K.k[j] : kmx;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint32_t y = __shfl_xor(kmx, o);
-        kmx = y > kmx ? y : kmx;
-      }
-      if (threadIdx.x == 0) sh.kmax = 0;
-      __syncthreads();
-      if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh.kmax, kmx);
-    }
-    finish_head<KPT, NT, MASS>(a, head, row, out, out_s, false, 0, T, take, a.n_budget, 0, sh);
   }
+  if (list) mark_from_list<NT, MASS>(C, T, sh);
+  else mark_row<NT, MASS>(row, t, T, sh);
+  finish_head<NT, MASS>(a, head, row, out, out_s, list, C, T, take, n_sel, hit, sh);
 }
 
 constexpr int kSelThreads = 1024;
