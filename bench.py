@@ -35,24 +35,19 @@ import torch
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_scan_mistral_gqa_32k_hbm_traffic.md")
-SCAN_SOURCES = ["sparse_top_kv_head_amd/csrc/score.hip", "sparse_top_kv_head_amd/csrc/prhs_device.hpp",
-                "sparse_top_kv_head_amd/csrc/prhs_launch.hpp"]
 
 
 def scan_traffic_bytes():
     """HBM bytes per scan launch from the committed counter profile, or None when
     the scan kernel's sources changed since the counters were taken."""
-    import hashlib
+    from sparse_top_kv_head_amd.prof_summary import source_hash
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
     rec = dict(line.split(": ", 1) for line in text.splitlines()
                if line.startswith(("scan_traffic_bytes_per_launch:", "scan_source_hash:")))
-    h = hashlib.sha256()
-    for f in SCAN_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if rec.get("scan_source_hash", "").strip() != h.hexdigest()[:16]:
+    if rec.get("scan_source_hash", "").strip() != source_hash():
         return None
     return float(rec["scan_traffic_bytes_per_launch"])
 
@@ -163,6 +158,14 @@ def cpu_baseline(w, n_steps, budget_s):
                       f"of the {cfg.name} workload in {el:.1f} s"}
 
 
+def sharpest_layers(cfg, n):
+    """The n layers with the largest drawn query scale (the sharpest attention):
+    the ones whose smallest N varies below the cap."""
+    from sparse_top_kv_head_amd.synth import layer_q_scale
+    scales = [layer_q_scale(cfg, l) for l in range(cfg.n_layers)]
+    return sorted(sorted(range(cfg.n_layers), key=lambda l: -scales[l])[:n])
+
+
 def _rotated(w, copies):
     Ks = [w.K] + [w.K.clone() for _ in range(copies - 1)]
     Vs = [w.V] + [w.V.clone() for _ in range(copies - 1)]
@@ -253,12 +256,13 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
     return res
 
 
-def bench_delta(P, cfg, dev, stream, warmup, layers, steps_per_layer):
-    """Delta-budgeted decode, one layer-step per step, cycling over `layers`
-    independent KV caches (each larger than the Infinity Cache)."""
+def bench_delta(P, cfg, dev, stream, warmup, layer_ids, steps_per_layer):
+    """Delta-budgeted decode, one layer-step per step, cycling over the layers
+    `layer_ids` (independent KV caches, each larger than the Infinity Cache)."""
     from sparse_top_kv_head_amd.engine import DecodeEngine
     from sparse_top_kv_head_amd.synth import make_workload
-    ws = [make_workload(cfg, device=dev, layer=l) for l in range(layers)]
+    layers = len(layer_ids)
+    ws = [make_workload(cfg, device=dev, layer=l) for l in layer_ids]
     engs = [DecodeEngine(w.K, cfg.n_q_heads, cfg.budget) for w in ws]
 
     def mk(i):
@@ -276,7 +280,7 @@ def bench_delta(P, cfg, dev, stream, warmup, layers, steps_per_layer):
     counts = torch.stack([eng.count for eng in engs]).float()
     caps = torch.stack([eng.cap_hit for eng in engs]).float()
     res = _summary(cfg, per, gms, n_steps, scan + rows * d * e, {
-        "unit_of_step": "layer-step", "layers_cycled": layers, "delta_star": cfg.delta_star,
+        "unit_of_step": "layer-step", "layers_cycled": list(layer_ids), "delta_star": cfg.delta_star,
         "cap": cfg.budget, "mean_n_star": round(float(counts.mean()), 1),
         "min_n_star": int(counts.min()), "cap_hit_fraction": round(float(caps.mean()), 4),
         "q_scale": list(cfg.q_scale)})
@@ -379,13 +383,14 @@ def main():
     res["stream_read_ceiling"] = ceil
     res["roofline"]["frac_of_stream_ceiling"] = round(scan_gbs / ceil["gbs"], 4)
     if not a.no_extra_configs:
+        SHARP = CONFIGS["delta_16k"].replace(q_scale=(1.0, 4.0))
         other = {}
         for name, fn in (("toy", lambda: bench_topn(P, CONFIGS["toy"], dev, stream, 2, 1)),
                          ("llama2_4k", lambda: bench_topn(P, CONFIGS["llama2_4k"], dev, stream, 2, 16)),
                          ("llama2_cis_8k", lambda: bench_cis(P, CONFIGS["llama2_cis_8k"], dev, stream, 1, 2, 32)),
-                         ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 1, 2, 8)),
+                         ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 1, [0, 1], 8)),
                          ("delta_16k_sharp", lambda: bench_delta(
-                             P, CONFIGS["delta_16k"].replace(q_scale=(1.0, 4.0)), dev, stream, 1, 2, 8))):
+                             P, SHARP, dev, stream, 1, sharpest_layers(SHARP, 2), 8))):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             other[name] = fn()
         res["configs"] = other

@@ -143,6 +143,13 @@ def _place_clusters(rng, t, count, len_lo, len_hi):
     return out
 
 
+def layer_q_scale(cfg: DecodeConfig, layer: int) -> float:
+    """The query scale make_workload draws for ``layer`` (the first draw of its stream)."""
+    if cfg.q_scale[0] == cfg.q_scale[1]:
+        return cfg.q_scale[0]
+    return float(_layer_rng(cfg, layer).uniform(*cfg.q_scale))
+
+
 def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
     """Build one layer's q walk, K and V for ``cfg`` on ``device``."""
     rng = _layer_rng(cfg, layer)
