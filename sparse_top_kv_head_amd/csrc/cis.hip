@@ -4,27 +4,30 @@
 // clusters; Table VIII: dilation radius r; Fig. 8 / Fig. 9(c): sharing only
 // while the queries stay similar).
 //
-// One 256-thread workgroup per (b, h). The ascending anchor list is processed
-// in tiles of 256: each index i proposes the window [i - r, i + r] clipped to
+// One 512-thread workgroup per (b, h). The ascending anchor list is processed
+// in tiles of 512 (the next tile's indices are loaded while the current one
+// is processed): each index i proposes the window [i - r, i + r] clipped to
 // [0, t) and starts it after the largest window end seen so far (a workgroup
 // prefix-max), so windows never overlap and the output stays strictly
 // ascending. A prefix sum of the window lengths gives each window's output
-// offset; the tile's output is then written cooperatively, each thread finding
-// its source window by binary search over the tile's offsets, so the work is
-// balanced however large r is.
+// offset. Short windows (2r + 1 <= 64) are written by their own thread; longer
+// ones cooperatively, each thread finding its source window by binary search
+// over the tile's offsets, so the work stays balanced however large r is.
+// All positions are below t, so 32-bit arithmetic suffices.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
 namespace prhs {
 namespace {
 
-constexpr int kCisThreads = 256;
+constexpr int kCisThreads = 512;
+constexpr int kShortWindow = 64;
 
-__device__ __forceinline__ long long wave_inclusive_max(long long x) {
+__device__ __forceinline__ int wave_inclusive_max(int x) {
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const long long y = __shfl_up(x, o);
+    const int y = __shfl_up(x, o);
     if (lane >= o) x = x > y ? x : y;
   }
   return x;
@@ -37,10 +40,10 @@ __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
     const T* __restrict__ q_cur, const T* __restrict__ q_anchor, float sim_tau,
     int* __restrict__ reuse_ok, int D) {
   constexpr int NW = kCisThreads / kWave;
-  __shared__ long long s_end[kCisThreads];   // inclusive end offset of each window in the tile
-  __shared__ long long s_lo[kCisThreads];
-  __shared__ long long s_wmax[NW];
-  __shared__ long long s_wsum[NW];
+  __shared__ int s_end[kCisThreads];   // inclusive end offset of each window in the tile
+  __shared__ int s_lo[kCisThreads];
+  __shared__ int s_wmax[2][NW];        // double-buffered by tile parity
+  __shared__ uint32_t s_wsum[2][NW];
   __shared__ float s_red[3][NW];
 
   const int head = blockIdx.x;
@@ -50,66 +53,77 @@ __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
   const int n = max(0, min(anchor_count[head], anchor_cap));
   const int* src = anchor_idx + (size_t)head * anchor_cap;
   int* dst = out_idx + (size_t)head * out_cap;
-  const long long r = radius;
+  const int r = radius < t ? radius : t;
+  const bool short_windows = 2 * r + 1 <= kShortWindow;
 
-  long long base = 0;        // outputs written so far
-  long long prev_end = -1;   // largest window end so far
-  for (int tile = 0; tile < n; tile += kCisThreads) {
+  int base = 0;        // outputs written so far
+  int prev_end = -1;   // largest window end so far
+  int next = tid < n ? src[tid] : -1;
+  for (int tile = 0, par = 0; tile < n; tile += kCisThreads, par ^= 1) {
     const int j = tile + tid;
-    long long lo = 0, hi = -1;
-    if (j < n) {
-      const long long i = src[j];
-      if (i >= 0 && i < t) {
-        lo = i - r > 0 ? i - r : 0;
-        hi = i + r < t - 1 ? i + r : t - 1;
-      }
+    const int i = next;
+    next = j + kCisThreads < n ? src[j + kCisThreads] : -1;
+    int lo = 0, hi = -1;
+    if (j < n && i >= 0 && i < t) {
+      lo = i - r > 0 ? i - r : 0;
+      hi = i < t - 1 - r ? i + r : t - 1;
     }
     // exclusive prefix-max of window ends over the tile, seeded with prev_end
-    const long long incl_max = wave_inclusive_max(hi);
-    if (lane == kWave - 1) s_wmax[w] = incl_max;
+    const int incl_max = wave_inclusive_max(hi);
+    if (lane == kWave - 1) s_wmax[par][w] = incl_max;
     __syncthreads();
-    long long before = prev_end;
-    long long tile_max = prev_end;
+    int before = prev_end;
+    int tile_max = prev_end;
+#pragma unroll
     for (int k = 0; k < NW; ++k) {
-      const long long v = s_wmax[k];
+      const int v = s_wmax[par][k];
       if (k < w) before = before > v ? before : v;
       tile_max = tile_max > v ? tile_max : v;
     }
-    long long excl_max = __shfl_up(incl_max, 1);
+    int excl_max = __shfl_up(incl_max, 1);
     if (lane == 0) excl_max = -1;
     if (excl_max > before) before = excl_max;
     if (lo < before + 1) lo = before + 1;
-    const long long len = hi >= lo ? hi - lo + 1 : 0;
+    const uint32_t len = hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
     // prefix sum of lengths
-    const long long incl = wave_inclusive_scan(len);
-    if (lane == kWave - 1) s_wsum[w] = incl;
+    const uint32_t incl = wave_scan_u32(len);
+    if (lane == kWave - 1) s_wsum[par][w] = incl;
     __syncthreads();
-    long long off = 0, tile_total = 0;
+    uint32_t off = 0, tile_total = 0;
+#pragma unroll
     for (int k = 0; k < NW; ++k) {
-      const long long v = s_wsum[k];
+      const uint32_t v = s_wsum[par][k];
       if (k < w) off += v;
       tile_total += v;
     }
-    s_end[tid] = off + incl;
-    s_lo[tid] = lo;
-    __syncthreads();
-    for (long long p = tid; p < tile_total; p += kCisThreads) {
-      // first window whose inclusive end exceeds p
-      int a = 0, b = kCisThreads - 1;
-      while (a < b) {
-        const int mid = (a + b) >> 1;
-        if (s_end[mid] > p) b = mid;
-        else a = mid + 1;
+    off += incl - len;
+    if (short_windows) {
+      for (uint32_t k = 0; k < len; ++k) {
+        const uint32_t o = (uint32_t)base + off + k;
+        if (o < (uint32_t)out_cap) dst[o] = lo + (int)k;
       }
-      const long long start = a ? s_end[a - 1] : 0;
-      const long long o = base + p;
-      if (o < out_cap) dst[o] = (int)(s_lo[a] + (p - start));
+    } else {
+      s_end[tid] = (int)(off + len);
+      s_lo[tid] = lo;
+      __syncthreads();
+      for (int p = tid; p < (int)tile_total; p += kCisThreads) {
+        // first window whose inclusive end exceeds p
+        int a = 0, b = kCisThreads - 1;
+        while (a < b) {
+          const int mid = (a + b) >> 1;
+          if (s_end[mid] > p) b = mid;
+          else a = mid + 1;
+        }
+        const int start = a ? s_end[a - 1] : 0;
+        const long long o = (long long)base + p;
+        if (o < out_cap) dst[o] = s_lo[a] + (p - start);
+      }
+      __syncthreads();
     }
-    base += tile_total;
+    base += (int)tile_total;
     prev_end = tile_max;
-    __syncthreads();
   }
-  if (tid == 0) out_count[head] = (int)(base < out_cap ? base : out_cap);
+  if (tid == 0) out_count[head] = base < out_cap ? base : out_cap;
 
   if (reuse_ok != nullptr && q_cur != nullptr && q_anchor != nullptr) {
     float dot = 0.f, n1 = 0.f, n2 = 0.f;

@@ -751,13 +751,13 @@ __device__ __forceinline__ void emit_list(uint32_t C, uint32_t T, uint32_t take_
 // Gather the head's scan candidates (chunk by chunk, so in index order) into
 // sh.cand as (key, index). Returns false, with nothing written, when a chunk
 // carries no candidates or the total is outside [N, kCandCap].
+// `c` is this thread's chunk count (thread i holds chunk i's, loaded by the
+// caller ahead of other work; 0 past the last chunk).
 template <int NT, bool MASS>
-__device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand,
-                                                  const uint32_t* __restrict__ cand_cnt,
+__device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand, uint32_t c,
                                                   int head, int nch, uint32_t N, uint32_t& C,
                                                   SelShared<NT, MASS>& sh) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t c = (int)threadIdx.x < nch ? cand_cnt[(size_t)head * nch + threadIdx.x] : 0u;
   if (__syncthreads_or(c == kNoCand)) return false;
   uint32_t total;
   const uint32_t ex = block_exclusive_scan<NT>(c, sh.wtot, total);
@@ -908,6 +908,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const bool from_scan = !MASS && a.cand != nullptr;
   Keys<KPT> K;
   if (!from_scan) load_keys_raw<KPT>(K, row, t);
+  // the chunk counts of the scan's candidates, in flight under the partial merge
+  const uint32_t ccount = from_scan && (int)threadIdx.x < a.nchunks
+                              ? a.cand_cnt[(size_t)head * a.nchunks + threadIdx.x]
+                              : 0u;
   if (a.part != nullptr && threadIdx.x < kWave) {
     float m = -INFINITY, l = 0.f;
     for (int c = threadIdx.x; c < a.nchunks; c += kWave) {
@@ -934,7 +938,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if constexpr (!MASS) {
     uint32_t C = 0;
     if (from_scan &&
-        gather_candidates<NT, MASS>(a.cand, a.cand_cnt, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
+        gather_candidates<NT, MASS>(a.cand, ccount, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
       uint32_t T, take;
       cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
       emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh);
