@@ -17,8 +17,10 @@ launch stream. ``stream_read_ceiling`` is a plain read of 4 GiB with the
 library's probe kernel. ``configs`` reports the other workloads the same way:
 the LLaMA2-7B-shaped layer (top-256 of 4K), the CIS-reuse decode (anchor,
 reuse and amortised steps), the delta-budgeted layers (literal and sharp
-query scale) and the toy. ``cpu_baseline`` times the fp64 numpy oracle on a
-bounded sample of the headline workload.
+query scale) and the toy. ``table4`` compares dense attention with the anchor
+step, the CIS reuse step and amortised CIS-8/16 on LLaMA2-7B-shaped layers at
+the batch sizes and context lengths of the pages' Table IV. ``cpu_baseline``
+times the fp64 numpy oracle on a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -289,6 +291,63 @@ def bench_delta(P, cfg, dev, stream, warmup, layer_ids, steps_per_layer):
     return res
 
 
+TABLE4_SHAPES = [(8, 2048), (8, 4096), (8, 16384), (16, 2048), (16, 4096), (16, 16384)]
+TABLE4_BUDGET = 256   # the pages do not state it; the largest budget of their Fig. 12 sweep
+TABLE4_RADIUS = 2
+
+
+def bench_table4(P, dev, stream, steps=8):
+    """Dense against sparse attention-operator latency on LLaMA2-7B-shaped layers
+    (32 MHA heads, d = 128, fp16) at the batch sizes and context lengths of the
+    pages' Table IV: dense attention over every key; the anchor step (scan +
+    exact top-N + sparse decode); the CIS reuse step (dilation + gathered K/V +
+    decode); and CIS-s, one anchor step per s steps, amortised."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+    N, r = TABLE4_BUDGET, TABLE4_RADIUS
+    rows = []
+    for (bs, t) in TABLE4_SHAPES:
+        cfg = CONFIGS["llama2_4k"].replace(name=f"table4_bs{bs}_t{t}", batch=bs, ctx_len=t,
+                                           budget=N, steps=steps)
+        w = make_workload(cfg, device=dev)
+        kv_bytes = 2 * w.K.numel() * w.K.element_size()
+        copies = max(1, -(-(1 << 30) // kv_bytes))
+        Ks, Vs = _rotated(w, copies)
+        dense = DecodeEngine(w.K, cfg.n_q_heads, 1, dense=True)
+        anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
+        reuse = DecodeEngine(w.K, cfg.n_q_heads, min(t, (2 * r + 1) * N))
+
+        def qkv(i):
+            return w.q[i % steps], Ks[i % copies], Vs[i % copies]
+
+        dense.dense_step(*qkv(0))
+        anchor.anchor_step(*qkv(0), P.PRHS_TOPN, N)
+        reuse.reuse_step(*qkv(1), anchor.idx, anchor.count, N, r)
+        d_per, d_g = timed_steps([lambda i=i: dense.dense_step(*qkv(i)) for i in range(steps)], stream)
+        a_per, a_g = timed_steps([lambda i=i: anchor.anchor_step(*qkv(i), P.PRHS_TOPN, N)
+                                  for i in range(steps)], stream)
+        r_per, r_g = timed_steps([lambda i=i: reuse.reuse_step(*qkv(i), anchor.idx, anchor.count, N, r)
+                                  for i in range(steps)], stream)
+        d_ms, a_ms, r_ms = d_g / steps, a_g / steps, r_g / steps
+        cis = {s: (a_ms + (s - 1) * r_ms) / s for s in (8, 16)}
+        rows.append({"batch": bs, "ctx_len": t, "dense_ms": round(d_ms, 5),
+                     "dense_hbm_gbs": round(kv_bytes / (d_ms / 1e3) / 1e9, 1),
+                     "anchor_ms": round(a_ms, 5), "reuse_ms": round(r_ms, 5),
+                     "cis8_ms": round(cis[8], 5), "cis16_ms": round(cis[16], 5),
+                     "dense_over_anchor": round(d_ms / a_ms, 3),
+                     "dense_over_cis8": round(d_ms / cis[8], 3),
+                     "dense_over_cis16": round(d_ms / cis[16], 3),
+                     "p50_ms": {"dense": round(float(np.median(d_per)), 5),
+                                "anchor": round(float(np.median(a_per)), 5),
+                                "reuse": round(float(np.median(r_per)), 5)}})
+        del w, Ks, Vs, dense, anchor, reuse
+        torch.cuda.empty_cache()
+    return {"budget": N, "radius": r, "steps_per_mode": steps,
+            "shape": "LLaMA2-7B layer: 32 MHA heads, d = 128, fp16 K/V",
+            "cis_s": "one exact retrieval per s steps, reuse with +-radius dilation otherwise",
+            "rows": rows}
+
+
 def main():
     a = _parse()
     if a.gpus != 1:
@@ -394,6 +453,8 @@ def main():
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             other[name] = fn()
         res["configs"] = other
+        print("[bench] table4 sweep", file=sys.stderr, flush=True)
+        res["table4"] = bench_table4(P, dev, stream)
     if a.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -71,7 +71,8 @@ enum { PRHS_F32 = 0, PRHS_F16 = 1 };
 enum { PRHS_TOPN = 0, PRHS_DELTA = 1 };
 
 /* Operations for prhs_workspace_bytes. */
-enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2, PRHS_OP_ANCHOR_STEP = 3 };
+enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2, PRHS_OP_ANCHOR_STEP = 3,
+       PRHS_OP_DENSE = 4 };
 
 /* Largest context length the selection kernel keeps resident on chip. */
 #define PRHS_MAX_SELECT_CTX 65536
@@ -214,6 +215,22 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
  */
 int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* lse_all,
                       float* delta, float* tau, hipStream_t stream);
+
+/*
+ * prhs_dense_decode -- dense decode attention over all t keys: the baseline
+ * the sparse path is compared with (Table IV: attention-operator latency
+ * against dense FlashAttention; Abstract: speedup over the dense baseline).
+ *
+ *   out[b,h,:]  = sum_i softmax_i(s[b,h,:]) * V[b,h/G,i,:],  s as in prhs_score
+ *   lse[b,h]    = log sum_i exp(s[b,h,i])   (the dense log-sum-exp)
+ *
+ * One pass: K and V are each read once, split over keys; the per-split
+ * (max, sum, output) partials are merged exactly. No scores are written.
+ * q, k, v, out, lse and ws are required; q, k, v 16-byte aligned.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_DENSE, 0) bytes.
+ */
+int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                      float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by `op` (PRHS_OP_*) for these dims; `cap` is the
  * idx_cap of prhs_sparse_decode / prhs_anchor_step and is ignored otherwise.

@@ -295,6 +295,12 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
     if (d.head_dim == 128) launch_split<float, 128>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
     else launch_split<float, 64>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
   }
+  return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream);
+}
+
+hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float* out,
+                        float* lse_sel, const float* lse_all, float* delta, float* tau,
+                        hipStream_t stream) {
   const int nheads = d.batch * d.n_q_heads;
   if (d.head_dim == 128)
     hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(nheads), dim3(128), 0, stream, part, nsplit,

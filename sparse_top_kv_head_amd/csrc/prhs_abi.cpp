@@ -91,6 +91,9 @@ size_t score_ws(const prhs_dims* d) { return score_part_bytes(d); }
 
 size_t decode_ws(const prhs_dims* d, int cap) { return decode_part_bytes(d, cap); }
 
+// Dense decode: split partials over all t keys.
+size_t dense_ws(const prhs_dims* d) { return decode_part_bytes(d, d->ctx_len); }
+
 // Anchor-step workspace: scan partials | candidate counts | candidates |
 // selected scores | decode partials, each part 256-byte aligned.
 struct StepWs {
@@ -140,6 +143,7 @@ size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap) {
     case PRHS_OP_SELECT: return 0;
     case PRHS_OP_DECODE: return cap >= 1 ? decode_ws(dims, cap) : 0;
     case PRHS_OP_ANCHOR_STEP: return cap >= 1 ? step_ws(dims, cap) : 0;
+    case PRHS_OP_DENSE: return dense_ws(dims);
     default: return 0;
   }
 }
@@ -237,6 +241,21 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
   return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel_scores, scores,
                                     lse_all, out, lse_sel, delta, tau, ws, stream),
                 stream, "prhs_sparse_decode");
+}
+
+int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                      float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!q || !k || !v || !out || !lse) return fail(PRHS_E_NULL, "q, k, v, out and lse are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(PRHS_E_ALIGN, "q, k and v must be 16-byte aligned");
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < dense_ws(dims))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", dense_ws(dims), ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  return finish(prhs::launch_dense(*dims, q, k, v, out, lse, ws, stream), stream,
+                "prhs_dense_decode");
 }
 
 int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,

@@ -70,6 +70,16 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
                          const float* lse_all, float* out, float* lse_sel, float* delta, float* tau,
                          void* ws, hipStream_t stream);
 
+// Merge split partials [head][nsplit][d + 2] = (o[d], max, sum) of every head
+// into out and lse; delta/tau from lse_all when given.
+hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float* out,
+                        float* lse, const float* lse_all, float* delta, float* tau,
+                        hipStream_t stream);
+
+// Dense attention over all ctx_len keys: split partials in ws, then the merge.
+hipError_t launch_dense(const prhs_dims& d, const void* q, const void* k, const void* v,
+                        float* out, float* lse, void* ws, hipStream_t stream);
+
 // Read `bytes` (a multiple of 16) of device memory once (HBM ceiling probe).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

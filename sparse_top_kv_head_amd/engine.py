@@ -15,10 +15,11 @@ class DecodeEngine:
     """Buffers and calls for one layer shape.
 
     K, V layout [B, H_kv, t, d]; q [B, H_q, d]; index capacity ``cap`` per head
-    (TOPN budget, DELTA cap, or the dilated size of a reused set).
+    (TOPN budget, DELTA cap, or the dilated size of a reused set). ``dense``
+    sizes the workspace for dense_step as well.
     """
 
-    def __init__(self, K: torch.Tensor, n_q_heads: int, cap: int, device=None):
+    def __init__(self, K: torch.Tensor, n_q_heads: int, cap: int, device=None, dense=False):
         self.dims = P.make_dims(K, n_q_heads)
         d = self.dims
         dev = device or K.device
@@ -41,7 +42,8 @@ class DecodeEngine:
         self.theta = torch.full((d.batch, d.n_q_heads), float("nan"), **f32)
         ws = max(P.prhs_workspace_bytes(d, P.PRHS_OP_SCORE),
                  P.prhs_workspace_bytes(d, P.PRHS_OP_DECODE, cap),
-                 P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, cap))
+                 P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, cap),
+                 P.prhs_workspace_bytes(d, P.PRHS_OP_DENSE) if dense else 0)
         self.ws = torch.empty(((ws + 15) // 16 * 16,), dtype=torch.uint8, device=dev)
 
     def score(self, q, K, stream=None):
@@ -87,6 +89,10 @@ class DecodeEngine:
                          q if q_anchor is not None else None, q_anchor, sim_tau, self.idx, self.cap,
                          self.count, self.reuse_ok if q_anchor is not None else None, stream=stream)
         self.decode(q, K, V, use_scores=False, stream=stream)
+
+    def dense_step(self, q, K, V, stream=None):
+        """Dense attention over every key (the baseline): out and lse_all."""
+        P.prhs_dense_decode(self.dims, q, K, V, self.out, self.lse_all, self.ws, stream=stream)
 
     def dropped_mass(self, stream=None):
         P.prhs_dropped_mass(self.dims, self.lse_sel, self.lse_all, self.delta, self.tau, stream=stream)

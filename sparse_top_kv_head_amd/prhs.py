@@ -36,12 +36,13 @@ PRHS_OP_SCORE = 0
 PRHS_OP_SELECT = 1
 PRHS_OP_DECODE = 2
 PRHS_OP_ANCHOR_STEP = 3
+PRHS_OP_DENSE = 4
 PRHS_MAX_SELECT_CTX = 65536
 
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-    "prhs_dropped_mass", "prhs_anchor_step", "prhs_workspace_bytes", "prhs_status_string",
-    "prhs_last_error",
+    "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode", "prhs_workspace_bytes",
+    "prhs_status_string", "prhs_last_error",
 )
 # measurement aid (include/prhs_probe.h)
 PROBE_EXPORTED = ("prhs_probe_stream_read",)
@@ -89,6 +90,7 @@ def lib():
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
+        L.prhs_dense_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.prhs_probe_stream_read.restype = ctypes.c_int
         L.prhs_workspace_bytes.argtypes = [dp, i32, i32]
@@ -98,7 +100,7 @@ def lib():
         L.prhs_last_error.argtypes = []
         L.prhs_last_error.restype = ctypes.c_char_p
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-                     "prhs_dropped_mass", "prhs_anchor_step"):
+                     "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +191,13 @@ def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
 def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):
     _check(lib().prhs_dropped_mass(ctypes.byref(dims), _p(lse_sel), _p(lse_all), _p(delta),
                                    _p(tau), _stream(stream)))
+
+
+def prhs_dense_decode(dims, q, k, v, out, lse, ws=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(lib().prhs_dense_decode(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(out), _p(lse),
+                                   _p(ws), ws_bytes, _stream(stream)))
 
 
 def prhs_anchor_step(dims, mode, n_budget, delta_target, q, k, v, scores, lse_all, idx, idx_cap,

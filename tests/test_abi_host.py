@@ -73,6 +73,13 @@ def _decode(L, d, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cap=64, cnt=FAKE, s=FAKE, ls
                                 sel, s, lse, out, lsel, dl, tau, ws, wsb, None)
 
 
+def _dense(L, d, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_dense_decode(ctypes.byref(d) if d is not None else None, q, k, v, out, lse, ws,
+                               wsb, None)
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("n_q_heads", 7, P.PRHS_E_DIMS),
     ("n_kv_heads", 0, P.PRHS_E_DIMS),
@@ -94,6 +101,7 @@ def test_bad_dims_rejected_by_every_call(L, field, value, code):
     assert _select(L, d) == code
     assert _cis(L, d) == code
     assert _decode(L, d) == code
+    assert _dense(L, d) == code
     assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == code
     assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0) == 0
     assert L.prhs_last_error()
@@ -172,6 +180,19 @@ def test_decode_argument_checks(L):
     assert _decode(L, d, v=FAKE_MIS) == P.PRHS_E_ALIGN
     assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, None, None, None) == P.PRHS_E_NULL
     assert L.prhs_dropped_mass(ctypes.byref(d), None, FAKE, FAKE, None, None) == P.PRHS_E_NULL
+
+
+def test_dense_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DENSE, 0)
+    assert need == 2 * 8 * 4 * (128 + 2) * 4     # B*H_q*ceil(1000/256)*(d+2) floats
+    assert _dense(L, None) == P.PRHS_E_NULL
+    for kw in ("q", "k", "v", "out", "lse"):
+        assert _dense(L, d, **{kw: None}) == P.PRHS_E_NULL, kw
+    assert _dense(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _dense(L, d, wsb=need - 1) == P.PRHS_E_WORKSPACE
+    assert _dense(L, d, k=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert _dense(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
 
 
 def _step(L, d, mode=P.PRHS_TOPN, n=64, dt=0.05, q=FAKE, k=FAKE, v=FAKE, s=FAKE, lse=FAKE,

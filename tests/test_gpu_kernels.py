@@ -340,6 +340,50 @@ def test_sparse_decode(B, Hq, Hkv, d, t, dtype, N, with_scores):
     assert torch.equal(d2, delta)
 
 
+# ---------------------------------------------------------------------------
+# prhs_dense_decode: the dense baseline (N = t)
+# ---------------------------------------------------------------------------
+
+DENSE_CASES = [
+    # B, Hq, Hkv, d, t, dtype, row padding (strided K/V)
+    (1, 4, 4, 64, 512, torch.float32, 0),
+    (1, 8, 2, 128, 3000, torch.float16, 0),
+    (2, 8, 1, 64, 1537, torch.float16, 8),
+    (1, 6, 2, 128, 700, torch.float16, 0),      # G = 3: sub-groups of 2 and 1
+    (2, 32, 32, 128, 4096, torch.float16, 0),   # LLaMA2-7B-shaped layer
+    (1, 32, 8, 128, 9000, torch.float16, 0),    # Mistral-7B-shaped GQA layer
+    (1, 16, 2, 128, 255, torch.float16, 0),     # G = 8, a single partial chunk
+    (1, 2, 1, 128, 1, torch.float32, 0),        # one key
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,t,dtype,pad", DENSE_CASES)
+def test_dense_decode(B, Hq, Hkv, d, t, dtype, pad):
+    dev = _dev()
+    K = _kv(B, Hkv, t, d, dtype, 31, pad)
+    V = _kv(B, Hkv, t, d, dtype, 32, pad)
+    g = torch.Generator().manual_seed(33)
+    q = (torch.randn((B, Hq, d), generator=g) * 2.0).to(dtype).to(dev)
+    q64, K64, V64 = _np(q), _np(K), _np(V)
+    s = O.attention_scores(q64, K64)
+    _, lse = O.dense_softmax(s)
+    G = Hq // Hkv
+    dims = P.make_dims(K, Hq)
+    out = torch.full((B, Hq, d), float("nan"), device=dev)
+    lse_g = torch.full((B, Hq), float("nan"), device=dev)
+    ws = P.alloc_workspace(dims, P.PRHS_OP_DENSE, device=dev)
+    P.prhs_dense_decode(dims, q, K, V, out, lse_g, ws)
+    torch.cuda.synchronize()
+    o_g, l_g = _np(out), _np(lse_g)
+    every = np.arange(t)
+    for b in range(B):
+        for h in range(Hq):
+            o_ref, lse_ref = O.sparse_attention(s[b, h], V64[b, h // G], every)
+            assert np.max(np.abs(o_g[b, h] - o_ref)) <= OUT_TOL, (b, h)
+            assert abs(l_g[b, h] - lse[b, h]) <= 1e-4, (b, h)
+            assert abs(lse_ref - lse[b, h]) <= 1e-12
+
+
 def test_sparse_decode_edge_counts():
     """Empty sets, counts above the capacity, out-of-range indices."""
     dev = _dev()
