@@ -258,6 +258,56 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
     return res
 
 
+def bench_growing(P, cfg, dev, stream, copies, n_steps):
+    """Growing cache on the CIS workload's shape: step s appends one K/V row
+    (a row copy into the cache, timed) and attends over t = t0 + s keys, with
+    exact retrieval every refresh_period-th step and dilated reuse otherwise."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import make_workload
+    t0 = cfg.ctx_len
+    big = cfg.replace(ctx_len=t0 + n_steps)
+    w = make_workload(big, device=dev)
+    Ks, Vs = _rotated(w, copies)
+    src_k, src_v = w.K.clone(), w.V.clone()   # rows appended step by step
+    N, r, Pd = cfg.budget, cfg.radius, cfg.refresh_period
+    anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
+    reuse = DecodeEngine(w.K, cfg.n_q_heads, min(big.ctx_len, (2 * r + 1) * N))
+
+    def mk(i):
+        t = t0 + i
+        K, V = Ks[i % copies], Vs[i % copies]
+        q = w.q[i % cfg.steps]
+
+        def step():
+            K[:, :, t - 1].copy_(src_k[:, :, t - 1])
+            V[:, :, t - 1].copy_(src_v[:, :, t - 1])
+            anchor.set_ctx_len(t)
+            reuse.set_ctx_len(t)
+            if i % Pd == 0:
+                anchor.anchor_step(q, K, V, P.PRHS_TOPN, N)
+            else:
+                reuse.reuse_step(q, K, V, anchor.idx, anchor.count, N, r)
+        return step
+
+    for i in range(Pd):
+        mk(i)()
+    per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
+    e, d = cfg.elem_bytes, cfg.head_dim
+    is_a = np.array([i % Pd == 0 for i in range(n_steps)])
+    res = _summary(cfg, per, gms, n_steps,
+                   (cfg.batch * cfg.n_kv_heads * (t0 + n_steps // 2) * d * e * is_a.sum()
+                    + 2 * distinct_rows(reuse.idx, reuse.count, cfg.group) * d * e * (~is_a).sum())
+                   / n_steps,
+                   {"t0": t0, "t_final": t0 + n_steps, "budget": N, "radius": r, "refresh_period": Pd,
+                    "anchor_ms_p50": round(float(np.median(per[is_a])), 5),
+                    "reuse_ms_p50": round(float(np.median(per[~is_a])), 5),
+                    "note": "one K/V row appended per step (timed); hbm bytes are approximate "
+                            "(scan at the mean t, reused rows of the last step)"})
+    del w, Ks, Vs, src_k, src_v, anchor, reuse
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_delta(P, cfg, dev, stream, warmup, layer_ids, steps_per_layer):
     """Delta-budgeted decode, one layer-step per step, cycling over the layers
     `layer_ids` (independent KV caches, each larger than the Infinity Cache)."""
@@ -447,6 +497,8 @@ def main():
         for name, fn in (("toy", lambda: bench_topn(P, CONFIGS["toy"], dev, stream, 2, 1)),
                          ("llama2_4k", lambda: bench_topn(P, CONFIGS["llama2_4k"], dev, stream, 2, 16)),
                          ("llama2_cis_8k", lambda: bench_cis(P, CONFIGS["llama2_cis_8k"], dev, stream, 1, 2, 32)),
+                         ("llama2_cis_8k_growing", lambda: bench_growing(
+                             P, CONFIGS["llama2_cis_8k"], dev, stream, 2, 32)),
                          ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 1, [0, 1], 8)),
                          ("delta_16k_sharp", lambda: bench_delta(
                              P, SHARP, dev, stream, 1, sharpest_layers(SHARP, 2), 8))):

@@ -22,6 +22,7 @@ class DecodeEngine:
     def __init__(self, K: torch.Tensor, n_q_heads: int, cap: int, device=None, dense=False):
         self.dims = P.make_dims(K, n_q_heads)
         d = self.dims
+        self._capacity = d.ctx_len
         dev = device or K.device
         self.nheads = d.batch * d.n_q_heads
         self.cap = cap
@@ -45,6 +46,18 @@ class DecodeEngine:
                  P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, cap),
                  P.prhs_workspace_bytes(d, P.PRHS_OP_DENSE) if dense else 0)
         self.ws = torch.empty(((ws + 15) // 16 * 16,), dtype=torch.uint8, device=dev)
+
+    @property
+    def capacity(self):
+        """Largest context length the buffers hold (the K/V tensor the engine was built on)."""
+        return self._capacity
+
+    def set_ctx_len(self, t):
+        """Attend over the first t keys of the cache from now on (a growing cache:
+        t = t0 + step). Buffers and the workspace are sized for the capacity."""
+        if not 1 <= t <= self._capacity:
+            raise ValueError(f"ctx_len {t} outside [1, {self._capacity}]")
+        self.dims.ctx_len = t
 
     def score(self, q, K, stream=None):
         P.prhs_score(self.dims, q, K, self.scores, self.lse_all, self.ws, stream=stream)

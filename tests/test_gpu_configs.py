@@ -189,3 +189,58 @@ def test_delta_16k_layer_sampled(variant):
             assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL
             if not int(eng.cap_hit[b, h]):
                 assert eng.delta[b, h].item() <= cfg.delta_star + DELTA_TOL
+
+
+def test_growing_cache_cis_schedule():
+    """Growing cache (t = t0 + step: one more key visible each step) with the
+    CIS schedule of the LLaMA2 reuse workload: exact top-N at anchor steps (the
+    threshold hint carried across the growth) and the anchor's set dilated and
+    clipped to the current t at reuse steps. Sets, outputs and delta against the
+    oracle on the first t keys of every step."""
+    dev = _dev()
+    t0, steps = 3000, 10
+    cfg = CONFIGS["llama2_cis_8k"].replace(batch=1, ctx_len=t0 + steps, steps=steps)
+    w = make_workload(cfg, device=dev)
+    N, r, Pd = cfg.budget, cfg.radius, cfg.refresh_period
+    anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
+    reuse = DecodeEngine(w.K, cfg.n_q_heads, min(cfg.ctx_len, (2 * r + 1) * N))
+    cache = _KVCache(w)
+    heads = _sample_heads(cfg, 8, 5)
+    anchor_sets = {}
+    for step in range(steps):
+        t = t0 + step
+        anchor.set_ctx_len(t)
+        reuse.set_ctx_len(t)
+        q64 = _np(w.q[step])
+        if step % Pd == 0:
+            anchor.topn_step(w.q[step], w.K, w.V, N)
+            torch.cuda.synchronize()
+            for (b, h) in heads:
+                s_full, V = _oracle_scores(cache, q64, b, h, cfg.group)
+                s, V = s_full[:t], V[:t]
+                n = int(anchor.count[b, h])
+                gidx = anchor.idx[b, h, :n].cpu().numpy()
+                assert n == N and gidx.max() < t
+                exact = check_set_band(gidx, s, N)
+                S_ref = O.topn_select(s, N) if exact else gidx
+                o_ref, _ = O.sparse_attention(s, V, S_ref)
+                d_ref, _ = O.dropped_mass(s, S_ref)
+                assert np.max(np.abs(_np(anchor.out[b, h]) - o_ref)) <= OUT_TOL
+                assert abs(anchor.delta[b, h].item() - d_ref) <= DELTA_TOL
+                anchor_sets[(b, h)] = gidx
+            continue
+        reuse.reuse_step(w.q[step], w.K, w.V, anchor.idx, anchor.count, N, r)
+        reuse.score(w.q[step], w.K)
+        reuse.dropped_mass()
+        torch.cuda.synchronize()
+        for (b, h) in heads:
+            s_full, V = _oracle_scores(cache, q64, b, h, cfg.group)
+            s, V = s_full[:t], V[:t]
+            D_ref = O.cis_dilate(anchor_sets[(b, h)], r, t)
+            n = int(reuse.count[b, h])
+            assert np.array_equal(reuse.idx[b, h, :n].cpu().numpy(), D_ref)
+            o_ref, lse_ref = O.sparse_attention(s, V, D_ref)
+            d_ref, _ = O.dropped_mass(s, D_ref)
+            assert np.max(np.abs(_np(reuse.out[b, h]) - o_ref)) <= OUT_TOL
+            assert abs(reuse.lse_sel[b, h].item() - lse_ref) <= 1e-3
+            assert abs(reuse.delta[b, h].item() - d_ref) <= DELTA_TOL
