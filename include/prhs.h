@@ -217,6 +217,43 @@ int prhs_dropped_mass(const prhs_dims* dims, const float* lse_sel, const float* 
                       float* delta, float* tau, hipStream_t stream);
 
 /*
+ * prhs_adaptive_step -- one decode step of critical-index-set sharing with a
+ * per-head similarity gate (Fig. 4: one query's set serves the next queries,
+ * dilated; Fig. 8 and Fig. 9(c): sharing only while sim(q, q') >= tau;
+ * Table VIII: block size s, threshold tau, radius r).
+ *
+ * Per head h, all on the device:
+ *   refresh[h] = force_refresh || anchor_count[h] == 0
+ *                || cos(q[h], anchor_q[h]) < sim_tau
+ *   refresh heads: the exact top-n_budget over a fresh score scan (as
+ *     prhs_anchor_step in TOPN mode) becomes the head's anchor set
+ *     (anchor_idx, anchor_count), anchor_q[h] = q[h], attention runs over the
+ *     new set, and lse_all, delta and tau are written;
+ *   other heads: the anchor set dilated by `radius` (as prhs_cis_reuse) is
+ *     written to dil_idx / dil_count and attention runs over it with gathered
+ *     K and V rows; lse_all, delta and tau are left untouched (no scan ran).
+ * A KV group with no refreshing head is not scanned. The caller passes
+ * force_refresh = 1 on every s-th step (block size s); the gate then decides
+ * the steps in between.
+ * State, caller-owned and kept across steps: anchor_idx [B,H_q,n_budget],
+ * anchor_count [B,H_q] (all zero before the first step), anchor_q [B,H_q,d]
+ * (element type of q). Outputs: refresh [B,H_q] int32 0/1; sim (nullable)
+ * fp32 [B,H_q], the cosine the gate used (NaN before a head's first anchor);
+ * out, lse_sel; delta and tau (nullable; tau needs delta); theta (nullable)
+ * as in prhs_anchor_step. Requires 1 <= n_budget <= t, radius >= 0,
+ * dil_cap >= min(t, (2 radius + 1) n_budget), t <= PRHS_MAX_SELECT_CTX,
+ * sim_tau not NaN.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_ANCHOR_STEP, dil_cap) bytes.
+ */
+int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
+                       int32_t force_refresh, float sim_tau, const void* q, const void* k,
+                       const void* v, float* scores, float* lse_all, int32_t* anchor_idx,
+                       int32_t* anchor_count, void* anchor_q, int32_t* dil_idx, int32_t dil_cap,
+                       int32_t* dil_count, int32_t* refresh, float* sim, float* out,
+                       float* lse_sel, float* delta, float* tau, float* theta, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
  * prhs_dense_decode -- dense decode attention over all t keys: the baseline
  * the sparse path is compared with (Table IV: attention-operator latency
  * against dense FlashAttention; Abstract: speedup over the dense baseline).

@@ -38,8 +38,9 @@ __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
     const int* __restrict__ anchor_idx, int anchor_cap, const int* __restrict__ anchor_count,
     int radius, int t, int* __restrict__ out_idx, int out_cap, int* __restrict__ out_count,
     const T* __restrict__ q_cur, const T* __restrict__ q_anchor, float sim_tau,
-    int* __restrict__ reuse_ok, int D) {
+    int* __restrict__ reuse_ok, int D, const int* __restrict__ skip) {
   constexpr int NW = kCisThreads / kWave;
+  if (skip != nullptr && skip[blockIdx.x] != 0) return;  // head left untouched
   __shared__ int s_end[kCisThreads];   // inclusive end offset of each window in the tile
   __shared__ int s_lo[kCisThreads];
   __shared__ int s_wmax[2][NW];        // double-buffered by tile parity
@@ -156,23 +157,78 @@ __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
   }
 }
 
+// Similarity gate of the adaptive step: one wave per head. Sharing continues
+// while cos(q, q_anchor) >= sim_tau (Fig. 8 / Fig. 9(c)); otherwise, when the
+// step is forced, or before the head's first anchor, the head refreshes and
+// its anchor query becomes q.
+template <typename T>
+__global__ __launch_bounds__(256) void cis_gate_kernel(const T* __restrict__ q,
+                                                       T* __restrict__ q_anchor,
+                                                       const int* __restrict__ anchor_count,
+                                                       int force, float sim_tau,
+                                                       int* __restrict__ refresh,
+                                                       float* __restrict__ sim, int D,
+                                                       int nheads) {
+  const int head = blockIdx.x * (256 / kWave) + (int)(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  if (head >= nheads) return;
+  const T* qc = q + (size_t)head * D;
+  T* qa = q_anchor + (size_t)head * D;
+  float dot = 0.f, n1 = 0.f, n2 = 0.f;
+  for (int c = lane; c < D; c += kWave) {
+    const float x = (float)qc[c];
+    const float y = (float)qa[c];
+    dot += x * y;
+    n1 += x * x;
+    n2 += y * y;
+  }
+  dot = wave_sum(dot);
+  n1 = wave_sum(n1);
+  n2 = wave_sum(n2);
+  const bool has_anchor = anchor_count[head] > 0;
+  const float den = sqrtf(n1) * sqrtf(n2);
+  const bool share = has_anchor && den > 0.f && dot >= sim_tau * den;
+  const bool fresh = force != 0 || !share;
+  if (fresh)
+    for (int c = lane; c < D; c += kWave) qa[c] = qc[c];
+  if (lane == 0) {
+    refresh[head] = fresh ? 1 : 0;
+    if (sim != nullptr) sim[head] = has_anchor && den > 0.f ? dot / den : __builtin_nanf("");
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gate(const prhs_dims& d, const void* q, void* q_anchor, const int* anchor_count,
+                       int force, float sim_tau, int* refresh, float* sim, hipStream_t stream) {
+  const int nheads = d.batch * d.n_q_heads;
+  const dim3 grid((nheads + 3) / 4);
+  if (d.dtype == PRHS_F16)
+    hipLaunchKernelGGL((cis_gate_kernel<__half>), grid, dim3(256), 0, stream,
+                       static_cast<const __half*>(q), static_cast<__half*>(q_anchor), anchor_count,
+                       force, sim_tau, refresh, sim, d.head_dim, nheads);
+  else
+    hipLaunchKernelGGL((cis_gate_kernel<float>), grid, dim3(256), 0, stream,
+                       static_cast<const float*>(q), static_cast<float*>(q_anchor), anchor_count,
+                       force, sim_tau, refresh, sim, d.head_dim, nheads);
+  return hipGetLastError();
+}
 
 hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                       const int* anchor_count, int radius, const void* q_cur, const void* q_anchor,
                       float sim_tau, int* out_idx, int out_cap, int* out_count, int* reuse_ok,
-                      hipStream_t stream) {
+                      hipStream_t stream, const int* skip) {
   const int nheads = d.batch * d.n_q_heads;
   if (d.dtype == PRHS_F16)
     hipLaunchKernelGGL((cis_dilate_kernel<__half>), dim3(nheads), dim3(kCisThreads), 0, stream,
                        anchor_idx, anchor_cap, anchor_count, radius, d.ctx_len, out_idx, out_cap,
                        out_count, static_cast<const __half*>(q_cur),
-                       static_cast<const __half*>(q_anchor), sim_tau, reuse_ok, d.head_dim);
+                       static_cast<const __half*>(q_anchor), sim_tau, reuse_ok, d.head_dim, skip);
   else
     hipLaunchKernelGGL((cis_dilate_kernel<float>), dim3(nheads), dim3(kCisThreads), 0, stream,
                        anchor_idx, anchor_cap, anchor_count, radius, d.ctx_len, out_idx, out_cap,
                        out_count, static_cast<const float*>(q_cur),
-                       static_cast<const float*>(q_anchor), sim_tau, reuse_ok, d.head_dim);
+                       static_cast<const float*>(q_anchor), sim_tau, reuse_ok, d.head_dim, skip);
   return hipGetLastError();
 }
 

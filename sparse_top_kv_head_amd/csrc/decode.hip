@@ -27,7 +27,7 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ p, int nspl
                                            float* __restrict__ out, float* __restrict__ lse_sel,
                                            const float* __restrict__ lse_all,
                                            float* __restrict__ delta, float* __restrict__ tau,
-                                           int head) {
+                                           const int* __restrict__ mix, int head) {
   float m = -INFINITY, l = 0.f, o = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += 8) {
     float ms[8], ls[8], os[8];
@@ -66,7 +66,7 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ p, int nspl
   if (col == 0) {
     const float lse = l > 0.f ? m + __logf(l) : -INFINITY;
     lse_sel[head] = lse;
-    if (lse_all != nullptr && delta != nullptr) {
+    if (lse_all != nullptr && delta != nullptr && (mix == nullptr || mix[head] != 0)) {
       const float dlt = fminf(fmaxf(-expm1f(lse - lse_all[head]), 0.f), 1.f);
       delta[head] = dlt;
       if (tau != nullptr) tau[head] = 1.f - dlt;
@@ -74,21 +74,28 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ p, int nspl
   }
 }
 
-// One split of one head. HAS_SCORES: the scores of the selected rows are read,
-// from sel_scores (compact, in idx order) when it is given, else gathered from
-// `scores`; otherwise they are computed from gathered K rows. Each wave owns
+constexpr int kModeScores = 0;  // scores of the selected rows are given
+constexpr int kModeGather = 1;  // scores are computed from gathered K rows
+constexpr int kModeMixed = 2;   // per head, by mix[head]: given (idx) or gathered (idx2)
+
+// One split of one head. With given scores, the scores of the selected rows are
+// read from sel_scores (compact, in idx order) when it is given, else gathered
+// from `scores`; otherwise they are computed from gathered K rows. In the mixed
+// mode a head with mix[head] != 0 takes (idx, count, sel_scores) and any other
+// head (idx2, count2) with gathered K rows. Each wave owns
 // 64 consecutive rows of the split; their V rows are requested as soon as the
 // indices are known, before the split's weights are formed. The split leaves
 // (max, sum, o[D]) for the merge kernel. (Merging in the last split to arrive
 // needs a device-scope fence per workgroup, which costs far more on this chip
 // than the separate merge launch.)
-template <typename T, int D, bool HAS_SCORES>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int* __restrict__ idx, int idx_cap, const int* __restrict__ count,
-    const float* __restrict__ sel_scores, const float* __restrict__ scores, int Hq, int Hkv,
-    int t, long long sb, long long sh, long long st, int ld, float scale,
-    float* __restrict__ part, int nsplit) {
+    const float* __restrict__ sel_scores, const float* __restrict__ scores,
+    const int* __restrict__ idx2, int idx2_cap, const int* __restrict__ count2,
+    const int* __restrict__ mix, int Hq, int Hkv, int t, long long sb, long long sh,
+    long long st, int ld, float scale, float* __restrict__ part, int nsplit) {
   constexpr int NW = kDecThreads / kWave;
   constexpr int ROWS = kDecodeRows;
   constexpr int E = Elem<T>::kPer16B;
@@ -115,16 +122,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int c = lane % LPR;
   const int rr = lane / LPR;
 
-  const int n = max(0, min(count[head], idx_cap));
+  const bool has_scores = MODE == kModeScores || (MODE == kModeMixed && mix[head] != 0);
+  const int* ih = has_scores || MODE == kModeGather ? idx : idx2;
+  const int icap = has_scores || MODE == kModeGather ? idx_cap : idx2_cap;
+  const int* ch = has_scores || MODE == kModeGather ? count : count2;
+  const int n = max(0, min(ch[head], icap));
   const int beg = split * ROWS;
   const int nr = max(0, min(ROWS, n - beg));
-  const int* irow = idx + (size_t)head * idx_cap + beg;
+  const int* irow = ih + (size_t)head * icap + beg;
 
   for (int i = tid; i < nr; i += kDecThreads) {
     const int id = irow[i];
     const bool ok = id >= 0 && id < t;
     sidx[i] = ok ? id : -1;
-    if constexpr (HAS_SCORES)
+    if (has_scores)
       sp[i] = !ok ? -INFINITY
                   : sel_scores ? sel_scores[(size_t)head * idx_cap + beg + i]
                                : scores[(size_t)head * ld + id];
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
   const size_t row_bytes = (size_t)st * sizeof(T);
-  if constexpr (!HAS_SCORES) {
+  if (MODE != kModeScores && !has_scores) {
     const uint4 qv = load16(q + (size_t)head * D + c * E);
     const char* kbase = reinterpret_cast<const char*>(k + kv_off) + c * 16;
 #pragma unroll 1
@@ -241,10 +252,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
                                                          float* __restrict__ lse_sel,
                                                          const float* __restrict__ lse_all,
                                                          float* __restrict__ delta,
-                                                         float* __restrict__ tau) {
+                                                         float* __restrict__ tau,
+                                                         const int* __restrict__ mix) {
   const int head = blockIdx.x;
   merge_head<D>(part + (size_t)head * nsplit * (D + 2), nsplit, threadIdx.x, out, lse_sel,
-                lse_all, delta, tau, head);
+                lse_all, delta, tau, mix, head);
 }
 
 __global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restrict__ lse_sel,
@@ -258,26 +270,51 @@ __global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restri
   if (tau != nullptr) tau[h] = 1.f - dlt;
 }
 
-template <typename T, int D>
-void launch_split(const prhs_dims& d, const void* q, const void* k, const void* v, const int* idx,
-                  int idx_cap, const int* count, const float* sel_scores, const float* scores,
-                  float* part, int nsplit, hipStream_t stream) {
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* idx;
+  int idx_cap;
+  const int* count;
+  const float* sel_scores;
+  const float* scores;
+  const int* idx2;
+  int idx2_cap;
+  const int* count2;
+  const int* mix;
+};
+
+template <typename T, int D, int MODE>
+void launch_split_mode(const prhs_dims& d, const SplitArgs& a, float* part, int nsplit,
+                       hipStream_t stream) {
   dim3 grid(nsplit, d.batch * d.n_q_heads);
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
-  if (scores || sel_scores)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, true>), grid, dim3(kDecThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, idx_cap, count, sel_scores, scores, d.n_q_heads,
-                       d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
-                       (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
-                       part, nsplit);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, false>), grid, dim3(kDecThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), idx, idx_cap, count, sel_scores, scores, d.n_q_heads,
-                       d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
-                       (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale,
-                       part, nsplit);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, MODE>), grid, dim3(kDecThreads), 0, stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), a.idx, a.idx_cap, a.count, a.sel_scores, a.scores,
+                     a.idx2, a.idx2_cap, a.count2, a.mix, d.n_q_heads, d.n_kv_heads, d.ctx_len,
+                     (long long)d.kv_stride_b, (long long)d.kv_stride_h, (long long)d.kv_stride_t,
+                     d.scores_ld, scale, part, nsplit);
+}
+
+template <typename T, int D>
+void launch_split(const prhs_dims& d, const SplitArgs& a, float* part, int nsplit,
+                  hipStream_t stream) {
+  if (a.mix != nullptr) launch_split_mode<T, D, kModeMixed>(d, a, part, nsplit, stream);
+  else if (a.scores || a.sel_scores) launch_split_mode<T, D, kModeScores>(d, a, part, nsplit, stream);
+  else launch_split_mode<T, D, kModeGather>(d, a, part, nsplit, stream);
+}
+
+void launch_split_any(const prhs_dims& d, const SplitArgs& a, float* part, int nsplit,
+                      hipStream_t stream) {
+  if (d.dtype == PRHS_F16) {
+    if (d.head_dim == 128) launch_split<__half, 128>(d, a, part, nsplit, stream);
+    else launch_split<__half, 64>(d, a, part, nsplit, stream);
+  } else {
+    if (d.head_dim == 128) launch_split<float, 128>(d, a, part, nsplit, stream);
+    else launch_split<float, 64>(d, a, part, nsplit, stream);
+  }
 }
 
 }  // namespace
@@ -288,26 +325,34 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
                          float* delta, float* tau, void* ws, hipStream_t stream) {
   const int nsplit = decode_nsplit(idx_cap);
   float* part = static_cast<float*>(ws);
-  if (d.dtype == PRHS_F16) {
-    if (d.head_dim == 128) launch_split<__half, 128>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
-    else launch_split<__half, 64>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
-  } else {
-    if (d.head_dim == 128) launch_split<float, 128>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
-    else launch_split<float, 64>(d, q, k, v, idx, idx_cap, count, sel_scores, scores, part, nsplit, stream);
-  }
+  const SplitArgs a{q, k, v, idx, idx_cap, count, sel_scores, scores, nullptr, 0, nullptr, nullptr};
+  launch_split_any(d, a, part, nsplit, stream);
   return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream);
+}
+
+hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k, const void* v,
+                               const int* mix, const int* idx, int idx_cap, const int* count,
+                               const float* sel_scores, const int* idx2, int idx2_cap,
+                               const int* count2, const float* lse_all, float* out,
+                               float* lse_sel, float* delta, float* tau, void* ws,
+                               hipStream_t stream) {
+  const int nsplit = decode_nsplit(idx_cap > idx2_cap ? idx_cap : idx2_cap);
+  float* part = static_cast<float*>(ws);
+  const SplitArgs a{q, k, v, idx, idx_cap, count, sel_scores, nullptr, idx2, idx2_cap, count2, mix};
+  launch_split_any(d, a, part, nsplit, stream);
+  return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream, mix);
 }
 
 hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float* out,
                         float* lse_sel, const float* lse_all, float* delta, float* tau,
-                        hipStream_t stream) {
+                        hipStream_t stream, const int* mix) {
   const int nheads = d.batch * d.n_q_heads;
   if (d.head_dim == 128)
     hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(nheads), dim3(128), 0, stream, part, nsplit,
-                       out, lse_sel, lse_all, delta, tau);
+                       out, lse_sel, lse_all, delta, tau, mix);
   else
     hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(nheads), dim3(64), 0, stream, part, nsplit,
-                       out, lse_sel, lse_all, delta, tau);
+                       out, lse_sel, lse_all, delta, tau, mix);
   return hipGetLastError();
 }
 

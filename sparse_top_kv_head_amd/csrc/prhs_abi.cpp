@@ -243,6 +243,78 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                 stream, "prhs_sparse_decode");
 }
 
+int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
+                       int32_t force_refresh, float sim_tau, const void* q, const void* k,
+                       const void* v, float* scores, float* lse_all, int32_t* anchor_idx,
+                       int32_t* anchor_count, void* anchor_q, int32_t* dil_idx, int32_t dil_cap,
+                       int32_t* dil_count, int32_t* refresh, float* sim, float* out,
+                       float* lse_sel, float* delta, float* tau, float* theta, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
+    return fail(PRHS_E_DIMS, "selection supports ctx_len <= %d", PRHS_MAX_SELECT_CTX);
+  if (!q || !k || !v || !scores || !lse_all || !anchor_idx || !anchor_count || !anchor_q ||
+      !dil_idx || !dil_count || !refresh || !out || !lse_sel)
+    return fail(PRHS_E_NULL, "q, k, v, scores, lse_all, anchor_idx, anchor_count, anchor_q, "
+                             "dil_idx, dil_count, refresh, out and lse_sel are required");
+  if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(scores))
+    return fail(PRHS_E_ALIGN, "q, k, v and scores must be 16-byte aligned");
+  if (n_budget < 1 || n_budget > dims->ctx_len)
+    return fail(PRHS_E_BUDGET, "n_budget %d outside [1, %d]", n_budget, dims->ctx_len);
+  if (radius < 0) return fail(PRHS_E_BUDGET, "radius must be >= 0");
+  if (std::isnan(sim_tau)) return fail(PRHS_E_BUDGET, "sim_tau is NaN");
+  const long long need_ll = (2LL * radius + 1) * (long long)n_budget;
+  const long long need = need_ll < dims->ctx_len ? need_ll : dims->ctx_len;
+  if (dil_cap < need)
+    return fail(PRHS_E_CAPACITY, "dil_cap %d < min(t, (2r+1)*n_budget) = %lld", dil_cap, need);
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < step_ws(dims, dil_cap))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", step_ws(dims, dil_cap),
+                ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  char* w = static_cast<char*>(ws);
+  const StepWs L = step_ws_layout(dims, dil_cap);
+  float2* part = reinterpret_cast<float2*>(w + L.part);
+  float* sel = reinterpret_cast<float*>(w + L.sel);
+  hipError_t err = prhs::launch_gate(*dims, q, anchor_q, anchor_count, force_refresh ? 1 : 0,
+                                     sim_tau, refresh, sim, stream);
+  prhs::ScanCand cd;
+  cd.active = refresh;
+  if (theta) {
+    cd.theta = theta;
+    cd.cand = reinterpret_cast<uint2*>(w + L.cand);
+    cd.cand_cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+  }
+  if (err == hipSuccess) err = prhs::launch_score(*dims, q, k, scores, nullptr, part, stream, &cd);
+  if (err == hipSuccess) {
+    prhs::SelectArgs a;
+    a.scores = scores;
+    a.lse_all = lse_all;
+    a.part = part;
+    a.mode = PRHS_TOPN;
+    a.n_budget = n_budget;
+    a.idx = anchor_idx;
+    a.idx_cap = n_budget;
+    a.count = anchor_count;
+    a.sel_scores = sel;
+    a.cand = cd.cand;
+    a.cand_cnt = cd.cand_cnt;
+    a.theta_out = theta;
+    a.active = refresh;
+    err = prhs::launch_select(*dims, a, stream);
+  }
+  if (err == hipSuccess)
+    err = prhs::launch_cis(*dims, anchor_idx, n_budget, anchor_count, radius, nullptr, nullptr, 0.f,
+                           dil_idx, dil_cap, dil_count, nullptr, stream, refresh);
+  if (err == hipSuccess)
+    err = prhs::launch_decode_mixed(*dims, q, k, v, refresh, anchor_idx, n_budget, anchor_count,
+                                    sel, dil_idx, dil_cap, dil_count, lse_all, out, lse_sel, delta,
+                                    tau, w + L.dec, stream);
+  return finish(err, stream, "prhs_adaptive_step");
+}
+
 int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(dims);

@@ -25,6 +25,7 @@ struct ScanCand {
   const float* theta = nullptr;
   uint2* cand = nullptr;
   uint32_t* cand_cnt = nullptr;
+  const int* active = nullptr;   // per query head; a KV group with no active head is skipped
 };
 
 // Writes scores; with ws, also the per-chunk (max, sum) partials of the dense
@@ -50,6 +51,7 @@ struct SelectArgs {
   const uint2* cand = nullptr;    // scan candidates (TOPN)
   const uint32_t* cand_cnt = nullptr;
   float* theta_out = nullptr;     // next-step threshold hint (TOPN)
+  const int* active = nullptr;    // per head; inactive heads are left untouched
   int t = 0;
   int ld = 0;
   int nchunks = 0;
@@ -60,7 +62,13 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& a, hipStream_t st
 hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                       const int* anchor_count, int radius, const void* q_cur, const void* q_anchor,
                       float sim_tau, int* out_idx, int out_cap, int* out_count, int* reuse_ok,
-                      hipStream_t stream);
+                      hipStream_t stream, const int* skip = nullptr);
+
+// Similarity gate of the adaptive CIS step, per head: refresh = force, or no
+// anchor yet, or cos(q, q_anchor) < sim_tau; a refreshing head's q_anchor
+// becomes q. sim (nullable) receives the cosine (NaN without an anchor).
+hipError_t launch_gate(const prhs_dims& d, const void* q, void* q_anchor, const int* anchor_count,
+                       int force, float sim_tau, int* refresh, float* sim, hipStream_t stream);
 
 // Scores of the selected rows come from sel_scores (compact, in idx order) if
 // given, else are gathered from scores, else computed from gathered K rows.
@@ -74,7 +82,17 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
 // into out and lse; delta/tau from lse_all when given.
 hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float* out,
                         float* lse, const float* lse_all, float* delta, float* tau,
-                        hipStream_t stream);
+                        hipStream_t stream, const int* mix = nullptr);
+
+// Decode where head h attends over (idx, count, sel_scores) when mix[h] != 0
+// and over (idx2, count2) with scores from gathered K rows otherwise; delta
+// and tau are written for the mix[h] != 0 heads only.
+hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k, const void* v,
+                               const int* mix, const int* idx, int idx_cap, const int* count,
+                               const float* sel_scores, const int* idx2, int idx2_cap,
+                               const int* count2, const float* lse_all, float* out,
+                               float* lse_sel, float* delta, float* tau, void* ws,
+                               hipStream_t stream);
 
 // Dense attention over all ctx_len keys: split partials in ws, then the merge.
 hipError_t launch_dense(const prhs_dims& d, const void* q, const void* k, const void* v,

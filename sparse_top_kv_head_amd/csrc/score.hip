@@ -19,7 +19,8 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
-// With `theta` (a per-head score threshold), the chunk's keys whose score is
+// With `active` (per query head), a workgroup whose group has no active head
+// does nothing. With `theta` (a per-head score threshold), the chunk's keys whose score is
 // >= theta are also written, in index order, as (score bits, index) pairs to
 // cand[head][chunk][0:n] with n in cand_cnt[head][chunk]; a head whose theta is
 // not finite gets the count kNoCand.
@@ -27,8 +28,8 @@ template <typename T, int D, int G, int CHUNK = kScoreChunk, int UMAX = kScoreLo
 __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
     float2* __restrict__ part, const float* __restrict__ theta, uint2* __restrict__ cand,
-    uint32_t* __restrict__ cand_cnt, int Hq, int Hkv, int t, long long sb, long long sh,
-    long long st, int ld, int nchunks, int g_off, float scale) {
+    uint32_t* __restrict__ cand_cnt, const int* __restrict__ active, int Hq, int Hkv, int t,
+    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, float scale) {
   constexpr int NW = kScoreThreads / kWave;
   constexpr int E = Elem<T>::kPer16B;
   constexpr int LPR = D / E;
@@ -52,6 +53,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   const int w = threadIdx.x / kWave;
   const int c = lane % LPR;
   const int rr = lane / LPR;
+  if (active != nullptr) {
+    // the whole workgroup leaves when no head of the group is active
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < G; ++j) any |= active[b * Hq + h0 + j] != 0;
+    if (!any) return;
+  }
 
   uint4 qv[G];
 #pragma unroll
@@ -175,7 +183,7 @@ void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
   hipLaunchKernelGGL((score_scan_kernel<T, D, G>), grid, dim3(kScoreThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), scores, part, cd.theta,
-                     cd.cand, cd.cand_cnt, d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
+                     cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
                      (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
 }
 

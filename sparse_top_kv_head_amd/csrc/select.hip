@@ -889,6 +889,7 @@ __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const
   }
 }
 
+// Heads with a zero `active` flag (when given) are left untouched.
 // lse_all is read (DELTA) unless `part` is given: then the head's per-chunk
 // (max, sum) partials of the score scan are merged here, the result used and
 // written to lse_all. TOPN with scan candidates (cand != NULL) selects from
@@ -899,6 +900,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ SelShared<NT, MASS> sh;
 
   const int head = blockIdx.x;
+  if (a.active != nullptr && a.active[head] == 0) return;
   const int t = a.t;
   const float* row = a.scores + (size_t)head * a.ld;
   int* out = a.idx + (size_t)head * a.idx_cap;

@@ -121,3 +121,51 @@ class DecodeEngine:
             for (q, K, V) in steps:
                 self.anchor_step(q, K, V, mode, n_budget, delta_target)
         return g
+
+
+class AdaptiveEngine:
+    """Critical-index-set sharing with a per-head similarity gate, one call per step.
+
+    Every ``period``-th step refreshes every head; in between, a head reuses its
+    anchor set (dilated by ``radius``) while the cosine of its query with its
+    anchor query stays at or above ``sim_tau``, and refreshes otherwise. The
+    anchor sets and anchor queries live on the device across steps; the
+    per-step decisions come back in ``refresh`` (1 = exact retrieval this step).
+    """
+
+    def __init__(self, K: torch.Tensor, n_q_heads: int, n_budget: int, radius: int, period: int,
+                 sim_tau: float, hint=True):
+        self.dims = P.make_dims(K, n_q_heads)
+        d = self.dims
+        dev = K.device
+        self.n_budget, self.radius, self.period, self.sim_tau = n_budget, radius, period, sim_tau
+        self.dil_cap = min(d.ctx_len, (2 * radius + 1) * n_budget)
+        B, H = d.batch, d.n_q_heads
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.scores = torch.empty((B, H, d.scores_ld), **f32)
+        self.lse_all = torch.empty((B, H), **f32)
+        self.anchor_idx = torch.empty((B, H, n_budget), **i32)
+        self.anchor_count = torch.zeros((B, H), **i32)
+        self.anchor_q = torch.zeros((B, H, d.head_dim), dtype=K.dtype, device=dev)
+        self.dil_idx = torch.empty((B, H, self.dil_cap), **i32)
+        self.dil_count = torch.zeros((B, H), **i32)
+        self.refresh = torch.zeros((B, H), **i32)
+        self.sim = torch.empty((B, H), **f32)
+        self.out = torch.empty((B, H, d.head_dim), **f32)
+        self.lse_sel = torch.empty((B, H), **f32)
+        self.delta = torch.empty((B, H), **f32)
+        self.tau = torch.empty((B, H), **f32)
+        self.theta = torch.full((B, H), float("nan"), **f32) if hint else None
+        ws = P.prhs_workspace_bytes(d, P.PRHS_OP_ANCHOR_STEP, self.dil_cap)
+        self.ws = torch.empty(((ws + 15) // 16 * 16,), dtype=torch.uint8, device=dev)
+        self.step_no = 0
+
+    def step(self, q, K, V, stream=None):
+        force = self.step_no % self.period == 0
+        P.prhs_adaptive_step(self.dims, self.n_budget, self.radius, force, self.sim_tau, q, K, V,
+                             self.scores, self.lse_all, self.anchor_idx, self.anchor_count,
+                             self.anchor_q, self.dil_idx, self.dil_cap, self.dil_count,
+                             self.refresh, self.sim, self.out, self.lse_sel, self.delta, self.tau,
+                             self.theta, self.ws, stream=stream)
+        self.step_no += 1

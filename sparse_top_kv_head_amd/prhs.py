@@ -41,7 +41,8 @@ PRHS_MAX_SELECT_CTX = 65536
 
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-    "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode", "prhs_workspace_bytes",
+    "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step", "prhs_dense_decode",
+    "prhs_workspace_bytes",
     "prhs_status_string", "prhs_last_error",
 )
 # measurement aid (include/prhs_probe.h)
@@ -91,6 +92,8 @@ def lib():
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
         L.prhs_dense_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.prhs_adaptive_step.argtypes = [dp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_probe_stream_read.argtypes = [vp, sz, vp, vp]
         L.prhs_probe_stream_read.restype = ctypes.c_int
         L.prhs_workspace_bytes.argtypes = [dp, i32, i32]
@@ -100,7 +103,8 @@ def lib():
         L.prhs_last_error.argtypes = []
         L.prhs_last_error.restype = ctypes.c_char_p
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
-                     "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode"):
+                     "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode",
+                     "prhs_adaptive_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,6 +195,20 @@ def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
 def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):
     _check(lib().prhs_dropped_mass(ctypes.byref(dims), _p(lse_sel), _p(lse_all), _p(delta),
                                    _p(tau), _stream(stream)))
+
+
+def prhs_adaptive_step(dims, n_budget, radius, force_refresh, sim_tau, q, k, v, scores, lse_all,
+                       anchor_idx, anchor_count, anchor_q, dil_idx, dil_cap, dil_count, refresh,
+                       sim, out, lse_sel, delta=None, tau=None, theta=None, ws=None, ws_bytes=None,
+                       stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(lib().prhs_adaptive_step(ctypes.byref(dims), n_budget, radius, int(bool(force_refresh)),
+                                    sim_tau, _p(q), _p(k), _p(v), _p(scores), _p(lse_all),
+                                    _p(anchor_idx), _p(anchor_count), _p(anchor_q), _p(dil_idx),
+                                    dil_cap, _p(dil_count), _p(refresh), _p(sim), _p(out),
+                                    _p(lse_sel), _p(delta), _p(tau), _p(theta), _p(ws), ws_bytes,
+                                    _stream(stream)))
 
 
 def prhs_dense_decode(dims, q, k, v, out, lse, ws=None, ws_bytes=None, stream=None):

@@ -102,6 +102,7 @@ def test_bad_dims_rejected_by_every_call(L, field, value, code):
     assert _cis(L, d) == code
     assert _decode(L, d) == code
     assert _dense(L, d) == code
+    assert _adaptive(L, d) == code
     assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == code
     assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0) == 0
     assert L.prhs_last_error()
@@ -225,6 +226,38 @@ def test_anchor_step_argument_checks(L):
     assert _step(L, d, ws=None) == P.PRHS_E_WORKSPACE
     assert _step(L, d, wsb=need - 1) == P.PRHS_E_WORKSPACE
     assert _step(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
+
+
+def _adaptive(L, d, n=64, r=2, force=0, tau=0.9, q=FAKE, k=FAKE, v=FAKE, s=FAKE, lse=FAKE,
+              aidx=FAKE, acnt=FAKE, aq=FAKE, didx=FAKE, dcap=320, dcnt=FAKE, ref=FAKE, out=FAKE,
+              lsel=FAKE, dl=FAKE, tau_out=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_adaptive_step(ctypes.byref(d) if d is not None else None, n, r, force, tau, q, k,
+                                v, s, lse, aidx, acnt, aq, didx, dcap, dcnt, ref, None, out, lsel,
+                                dl, tau_out, None, ws, wsb, None)
+
+
+def test_adaptive_step_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_ANCHOR_STEP, 320)
+    assert _adaptive(L, None) == P.PRHS_E_NULL
+    assert _adaptive(L, _dims(head_dim=96)) == P.PRHS_E_DIMS
+    assert _adaptive(L, _dims(ctx_len=P.PRHS_MAX_SELECT_CTX + 1,
+                              scores_ld=P.PRHS_MAX_SELECT_CTX + 4)) == P.PRHS_E_DIMS
+    for kw in ("q", "k", "v", "s", "lse", "aidx", "acnt", "aq", "didx", "dcnt", "ref", "out", "lsel"):
+        assert _adaptive(L, d, **{kw: None}) == P.PRHS_E_NULL, kw
+    assert _adaptive(L, d, dl=None) == P.PRHS_E_NULL          # tau without delta
+    assert _adaptive(L, d, s=FAKE_MIS) == P.PRHS_E_ALIGN
+    assert _adaptive(L, d, n=0) == P.PRHS_E_BUDGET
+    assert _adaptive(L, d, n=1001) == P.PRHS_E_BUDGET
+    assert _adaptive(L, d, r=-1) == P.PRHS_E_BUDGET
+    assert _adaptive(L, d, tau=math.nan) == P.PRHS_E_BUDGET
+    assert _adaptive(L, d, dcap=319) == P.PRHS_E_CAPACITY      # (2r+1)*n = 320
+    assert _adaptive(L, d, n=300, dcap=999) == P.PRHS_E_CAPACITY   # min(t, 1500) = 1000
+    assert _adaptive(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _adaptive(L, d, wsb=need - 1) == P.PRHS_E_WORKSPACE
+    assert _adaptive(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
 
 
 def test_status_strings(L):

@@ -13,7 +13,7 @@ import torch
 
 from oracle import prhs_oracle as O
 from sparse_top_kv_head_amd import prhs as P
-from sparse_top_kv_head_amd.engine import DecodeEngine
+from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
 from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
 from tests.parity_util import DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band
 
@@ -244,3 +244,71 @@ def test_growing_cache_cis_schedule():
             assert np.max(np.abs(_np(reuse.out[b, h]) - o_ref)) <= OUT_TOL
             assert abs(reuse.lse_sel[b, h].item() - lse_ref) <= 1e-3
             assert abs(reuse.delta[b, h].item() - d_ref) <= DELTA_TOL
+
+
+@pytest.mark.parametrize("period,sim_tau", [(4, 0.7), (8, 0.97), (16, 0.95), (4, 0.99)])
+def test_adaptive_cis_gate(period, sim_tau):
+    """Per-head gated CIS (one exact retrieval per `period` steps, and in between
+    whenever the cosine of a head's query with its anchor query falls below
+    sim_tau) on the LLaMA2 reuse workload's head shape. Every gate decision is
+    checked against the fp64 cosine wherever that cosine is more than 1e-4 from
+    the threshold; refreshed heads' exact sets, reused heads' dilated sets,
+    outputs and delta against the oracle on sampled heads."""
+    dev = _dev()
+    cfg = CONFIGS["llama2_cis_8k"].replace(batch=1, steps=12)
+    w = make_workload(cfg, device=dev)
+    N, r, t, H = cfg.budget, cfg.radius, cfg.ctx_len, cfg.n_q_heads
+    eng = AdaptiveEngine(w.K, H, N, r, period, sim_tau)
+    cache = _KVCache(w)
+    heads = _sample_heads(cfg, 8, 11)
+    anchor_q, anchor_set = {}, {}
+    refreshes = 0
+    for step in range(cfg.steps):
+        eng.step(w.q[step], w.K, w.V)
+        torch.cuda.synchronize()
+        q64 = _np(w.q[step])
+        ref = eng.refresh.cpu().numpy()
+        sim = eng.sim.cpu().numpy()
+        refreshes += int(ref.sum())
+        for h in range(H):
+            force = step % period == 0
+            if h in anchor_q:
+                a, x = anchor_q[h], q64[0, h]
+                cos = float(a @ x) / (np.linalg.norm(a) * np.linalg.norm(x))
+                assert abs(sim[0, h] - cos) <= 1e-5
+                if not force and abs(cos - sim_tau) > 1e-4:
+                    assert ref[0, h] == int(cos < sim_tau), (step, h, cos)
+            else:
+                assert ref[0, h] == 1
+            if force:
+                assert ref[0, h] == 1
+            if ref[0, h]:
+                anchor_q[h] = q64[0, h].copy()
+        for (b, h) in heads:
+            s, V = _oracle_scores(cache, q64, b, h, cfg.group)
+            if ref[b, h]:
+                n = int(eng.anchor_count[b, h])
+                gidx = eng.anchor_idx[b, h, :n].cpu().numpy()
+                assert n == N
+                exact = check_set_band(gidx, s, N)
+                S = O.topn_select(s, N) if exact else gidx
+                anchor_set[(b, h)] = gidx
+                d_ref, _ = O.dropped_mass(s, S)
+                assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL
+            else:
+                S = O.cis_dilate(anchor_set[(b, h)], r, t)
+                n = int(eng.dil_count[b, h])
+                assert np.array_equal(eng.dil_idx[b, h, :n].cpu().numpy(), S)
+            o_ref, lse_ref = O.sparse_attention(s, V, S)
+            assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL
+            assert abs(eng.lse_sel[b, h].item() - lse_ref) <= 1e-3
+    # forced refreshes on steps 0, period, ...; the gate adds some in between.
+    # Adjacent queries of this walk have cosine ~0.98, so a threshold of 0.99
+    # refreshes every head at every step, one of 0.7 never fires in 4 steps.
+    forced = H * len(range(0, cfg.steps, period))
+    if sim_tau >= 0.99:
+        assert refreshes == H * cfg.steps
+    elif sim_tau <= 0.7:
+        assert refreshes == forced
+    else:
+        assert forced < refreshes < H * cfg.steps
