@@ -154,6 +154,32 @@ def cis_dilate(anchor_idx, r, t):
     return np.flatnonzero(mask)
 
 
+def random_expansion(anchor_idx, draws, m):
+    """The RandomExpansion control of Table VI (Panel A): the anchor's set grown
+    to a matched size m with keys chosen at random instead of by dilation.
+
+    Reading (the pages give the control's name and its matched budget only):
+    the random choice is made by per-key draws passed in as an input, so that
+    any implementation makes the same choice: the m - |S_a| keys outside the
+    anchor set with the smallest draws, the lower index winning equal draws.
+    Draws are used as 23-bit integers (draws & 0x7FFFFF).
+
+    anchor_idx: ascending anchor set; draws: [t] non-negative integers; m:
+    target size, |S_a| <= m <= t. Returns the ascending expanded set.
+    """
+    S = np.asarray(anchor_idx, dtype=np.int64)
+    d = np.asarray(draws, dtype=np.int64) & 0x7FFFFF
+    t = d.size
+    if not S.size <= m <= t:
+        raise ValueError("m outside [|S_a|, t]")
+    member = np.zeros(t, dtype=bool)
+    member[S] = True
+    outside = np.flatnonzero(~member)
+    order = np.lexsort((outside, d[outside]))     # by draw, then by index
+    extra = outside[order[:m - S.size]]
+    return np.sort(np.concatenate([S, extra]))
+
+
 def cis_schedule(n_steps, period, q_steps=None, sim_tau=None):
     """Which decode steps run exact retrieval, and which anchor each step reuses.
 

@@ -304,6 +304,42 @@ def check_cis_properties(dilate_fn):
     assert list(D) == list(range(37, 54))
 
 
+def check_random_expansion(expand_fn):
+    """Random expansion: against a sequential argmin draw (a different procedure),
+    an optimality certificate, and the special cases."""
+    rng = np.random.default_rng(41)
+    for trial in range(50):
+        t = int(rng.integers(1, 120))
+        n = int(rng.integers(1, t + 1))
+        S = np.sort(rng.choice(t, n, replace=False))
+        m = int(rng.integers(n, t + 1))
+        hi = 1 << 23 if trial % 3 else 8            # some trials with many equal draws
+        draws = rng.integers(0, hi, t) | (rng.integers(0, 2, t) << 30)   # bits above 23 are ignored
+        E = expand_fn(S, draws, m)
+        # sequential draw: repeatedly take the outsider with the smallest
+        # 23-bit draw, the lowest index among equal ones
+        low = [int(x) & 0x7FFFFF for x in draws]
+        taken = set(int(i) for i in S)
+        while len(taken) < m:
+            best = min((i for i in range(t) if i not in taken), key=lambda i: (low[i], i))
+            taken.add(best)
+        assert list(E) == sorted(taken)
+        assert np.all(np.diff(E) > 0) and np.isin(S, E).all() and E.size == m
+        chosen = np.setdiff1d(E, S)
+        rest = np.setdiff1d(np.arange(t), E)
+        if chosen.size and rest.size:
+            worst = max((low[i], i) for i in chosen)
+            assert all((low[j], j) > worst for j in rest)
+    S = np.array([3, 9, 10])
+    assert list(expand_fn(S, np.arange(20), 3)) == [3, 9, 10]
+    assert list(expand_fn(S, np.arange(20)[::-1], 20)) == list(range(20))
+    assert list(expand_fn(S, np.zeros(20, dtype=np.int64), 6)) == [0, 1, 2, 3, 9, 10]
+
+
+def test_random_expansion_pins():
+    check_random_expansion(O.random_expansion)
+
+
 def test_cis_fig4_golden():
     check_cis_fig4(O.cis_dilate)
 
@@ -409,6 +445,27 @@ def _dilate_unclipped_left(S, r, t):
     return D[D >= r] if r > 0 else D
 
 
+def _expand_high_index_ties(S, draws, m):
+    d = np.asarray(draws, dtype=np.int64) & 0x7FFFFF
+    t = d.size
+    out = np.setdiff1d(np.arange(t), S)
+    order = np.lexsort((-out, d[out]))
+    return np.sort(np.concatenate([S, out[order[:m - len(S)]]]))
+
+
+def _expand_unmasked(S, draws, m):
+    d = np.asarray(draws, dtype=np.int64)
+    out = np.setdiff1d(np.arange(d.size), S)
+    order = np.lexsort((out, d[out]))
+    return np.sort(np.concatenate([S, out[order[:m - len(S)]]]))
+
+
+def _expand_ignoring_members(S, draws, m):
+    d = np.asarray(draws, dtype=np.int64) & 0x7FFFFF
+    order = np.lexsort((np.arange(d.size), d))
+    return np.union1d(S, order[:m - len(S)])
+
+
 def _delta_via_kept_count(s, S):
     d, tau = O.dropped_mass(s, S)
     t = len(s)
@@ -434,6 +491,9 @@ def _delta_swapped(s, S):
     (check_tau_vs_lse, (O.sparse_attention, _delta_via_kept_count)),
     (check_delta_properties, (_delta_swapped,)),
     (check_decomposition_and_bound, (O.sparse_attention, _delta_via_kept_count)),
+    (check_random_expansion, (_expand_high_index_ties,)),
+    (check_random_expansion, (_expand_unmasked,)),
+    (check_random_expansion, (_expand_ignoring_members,)),
 ])
 def test_planted_mistake_is_caught(check, args):
     with pytest.raises((AssertionError, ValueError, IndexError)):
