@@ -72,7 +72,7 @@ enum { PRHS_TOPN = 0, PRHS_DELTA = 1 };
 
 /* Operations for prhs_workspace_bytes. */
 enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2, PRHS_OP_ANCHOR_STEP = 3,
-       PRHS_OP_DENSE = 4 };
+       PRHS_OP_DENSE = 4, PRHS_OP_EXPAND = 5 };
 
 /* Largest context length the selection kernel keeps resident on chip. */
 #define PRHS_MAX_SELECT_CTX 65536
@@ -251,6 +251,26 @@ int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
                        int32_t* anchor_count, void* anchor_q, int32_t* dil_idx, int32_t dil_cap,
                        int32_t* dil_count, int32_t* refresh, float* sim, float* out,
                        float* lse_sel, float* delta, float* tau, float* theta, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * prhs_random_expand -- the RandomExpansion control of Table VI (Panel A): the
+ * anchor set grown to a matched size m with randomly chosen keys instead of
+ * by dilation, for budget-matched comparisons with prhs_cis_reuse.
+ *
+ *   out = anchor set  U  the (m - |S_a|) keys outside it with the smallest
+ *         draws[b,h,i] & 0x7FFFFF (the lower index on equal draws)
+ *
+ * draws: int32 [B, H_q, t] contiguous, caller-supplied random integers (only
+ * the low 23 bits are used). anchor_idx [B,H_q,anchor_cap] ascending and
+ * unique, anchor_count <= anchor_cap <= m <= t, out_cap >= m; out ascending,
+ * out_count[b,h] = m. t <= PRHS_MAX_SELECT_CTX.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_EXPAND, 0) bytes (a control
+ * score row per head).
+ */
+int prhs_random_expand(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                       const int32_t* anchor_count, const int32_t* draws, int32_t m,
+                       int32_t* out_idx, int32_t out_cap, int32_t* out_count, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -197,7 +197,45 @@ __global__ __launch_bounds__(256) void cis_gate_kernel(const T* __restrict__ q,
   }
 }
 
+// Control scores of the random expansion (Table VI, Panel A: RandomExpansion,
+// the budget-matched control of dilation): members of the anchor set score
+// kMember, every other key minus its 23-bit draw, so that the exact top-m of
+// these scores is the anchor set plus the m - |S_a| outside keys of smallest
+// draw (the lower index on equal draws, by the selection's tie rule). One
+// workgroup per head marks the set in an LDS bitmap, then writes the row.
+constexpr float kMember = 3.0e38f;
+
+__global__ __launch_bounds__(256) void expand_scores_kernel(
+    const int* __restrict__ anchor_idx, int anchor_cap, const int* __restrict__ anchor_count,
+    const int* __restrict__ draws, int t, float* __restrict__ out, int ld) {
+  __shared__ uint32_t member[PRHS_MAX_SELECT_CTX / 32];
+  const int head = blockIdx.x;
+  const int nwords = (t + 31) >> 5;
+  for (int i = threadIdx.x; i < nwords; i += 256) member[i] = 0u;
+  __syncthreads();
+  const int n = max(0, min(anchor_count[head], anchor_cap));
+  const int* src = anchor_idx + (size_t)head * anchor_cap;
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int i = src[j];
+    if (i >= 0 && i < t) atomicOr(&member[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  const int* dr = draws + (size_t)head * t;
+  float* row = out + (size_t)head * ld;
+  for (int i = threadIdx.x; i < t; i += 256)
+    row[i] = (member[i >> 5] >> (i & 31)) & 1u ? kMember : -(float)(dr[i] & 0x7FFFFF);
+}
+
 }  // namespace
+
+hipError_t launch_expand_scores(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
+                                const int* anchor_count, const int* draws, float* out,
+                                hipStream_t stream) {
+  const int nheads = d.batch * d.n_q_heads;
+  hipLaunchKernelGGL(expand_scores_kernel, dim3(nheads), dim3(256), 0, stream, anchor_idx,
+                     anchor_cap, anchor_count, draws, d.ctx_len, out, d.scores_ld);
+  return hipGetLastError();
+}
 
 hipError_t launch_gate(const prhs_dims& d, const void* q, void* q_anchor, const int* anchor_count,
                        int force, float sim_tau, int* refresh, float* sim, hipStream_t stream) {

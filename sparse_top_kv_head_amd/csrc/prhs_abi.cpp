@@ -91,6 +91,11 @@ size_t score_ws(const prhs_dims* d) { return score_part_bytes(d); }
 
 size_t decode_ws(const prhs_dims* d, int cap) { return decode_part_bytes(d, cap); }
 
+// Random expansion: one control-score row (scores_ld floats) per head.
+size_t expand_ws(const prhs_dims* d) {
+  return (size_t)d->batch * d->n_q_heads * (size_t)d->scores_ld * sizeof(float);
+}
+
 // Dense decode: split partials over all t keys.
 size_t dense_ws(const prhs_dims* d) { return decode_part_bytes(d, d->ctx_len); }
 
@@ -144,6 +149,7 @@ size_t prhs_workspace_bytes(const prhs_dims* dims, int32_t op, int32_t cap) {
     case PRHS_OP_DECODE: return cap >= 1 ? decode_ws(dims, cap) : 0;
     case PRHS_OP_ANCHOR_STEP: return cap >= 1 ? step_ws(dims, cap) : 0;
     case PRHS_OP_DENSE: return dense_ws(dims);
+    case PRHS_OP_EXPAND: return expand_ws(dims);
     default: return 0;
   }
 }
@@ -313,6 +319,40 @@ int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
                                     sel, dil_idx, dil_cap, dil_count, lse_all, out, lse_sel, delta,
                                     tau, w + L.dec, stream);
   return finish(err, stream, "prhs_adaptive_step");
+}
+
+int prhs_random_expand(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                       const int32_t* anchor_count, const int32_t* draws, int32_t m,
+                       int32_t* out_idx, int32_t out_cap, int32_t* out_count, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->ctx_len > PRHS_MAX_SELECT_CTX)
+    return fail(PRHS_E_DIMS, "selection supports ctx_len <= %d", PRHS_MAX_SELECT_CTX);
+  if (!anchor_idx || !anchor_count || !draws || !out_idx || !out_count)
+    return fail(PRHS_E_NULL, "anchor_idx, anchor_count, draws, out_idx and out_count are required");
+  if (anchor_cap < 1) return fail(PRHS_E_CAPACITY, "anchor_cap must be >= 1");
+  if (m < anchor_cap || m > dims->ctx_len)
+    return fail(PRHS_E_BUDGET, "m %d outside [anchor_cap %d, t %d]", m, anchor_cap, dims->ctx_len);
+  if (out_cap < m) return fail(PRHS_E_CAPACITY, "out_cap %d < m %d", out_cap, m);
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < expand_ws(dims))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", expand_ws(dims), ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  float* cs = static_cast<float*>(ws);
+  hipError_t err = prhs::launch_expand_scores(*dims, anchor_idx, anchor_cap, anchor_count, draws,
+                                              cs, stream);
+  if (err == hipSuccess) {
+    prhs::SelectArgs a;
+    a.scores = cs;
+    a.mode = PRHS_TOPN;
+    a.n_budget = m;
+    a.idx = out_idx;
+    a.idx_cap = out_cap;
+    a.count = out_count;
+    err = prhs::launch_select(*dims, a, stream);
+  }
+  return finish(err, stream, "prhs_random_expand");
 }
 
 int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,

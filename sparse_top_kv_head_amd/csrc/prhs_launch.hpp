@@ -64,6 +64,12 @@ hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                       float sim_tau, int* out_idx, int out_cap, int* out_count, int* reuse_ok,
                       hipStream_t stream, const int* skip = nullptr);
 
+// Control scores of the random expansion: anchor members score high, every
+// other key minus its 23-bit draw (rows of ld floats).
+hipError_t launch_expand_scores(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
+                                const int* anchor_count, const int* draws, float* out,
+                                hipStream_t stream);
+
 // Similarity gate of the adaptive CIS step, per head: refresh = force, or no
 // anchor yet, or cos(q, q_anchor) < sim_tau; a refreshing head's q_anchor
 // becomes q. sim (nullable) receives the cosine (NaN without an anchor).

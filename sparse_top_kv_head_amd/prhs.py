@@ -37,12 +37,13 @@ PRHS_OP_SELECT = 1
 PRHS_OP_DECODE = 2
 PRHS_OP_ANCHOR_STEP = 3
 PRHS_OP_DENSE = 4
+PRHS_OP_EXPAND = 5
 PRHS_MAX_SELECT_CTX = 65536
 
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
     "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step", "prhs_dense_decode",
-    "prhs_workspace_bytes",
+    "prhs_random_expand", "prhs_workspace_bytes",
     "prhs_status_string", "prhs_last_error",
 )
 # measurement aid (include/prhs_probe.h)
@@ -92,6 +93,7 @@ def lib():
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
         L.prhs_dense_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.prhs_random_expand.argtypes = [dp, vp, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]
         L.prhs_adaptive_step.argtypes = [dp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_probe_stream_read.argtypes = [vp, sz, vp, vp]
@@ -104,7 +106,7 @@ def lib():
         L.prhs_last_error.restype = ctypes.c_char_p
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
                      "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode",
-                     "prhs_adaptive_step"):
+                     "prhs_adaptive_step", "prhs_random_expand"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -209,6 +211,15 @@ def prhs_adaptive_step(dims, n_budget, radius, force_refresh, sim_tau, q, k, v, 
                                     dil_cap, _p(dil_count), _p(refresh), _p(sim), _p(out),
                                     _p(lse_sel), _p(delta), _p(tau), _p(theta), _p(ws), ws_bytes,
                                     _stream(stream)))
+
+
+def prhs_random_expand(dims, anchor_idx, anchor_cap, anchor_count, draws, m, out_idx, out_cap,
+                       out_count, ws=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(lib().prhs_random_expand(ctypes.byref(dims), _p(anchor_idx), anchor_cap,
+                                    _p(anchor_count), _p(draws), m, _p(out_idx), out_cap,
+                                    _p(out_count), _p(ws), ws_bytes, _stream(stream)))
 
 
 def prhs_dense_decode(dims, q, k, v, out, lse, ws=None, ws_bytes=None, stream=None):

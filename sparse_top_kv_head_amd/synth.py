@@ -208,3 +208,15 @@ def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
         del kb, vb
     q = torch.as_tensor(qw, dtype=cfg.torch_dtype).to(dev)
     return Workload(cfg, layer, q.contiguous(), K, V, plan)
+
+
+def expansion_draws(batch, n_heads, t, seed, device="cpu", bits=23):
+    """Random integers [batch, n_heads, t] (int32, below 2**bits) for the
+    RandomExpansion control: its random choice is an input, so that every
+    implementation makes the same choice. Seeded torch.Generator on ``device``."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    return torch.randint(0, 1 << bits, (batch, n_heads, t), generator=g, device=dev,
+                         dtype=torch.int32)
+

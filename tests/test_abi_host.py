@@ -103,6 +103,7 @@ def test_bad_dims_rejected_by_every_call(L, field, value, code):
     assert _decode(L, d) == code
     assert _dense(L, d) == code
     assert _adaptive(L, d) == code
+    assert _expand(L, d) == code
     assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, FAKE, None, None) == code
     assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_SCORE, 0) == 0
     assert L.prhs_last_error()
@@ -258,6 +259,30 @@ def test_adaptive_step_argument_checks(L):
     assert _adaptive(L, d, ws=None) == P.PRHS_E_WORKSPACE
     assert _adaptive(L, d, wsb=need - 1) == P.PRHS_E_WORKSPACE
     assert _adaptive(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
+
+
+def _expand(L, d, aidx=FAKE, acap=64, acnt=FAKE, draws=FAKE, m=300, out=FAKE, ocap=300,
+            ocnt=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_random_expand(ctypes.byref(d) if d is not None else None, aidx, acap, acnt,
+                                draws, m, out, ocap, ocnt, ws, wsb, None)
+
+
+def test_random_expand_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_EXPAND, 0)
+    assert need == 2 * 8 * 1000 * 4               # B*H_q*scores_ld floats
+    assert _expand(L, None) == P.PRHS_E_NULL
+    for kw in ("aidx", "acnt", "draws", "out", "ocnt"):
+        assert _expand(L, d, **{kw: None}) == P.PRHS_E_NULL, kw
+    assert _expand(L, d, acap=0) == P.PRHS_E_CAPACITY
+    assert _expand(L, d, m=63) == P.PRHS_E_BUDGET        # below anchor_cap
+    assert _expand(L, d, m=1001, ocap=1001) == P.PRHS_E_BUDGET
+    assert _expand(L, d, ocap=299) == P.PRHS_E_CAPACITY
+    assert _expand(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _expand(L, d, wsb=need - 4) == P.PRHS_E_WORKSPACE
+    assert _expand(L, d, ws=FAKE_MIS) == P.PRHS_E_ALIGN
 
 
 def test_status_strings(L):

@@ -384,6 +384,47 @@ def test_dense_decode(B, Hq, Hkv, d, t, dtype, pad):
             assert abs(lse_ref - lse[b, h]) <= 1e-12
 
 
+# ---------------------------------------------------------------------------
+# prhs_random_expand: the budget-matched random control of dilation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("t,n,m,bits", [(8192, 512, 2139, 23), (1000, 300, 1000, 23),
+                                         (5000, 64, 64, 23), (3000, 200, 900, 3),
+                                         (20000, 512, 2000, 23)])
+def test_random_expand_exact(t, n, m, bits):
+    """Bit-exact against the oracle: anchor sets from a clustered workload and
+    random ones, draws from the seeded generator (bits=3: many equal draws, so
+    the index tie rule decides)."""
+    from sparse_top_kv_head_amd.synth import expansion_draws
+    dev = _dev()
+    H = 6
+    rng = np.random.default_rng(t + n)
+    acap = n
+    aidx = torch.full((1, H, acap), -1, dtype=torch.int32)
+    acnt = torch.zeros((1, H), dtype=torch.int32)
+    sets = []
+    for h in range(H):
+        k = n if h % 3 else max(1, n // 2)        # some heads with fewer anchors
+        S = np.sort(rng.choice(t, k, replace=False))
+        if h == 1:
+            S = np.arange(min(k, t))             # one contiguous run
+        sets.append(S)
+        aidx[0, h, :S.size] = torch.from_numpy(S.astype(np.int32))
+        acnt[0, h] = S.size
+    draws = expansion_draws(1, H, t, seed=7 + t, device=dev, bits=bits)
+    dims = P.PrhsDims(1, H, H, 128, t, P.PRHS_F16, H * t * 128, t * 128, 128, (t + 3) // 4 * 4)
+    out = torch.full((1, H, m), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((1, H), -7, dtype=torch.int32, device=dev)
+    ws = P.alloc_workspace(dims, P.PRHS_OP_EXPAND, device=dev)
+    P.prhs_random_expand(dims, aidx.to(dev), acap, acnt.to(dev), draws, m, out, m, cnt, ws)
+    torch.cuda.synchronize()
+    dr = draws.cpu().numpy()
+    for h in range(H):
+        ref = O.random_expansion(sets[h], dr[0, h], m)
+        assert int(cnt[0, h]) == m
+        assert np.array_equal(out[0, h].cpu().numpy(), ref), h
+
+
 def test_sparse_decode_edge_counts():
     """Empty sets, counts above the capacity, out-of-range indices."""
     dev = _dev()
