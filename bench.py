@@ -21,7 +21,8 @@ query scale) and the toy. ``table4`` compares dense attention with the anchor
 step, the CIS reuse step and amortised CIS-8/16 on LLaMA2-7B-shaped layers at
 the batch sizes and context lengths of the pages' Table IV. ``adaptive_cis``
 sweeps the per-head gated refresh over block size and similarity threshold.
-``cpu_baseline``
+``table6`` compares CIS with its budget-matched DirectReuse and RandomExpansion
+controls (beta_emp, overlap, cost). ``cpu_baseline``
 times the fp64 numpy oracle on a bounded sample of the headline workload.
 """
 
@@ -416,6 +417,91 @@ def bench_adaptive(P, dev, stream, n_steps=32, copies=2):
             "rows": rows}
 
 
+def bench_table6(P, dev, stream, n_steps=16):
+    """The controls of the pages' Table VI (Panel A) on the CIS workload, at one
+    refresh period and a matched processed size m (the mean dilated size):
+    CIS (the top-N anchor set dilated by r), DirectReuse (a top-m anchor set
+    reused unchanged) and RandomExpansion (the top-N anchor set plus random
+    keys up to m, draws from the seeded input generator). On every reuse step,
+    per head: beta_emp = tau(exact top-|S|) - tau(S), with tau(S) from the
+    decode's lse over S against a dense scan, and the overlap of S with the
+    exact top-N of that step. Reuse-step costs are graph-timed per control."""
+    from sparse_top_kv_head_amd.engine import DecodeEngine
+    from sparse_top_kv_head_amd.synth import CONFIGS, expansion_draws, make_workload
+    cfg = CONFIGS["llama2_cis_8k"]
+    N, r, Pd, t = cfg.budget, cfg.radius, cfg.refresh_period, cfg.ctx_len
+    B, H = cfg.batch, cfg.n_q_heads
+    w = make_workload(cfg, device=dev)
+    K, V = w.K, w.V
+    base = DecodeEngine(K, H, N)
+    cis = DecodeEngine(K, H, min(t, (2 * r + 1) * N))
+    base.anchor_step(w.q[0], K, V, P.PRHS_TOPN, N)
+    cis.reuse_step(w.q[1], K, V, base.idx, base.count, N, r)
+    m = int(round(float(cis.count.float().mean())))
+    direct = DecodeEngine(K, H, m)
+    rexp = DecodeEngine(K, H, m)
+    M = min(t, (2 * r + 1) * N)
+    diag = DecodeEngine(K, H, M)
+    draws = expansion_draws(B, H, t, seed=cfg.seed, device=dev)
+    exp_ws = P.alloc_workspace(base.dims, P.PRHS_OP_EXPAND, device=dev)
+
+    def expand():
+        P.prhs_random_expand(base.dims, base.idx, N, base.count, draws, m, rexp.idx, m, rexp.count,
+                             exp_ws)
+
+    stats = {k: {"beta": [], "overlap": [], "size": []} for k in ("CIS", "DirectReuse", "RandomExpansion")}
+    for step in range(n_steps):
+        q = w.q[step]
+        if step % Pd == 0:
+            base.anchor_step(q, K, V, P.PRHS_TOPN, N)
+            direct.anchor_step(q, K, V, P.PRHS_TOPN, m)
+            expand()
+            continue
+        cis.reuse_step(q, K, V, base.idx, base.count, N, r)
+        direct.decode(q, K, V, use_scores=False)
+        rexp.decode(q, K, V, use_scores=False)
+        diag.score(q, K)
+        diag.select(P.PRHS_TOPN, M)
+        lse_all = diag.lse_all.cpu().numpy().astype(np.float64)
+        top_s = diag.sel_scores.cpu().numpy().astype(np.float64)
+        top_i = diag.idx.cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                order = np.argsort(-top_s[b, h], kind="stable")
+                tau_top = np.concatenate([[0.0], np.cumsum(np.exp(top_s[b, h][order] - lse_all[b, h]))])
+                exact_n = top_i[b, h][order[:N]]
+                for name, eng in (("CIS", cis), ("DirectReuse", direct), ("RandomExpansion", rexp)):
+                    n = int(eng.count[b, h])
+                    S = eng.idx[b, h, :n].cpu().numpy()
+                    tau_s = float(np.exp(float(eng.lse_sel[b, h]) - lse_all[b, h]))
+                    st = stats[name]
+                    st["beta"].append(tau_top[min(n, M)] - tau_s)
+                    st["overlap"].append(np.intersect1d(S, exact_n).size / N)
+                    st["size"].append(n)
+    # reuse-step costs (graph-timed): CIS dilates and decodes; the controls decode
+    steps = [w.q[i] for i in range(1, 9)]
+    costs = {}
+    _, g = timed_steps([lambda q=q: cis.reuse_step(q, K, V, base.idx, base.count, N, r) for q in steps], stream)
+    costs["CIS"] = g / len(steps)
+    _, g = timed_steps([lambda q=q: direct.decode(q, K, V, use_scores=False) for q in steps], stream)
+    costs["DirectReuse"] = g / len(steps)
+    _, g = timed_steps([lambda q=q: rexp.decode(q, K, V, use_scores=False) for q in steps], stream)
+    costs["RandomExpansion"] = g / len(steps)
+    _, g = timed_steps([expand for _ in range(8)], stream)
+    expand_ms = g / 8
+    rows = []
+    for name, st in stats.items():
+        rows.append({"control": name, "mean_size": round(float(np.mean(st["size"])), 1),
+                     "beta_emp_mean": round(float(np.mean(st["beta"])), 5),
+                     "overlap_top_n_mean": round(float(np.mean(st["overlap"])), 4),
+                     "reuse_step_ms": round(costs[name], 5)})
+    del w, K, V, base, cis, direct, rexp, diag, draws, exp_ws
+    torch.cuda.empty_cache()
+    return {"workload": "llama2_cis_8k: B=8, 32 MHA heads, t=8192", "budget": N, "radius": r,
+            "refresh_period": Pd, "matched_size_m": m, "reuse_steps_measured": n_steps - len(range(0, n_steps, Pd)),
+            "random_expand_ms": round(expand_ms, 5), "rows": rows}
+
+
 TABLE4_SHAPES = [(8, 2048), (8, 4096), (8, 16384), (16, 2048), (16, 4096), (16, 16384)]
 TABLE4_BUDGET = 256   # the pages do not state it; the largest budget of their Fig. 12 sweep
 TABLE4_RADIUS = 2
@@ -584,6 +670,8 @@ def main():
         res["table4"] = bench_table4(P, dev, stream)
         print("[bench] adaptive CIS sweep", file=sys.stderr, flush=True)
         res["adaptive_cis"] = bench_adaptive(P, dev, stream)
+        print("[bench] table6 controls", file=sys.stderr, flush=True)
+        res["table6"] = bench_table6(P, dev, stream)
     if a.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
