@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_split_kernel(
   static_assert(RW % (U * RPW) == 0 && RW % (UV * RPW) == 0, "chunk tiling");
   static_assert(ROWS == kDenseThreads, "the weights map one row per thread");
 
-  __shared__ float sc[G][ROWS];
+  constexpr int PITCH = ROWS + (RPW > 4 ? RPW : 4);  // distinct banks for the G heads' writes
+  __shared__ float sc[G][PITCH];
   __shared__ float smax[G][NW];
   __shared__ float ssum[G][NW];
   __shared__ __align__(16) float so[G][NW][D];

@@ -41,7 +41,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   static_assert(RW % (U * RPW) == 0, "chunk tiling");
   static_assert(CHUNK == kScoreThreads, "candidate compaction maps one row per thread");
 
-  __shared__ __align__(16) float sc[G][CHUNK];
+  // Each head's staging row is padded by RPW (at least 4) floats, so the
+  // lanes that write one wave-load's RPW rows for G heads hit distinct banks
+  // (and the rows stay 16-byte aligned for the vector read-back).
+  constexpr int PITCH = CHUNK + (RPW > 4 ? RPW : 4);
+  __shared__ __align__(16) float sc[G][PITCH];
   __shared__ uint32_t wcnt[G][NW];
 
   const int chunk = blockIdx.x;

@@ -65,10 +65,15 @@ def stats(statsdir, cmd, out, title):
         fh.write("\n".join(lines) + "\n")
 
 
-def _counter_means(d):
+def _counter_means(d, ours=None):
+    """Counter values per kernel (short name) and counter; `ours` collects the
+    short names of this library's kernels."""
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-        agg[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        k = short_name(r["Kernel_Name"])
+        agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if ours is not None and _ours(r["Kernel_Name"]):
+            ours.add(k)
     return agg
 
 
@@ -104,14 +109,15 @@ def traffic(fetch_dir, write_dir, cmds, out, title):
 
 
 def counters(d, cmd, out, title):
-    agg = _counter_means(d)
+    ours = set()
+    agg = _counter_means(d, ours)
     names = sorted({c for k in agg for c in agg[k]})
     lines = [f"# {title}\n", "Command (repository root, MI355X, one GPU):\n", "```", cmd, "```\n",
              "Mean counter value per dispatch.\n",
              "| kernel | dispatches | " + " | ".join(names) + " |",
              "|---|---|" + "---|" * len(names)]
     for k in sorted(agg):
-        if not _ours(k) and COPY_KERNEL not in k:
+        if k not in ours and COPY_KERNEL not in k:
             continue
         n = max(len(v) for v in agg[k].values())
         vals = [f"{sum(agg[k][c]) / len(agg[k][c]):.4g}" if agg[k].get(c) else "" for c in names]
