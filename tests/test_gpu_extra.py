@@ -1,0 +1,177 @@
+"""More GPU parity: the fused anchor step over shapes (grouped heads in
+sub-groups, ragged contexts, fp32 at d=64, DELTA), graph replay of the gated
+CIS step and of the dense decode, determinism, and the gate's extremes."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prhs_oracle as O
+from sparse_top_kv_head_amd import prhs as P
+from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
+from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+from tests.parity_util import DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()
+    return torch.device("cuda:0")
+
+
+def _np(x):
+    return x.detach().double().cpu().numpy()
+
+
+ANCHOR_CASES = [
+    # B, Hq, Hkv, d, t, dtype, N, mode, delta*
+    (2, 6, 2, 128, 1001, torch.float16, 100, P.PRHS_TOPN, 0.0),     # G = 3, ragged t
+    (1, 4, 4, 64, 777, torch.float32, 50, P.PRHS_TOPN, 0.0),        # fp32, d = 64
+    (1, 8, 1, 128, 5000, torch.float16, 4096, P.PRHS_TOPN, 0.0),    # G = 8, N close to t
+    (2, 4, 2, 64, 3001, torch.float16, 600, P.PRHS_DELTA, 0.2),     # DELTA, d = 64
+    (1, 2, 2, 128, 1, torch.float16, 1, P.PRHS_TOPN, 0.0),          # one key
+    (1, 4, 4, 128, 300, torch.float16, 300, P.PRHS_TOPN, 0.0),      # N = t
+    (1, 4, 1, 128, 9000, torch.float16, 700, P.PRHS_DELTA, 0.05),   # DELTA, scan candidates off
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,t,dtype,N,mode,ds", ANCHOR_CASES)
+def test_anchor_step_shapes(B, Hq, Hkv, d, t, dtype, N, mode, ds):
+    """Two anchor steps (the second with the carried hint) against the oracle."""
+    dev = _dev()
+    g = torch.Generator().manual_seed(B * 1000 + t)
+    K = torch.randn((B, Hkv, t, d), generator=g).to(dtype).to(dev)
+    V = torch.randn((B, Hkv, t, d), generator=g).to(dtype).to(dev)
+    K64, V64 = _np(K), _np(V)
+    eng = DecodeEngine(K, Hq, N)
+    G = Hq // Hkv
+    for step in range(2):
+        q = (torch.randn((B, Hq, d), generator=g) * 2.5).to(dtype).to(dev)
+        eng.anchor_step(q, K, V, mode, N, ds)
+        torch.cuda.synchronize()
+        s_all = O.attention_scores(_np(q), K64)
+        for b in range(B):
+            for h in range(Hq):
+                s = s_all[b, h]
+                _, lse = O.dense_softmax(s)
+                n = int(eng.count[b, h])
+                gidx = eng.idx[b, h, :n].cpu().numpy()
+                assert np.all(np.diff(gidx) > 0) and gidx.min() >= 0 and gidx.max() < t
+                if mode == P.PRHS_TOPN:
+                    assert n == N
+                    exact = check_set_band(gidx, s, N)
+                    S = O.topn_select(s, N) if exact else gidx
+                else:
+                    exact = check_delta_choice(gidx, n, s, float(lse), N, ds,
+                                               cap_hit=int(eng.cap_hit[b, h]))
+                    S = O.topn_select(s, n) if exact else gidx
+                o_ref, _ = O.sparse_attention(s, V64[b, h // G], S)
+                d_ref, _ = O.dropped_mass(s, S)
+                assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL, (step, b, h)
+                assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL
+                assert abs(eng.lse_all[b, h].item() - lse) <= 1e-3
+
+
+def _small_cis(dev, batch=1, heads=8, ctx=4096, steps=8):
+    cfg = CONFIGS["llama2_cis_8k"].replace(batch=batch, n_q_heads=heads, n_kv_heads=heads,
+                                           ctx_len=ctx, budget=256, steps=steps)
+    return cfg, make_workload(cfg, device=dev)
+
+
+def test_adaptive_all_refresh_equals_anchor_steps():
+    """A threshold above 1 refreshes every head at every step: the gated step then
+    gives bit-identical outputs to plain anchor steps."""
+    dev = _dev()
+    cfg, w = _small_cis(dev)
+    ad = AdaptiveEngine(w.K, cfg.n_q_heads, cfg.budget, cfg.radius, 4, 2.0)
+    an = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    for step in range(cfg.steps):
+        ad.step(w.q[step], w.K, w.V)
+        an.anchor_step(w.q[step], w.K, w.V, P.PRHS_TOPN, cfg.budget)
+        torch.cuda.synchronize()
+        assert torch.all(ad.refresh == 1)
+        for name in ("out", "lse_sel", "delta", "tau", "lse_all"):
+            assert torch.equal(getattr(ad, name), getattr(an, name)), (step, name)
+        assert torch.equal(ad.anchor_idx, an.idx) and torch.equal(ad.anchor_count, an.count)
+
+
+def test_adaptive_never_gated_follows_period():
+    """A threshold below -1 never fires: heads refresh exactly on the forced steps,
+    and the shared steps equal the plain CIS reuse step."""
+    dev = _dev()
+    cfg, w = _small_cis(dev)
+    period = 3
+    ad = AdaptiveEngine(w.K, cfg.n_q_heads, cfg.budget, cfg.radius, period, -2.0)
+    anchor = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    reuse = DecodeEngine(w.K, cfg.n_q_heads, ad.dil_cap)
+    for step in range(cfg.steps):
+        ad.step(w.q[step], w.K, w.V)
+        if step % period == 0:
+            anchor.anchor_step(w.q[step], w.K, w.V, P.PRHS_TOPN, cfg.budget)
+        else:
+            reuse.reuse_step(w.q[step], w.K, w.V, anchor.idx, anchor.count, cfg.budget, cfg.radius)
+        torch.cuda.synchronize()
+        assert torch.all(ad.refresh == int(step % period == 0))
+        ref = anchor if step % period == 0 else reuse
+        assert torch.equal(ad.out, ref.out) and torch.equal(ad.lse_sel, ref.lse_sel), step
+        if step % period:
+            assert torch.equal(ad.dil_count, reuse.count)
+
+
+def test_adaptive_graph_replay():
+    """The gated step captured as a HIP graph replays to the eager results, replay
+    after replay, with the state reset and eager work in between."""
+    dev = _dev()
+    cfg, w = _small_cis(dev, batch=2)
+    steps = 6
+
+    def fresh():
+        return AdaptiveEngine(w.K, cfg.n_q_heads, cfg.budget, cfg.radius, 4, 0.97)
+
+    eager = fresh()
+    for step in range(steps):
+        eager.step(w.q[step], w.K, w.V)
+    torch.cuda.synchronize()
+    names = ("out", "lse_sel", "anchor_idx", "anchor_count", "dil_count", "refresh", "anchor_q")
+    ref = {n: getattr(eager, n).clone() for n in names}
+    eng = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for step in range(steps):
+            eng.step(w.q[step], w.K, w.V)
+    other = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    for r in range(3):
+        other.anchor_step(w.q[r], w.K, w.V, P.PRHS_TOPN, cfg.budget)   # eager work in between
+        eng.anchor_count.zero_()
+        eng.anchor_q.zero_()
+        eng.theta.fill_(float("nan"))
+        eng.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(eng, n), ref[n]), (r, n)
+
+
+def test_dense_decode_deterministic_and_graph():
+    dev = _dev()
+    cfg, w = _small_cis(dev, batch=2, ctx=5000)
+    eng = DecodeEngine(w.K, cfg.n_q_heads, 1, dense=True)
+    eng.dense_step(w.q[0], w.K, w.V)
+    torch.cuda.synchronize()
+    out, lse = eng.out.clone(), eng.lse_all.clone()
+    eng.dense_step(w.q[0], w.K, w.V)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eng.out) and torch.equal(lse, eng.lse_all)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eng.dense_step(w.q[0], w.K, w.V)
+    for _ in range(3):
+        eng.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eng.out)
