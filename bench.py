@@ -247,6 +247,25 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
     is_a = np.array([i % Pd == 0 for i in range(n_steps)])
     a_ms, r_ms = per[is_a], per[~is_a]
     mean_bytes = (a_bytes * is_a.sum() + r_bytes * (~is_a).sum()) / n_steps
+    # Untimed diagnostics at the reuse steps, with the library's own calls: delta
+    # of the reused (dilated) set against a dense scan of that step, and delta
+    # of the exact top-N of the same step (the oracle's set), plus their overlap.
+    diag = DecodeEngine(w.K, cfg.n_q_heads, N)
+    d_reuse, d_exact, ov = [], [], []
+    delta_r = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    for i in range(n_steps):
+        q, K, V = w.q[i % cfg.steps], Ks[i % copies], Vs[i % copies]
+        if i % Pd == 0:
+            anchor.anchor_step(q, K, V, P.PRHS_TOPN, N)
+            continue
+        reuse.reuse_step(q, K, V, anchor.idx, anchor.count, N, r)
+        diag.anchor_step(q, K, V, P.PRHS_TOPN, N)
+        P.prhs_dropped_mass(diag.dims, reuse.lse_sel, diag.lse_all, delta_r)
+        d_reuse.append(float(delta_r.mean()))
+        d_exact.append(float(diag.delta.mean()))
+        dil, dc, ex = reuse.idx.cpu().numpy(), reuse.count.cpu().numpy(), diag.idx.cpu().numpy()
+        ov.append(np.mean([np.intersect1d(dil[b, h, :dc[b, h]], ex[b, h, :N]).size / N
+                           for b in range(cfg.batch) for h in range(cfg.n_q_heads)]))
     res = _summary(cfg, per, gms, n_steps, mean_bytes, {
         "kv_copies_rotated": copies, "budget": N, "radius": r, "refresh_period": Pd,
         "anchor": {"ms_p10_p50_p90": pct(a_ms), "hbm_alg_bytes": int(a_bytes),
@@ -254,9 +273,13 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
         "reuse": {"ms_p10_p50_p90": pct(r_ms), "hbm_alg_bytes": int(r_bytes),
                   "hbm_alg_gbs_p50": round(r_bytes / (np.median(r_ms) / 1e3) / 1e9, 1),
                   "mean_dilated_rows_per_head": round(float(reuse.count.float().mean()), 1),
-                  "heads_steps_per_s_p50": round(heads / (np.median(r_ms) / 1e3), 1)},
+                  "heads_steps_per_s_p50": round(heads / (np.median(r_ms) / 1e3), 1),
+                  "delta_reused_set_mean": round(float(np.mean(d_reuse)), 5),
+                  "delta_oracle_topn_mean": round(float(np.mean(d_exact)), 5),
+                  "tau_reused_set_mean": round(1.0 - float(np.mean(d_reuse)), 5),
+                  "overlap_with_oracle_topn_mean": round(float(np.mean(ov)), 4)},
         "note": "step time is the amortised mean over anchor and reuse steps"})
-    del w, Ks, Vs, anchor, reuse
+    del w, Ks, Vs, anchor, reuse, diag
     torch.cuda.empty_cache()
     return res
 
