@@ -3,27 +3,37 @@
 // N; the top-k oracle of Fig. 1, Fig. 2 and Fig. 9; the Abstract's control of
 // the dropped mass delta before attention).
 //
-// One 1024-thread workgroup per (b, h). The head's t scores are held in
-// registers as order-preserving 32-bit keys: each wave owns a contiguous
-// range of 64*KPT keys, loaded with coalesced 16-byte loads, lane l holding
-// granules of 4 consecutive keys at stride 256.
+// One 1024-thread workgroup per (b, h), working on order-preserving 32-bit
+// keys of the fp32 scores (-0 folded onto +0).
 //
-// TOPN: a 1-in-8 sample of the keys is histogrammed on its top 11 bits to
-// pick a threshold theta that at least N keys clear with a wide margin. The
-// keys >= theta (a few thousand) are compacted with their indices into an LDS
-// list, and the exact N-th largest key T is found by a radix search over that
-// list with 12-bit digits of key - theta (two passes for a typical range). One
-// wave locates the boundary bin of each pass while the others wait at the
-// barrier. If the sample misleads (fewer than N keys clear theta, or too many
-// for the list), a full radix search over the register keys runs instead:
-// 11 + 11 + 10-bit passes, the first adding into kRep1 copies of the
-// histogram (lane l into copy l % kRep1) because most keys land in a few
-// crowded bins, the later ones over the boundary bin's keys compacted to LDS.
+// TOPN, steady state: the score scan already wrote, per 256-key chunk, the
+// keys at or above a per-head threshold carried from the previous anchor step,
+// in index order. Their counts give each chunk its offset (one workgroup
+// scan); the candidates are gathered into an LDS list, still in index order,
+// and a radix search with 12-bit digits of key - min over that list finds the
+// exact N-th largest key T (two passes for a typical range; one wave locates
+// each boundary bin while the others wait). The selection is written in list
+// order, with each row's score, and a threshold for the next step. When the
+// carried threshold leaves fewer than N or more than kCandCap keys, the full
+// path below runs; the result is exact either way.
+//
+// Full path: the head's keys are loaded into registers (wave w owns a
+// contiguous range of 64*KPT keys, 16-byte loads, lane l holding granules of
+// 4 consecutive keys at stride 256). A 1-in-8 sample is histogrammed on its
+// top 11 bits to pick a threshold theta that at least N keys clear with a
+// wide margin; the keys >= theta (a few thousand) are compacted with their
+// indices into the LDS list and the same 12-bit radix search finds T. If the
+// sample misleads, an 11 + 11 + 10-bit radix search streams the (L2-resident)
+// score row instead of holding keys in registers, the first pass adding into
+// kRep1 copies of the histogram because most keys land in a few crowded bins,
+// the later ones over the boundary bin's keys compacted to LDS. Only candidate
+// building holds keys in registers, so no path spills.
 //
 // The result is every key above T plus the lowest-index keys equal to T. The
 // keys are marked in two LDS bitmaps (above T, equal to T) indexed by key
-// position; one workgroup scan over the bitmap words then gives each thread
-// its output offset, and the indices are written in ascending order.
+// position; one workgroup scan over the bitmap words gives each word its final
+// selection and output offset, and the indices and scores are scattered from
+// the LDS list (or the streamed row) in ascending index order.
 //
 // DELTA mode first finds the cap-th largest key Tc as above and sums the
 // dense weights exp(s - lse) of the keys outside the top-cap set, in 2^-40
@@ -42,7 +52,7 @@ namespace {
 
 constexpr int kBins = 2048;
 constexpr int kRep1 = 4;                 // copies of the first-pass count histogram
-constexpr int kCandCap = 8192;           // boundary-bin keys kept in LDS
+constexpr int kCandCap = 8192;           // LDS candidate list capacity (keys and indices)
 constexpr int kMaxWords = PRHS_MAX_SELECT_CTX / 32;
 constexpr double kMassScale = 1099511627776.0;  // 2^40
 
@@ -90,8 +100,8 @@ struct SelShared {
   uint32_t wtot2[NT / kWave];
   unsigned long long wmass[NT / kWave];
   float lse;                      // dense log-sum-exp merged from the scan partials
-  uint32_t ncand;                 // fast-path list length
-  uint32_t ncand_r;               // register-path list length
+  uint32_t ncand;                 // candidate list length (keys and indices)
+  uint32_t ncand_r;               // boundary-bin list length of the streamed searches (keys only)
   uint32_t kmax;
   uint32_t kmin;
   uint32_t digit;
