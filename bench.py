@@ -637,6 +637,8 @@ def main():
     rows = distinct_rows(eng.idx, eng.count, cfg.group)
     cnt = eng.count.cpu().numpy()
     step_bytes = scan_bytes + rows * d * eb
+    # the literal upper count: K scan plus K and V rows per query head, no dedup
+    lit_bytes = scan_bytes + int(cnt.sum()) * 2 * d * eb
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
     traffic_bytes = scan_traffic_bytes()
     traffic = None if traffic_bytes is None else round(traffic_bytes / (scan_ms / 1e3) / 1e9, 1)
@@ -663,6 +665,8 @@ def main():
                      "algorithmic_bytes_per_launch": scan_bytes,
                      "mean_launch_ms": round(scan_ms, 5)},
         "step": {"hbm_alg_bytes": int(step_bytes), "hbm_alg_gbs": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
+                 "hbm_lit_bytes": int(lit_bytes),
+                 "hbm_lit_gbs": round(lit_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
                  "frac_of_peak": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                  "eager_step_ms_p10_p50_p90": pct(per_ms),
                  "eager_ms_per_step": round(float(per_ms.mean()), 5),

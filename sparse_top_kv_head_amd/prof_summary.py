@@ -1,14 +1,14 @@
 """Summarise rocprofv3 CSV output into the short Markdown files kept under profiles/.
 
     python -m sparse_top_kv_head_amd.prof_summary stats <dir> "<command>" <out.md> "<title>"
-    python -m sparse_top_kv_head_amd.prof_summary traffic <fetch_dir> <write_dir> "<cmd1>||<cmd2>" <out.md> "<title>"
+    python -m sparse_top_kv_head_amd.prof_summary traffic <fetch_dir> <write_dir> "<cmd1>||<cmd2>" <out.md> "<title>" [--no-scan-line]
     python -m sparse_top_kv_head_amd.prof_summary counters <dir> "<command>" <out.md> "<title>"
 
 ``stats`` reads ``run_kernel_stats.csv`` of a ``--kernel-trace --stats`` run.
 ``traffic`` reads the ``run_counter_collection.csv`` of one FETCH_SIZE and one
 WRITE_SIZE run of ``bench.py --calibrate-copy`` and scales each counter by what
-it reads for the plain 256 MiB device copy of that run (bytes moved per KiB
-counted), giving HBM bytes per dispatch. The scan kernel's figure is written
+it reads for the plain 256 MiB device copies of that run (the last three copy
+dispatches; bytes moved per KiB counted), giving HBM bytes per dispatch. The scan kernel's figure is written
 with a hash of its sources, so that ``bench.py`` uses it only while the kernel
 is unchanged. ``counters`` tabulates every counter of a ``--pmc`` run per kernel
 (mean over dispatches).
@@ -77,33 +77,45 @@ def _counter_means(d, ours=None):
     return agg
 
 
-def traffic(fetch_dir, write_dir, cmds, out, title):
-    f = _counter_means(fetch_dir)
+def _calibration_copy(d, counter, n=3):
+    """Mean counter value of the calibration copies: the last n copy dispatches of
+    the run (bench.py --calibrate-copy issues them after all other GPU work)."""
+    rows = [r for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv")))
+            if short_name(r["Kernel_Name"]) == COPY_KERNEL and r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    last = rows[-n:]
+    return sum(float(r["Counter_Value"]) for r in last) / len(last)
+
+
+def traffic(fetch_dir, write_dir, cmds, out, title, scan_line=True):
+    ours = set()
+    f = _counter_means(fetch_dir, ours)
     w = _counter_means(write_dir)
-    copy_f = max(f[COPY_KERNEL]["FETCH_SIZE"])
-    copy_w = max(w[COPY_KERNEL]["WRITE_SIZE"])
+    copy_f = _calibration_copy(fetch_dir, "FETCH_SIZE")
+    copy_w = _calibration_copy(write_dir, "WRITE_SIZE")
     ff, fw = CALIBRATION_KIB / copy_f, CALIBRATION_KIB / copy_w
     lines = [f"# {title}\n", "Commands (repository root, MI355X, one GPU; each counter in its own run):\n",
              "```"] + cmds + ["```\n",
              f"Calibration: a plain device copy of 256 MiB (`--calibrate-copy`, torch `copy_`, dispatched as "
              f"`{COPY_KERNEL}`) reads FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB per "
              f"dispatch, so the scale factors to bytes moved are fetch x{ff:.4f}, write x{fw:.4f}.\n",
-             f"Scan kernel sources hash (sha256 of {', '.join(SCAN_SOURCES)}, first 16 hex): "
-             f"`{source_hash()}`\n",
+             (f"Scan kernel sources hash (sha256 of {', '.join(SCAN_SOURCES)}, first 16 hex): "
+              f"`{source_hash()}`\n" if scan_line else ""),
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled fetch MiB | scaled write MiB |",
              "|---|---|---|---|---|---|"]
     per = {}
     for k in sorted(f):
-        if not any(s in k for s in ("score_scan", "select", "decode", "lse_merge", "cis_dilate")):
+        if k not in ours:
             continue
         fv = f[k]["FETCH_SIZE"]
         wv = w.get(k, {}).get("WRITE_SIZE", [0.0])
         fm, wm = sum(fv) / len(fv), sum(wv) / len(wv)
         lines.append(f"| `{k[:70]}` | {len(fv)} | {fm:.1f} | {wm:.1f} | {fm * ff / 1024:.2f} | {wm * fw / 1024:.2f} |")
         per[k] = fm * ff * 1024 + wm * fw * 1024
-    scan = [k for k in per if "score_scan" in k][0]
-    lines.append(f"\nscan_traffic_bytes_per_launch: {per[scan]:.0f}")
-    lines.append(f"scan_source_hash: {source_hash()}")
+    if scan_line:
+        scan = [k for k in per if "score_scan" in k][0]
+        lines.append(f"\nscan_traffic_bytes_per_launch: {per[scan]:.0f}")
+        lines.append(f"scan_source_hash: {source_hash()}")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -131,7 +143,8 @@ if __name__ == "__main__":
     if what == "stats":
         stats(*sys.argv[2:6])
     elif what == "traffic":
-        traffic(sys.argv[2], sys.argv[3], sys.argv[4].split("||"), sys.argv[5], sys.argv[6])
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4].split("||"), sys.argv[5], sys.argv[6],
+                scan_line=not (len(sys.argv) > 7 and sys.argv[7] == "--no-scan-line"))
     elif what == "counters":
         counters(*sys.argv[2:6])
     else:
