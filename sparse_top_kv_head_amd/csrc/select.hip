@@ -626,7 +626,8 @@ __device__ __forceinline__ bool build_candidates(const Keys<KPT>& K, int t, uint
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   uint32_t theta = 0;
-  if (t > kCandCap) {
+  // sample whenever the list would otherwise hold far more keys than needed
+  if (t > kCandCap || (SR > 1 && (uint32_t)t >= 8u * N)) {
     if (threadIdx.x == 0) {
       sh.digit = 0;
       sh.ncand = 0;
