@@ -112,6 +112,9 @@ SELECT_CASES = [
     ("normal", 3, 1), ("normal", 3, 2), ("normal", 5, 7), ("normal", 4, 1000), ("normal", 2, 1025),
     ("normal", 2, 4097), ("normal", 2, 32768), ("normal", 1, 65536), ("ties", 3, 5000),
     ("flat", 2, 3000), ("signed_zero", 2, 777), ("neg_inf", 2, 2049), ("wide", 2, 16384),
+    # sampled threshold and its streamed fallback at larger t
+    ("flat", 2, 16384), ("ties", 2, 8192), ("neg_inf", 2, 32768), ("wide", 1, 65536),
+    ("signed_zero", 2, 20000),
 ]
 
 
