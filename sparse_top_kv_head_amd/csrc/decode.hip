@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   constexpr int LPR = D / E;
   constexpr int RPW = kWave / LPR;
   constexpr int RW = ROWS / NW;                    // rows per wave
-  constexpr int U = RW / RPW < 16 ? RW / RPW : 16;  // loads in flight per lane
+  constexpr int U = RW / RPW < 8 ? RW / RPW : 8;  // loads in flight per lane
   constexpr int IT = RW / (U * RPW);
   static_assert(RW % (U * RPW) == 0, "split tiling");
 

@@ -407,6 +407,9 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     cd.cand = reinterpret_cast<uint2*>(w + L.cand);
     cd.cand_cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
   }
+  // With enough heads (or a one-split budget) each head's select workgroup
+  // also decodes its head: no split partials and no merge launch.
+  const bool fuse = prhs::fuse_decode(*dims, mode, n_budget);
   hipError_t err = prhs::launch_score(*dims, q, k, scores, nullptr, part, stream, &cd);
   if (err == hipSuccess) {
     prhs::SelectArgs a;
@@ -420,13 +423,25 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     a.idx_cap = idx_cap;
     a.count = count;
     a.cap_hit = cap_hit;
-    a.sel_scores = sel;
+    a.sel_scores = fuse ? nullptr : sel;
     a.cand = cd.cand;
     a.cand_cnt = cd.cand_cnt;
     a.theta_out = hint ? theta : nullptr;
+    if (fuse) {
+      a.v = v;
+      a.kv_sb = dims->kv_stride_b;
+      a.kv_sh = dims->kv_stride_h;
+      a.kv_st = dims->kv_stride_t;
+      a.hq = dims->n_q_heads;
+      a.hkv = dims->n_kv_heads;
+      a.out = out;
+      a.lse_sel = lse_sel;
+      a.delta = delta;
+      a.tau = tau;
+    }
     err = prhs::launch_select(*dims, a, stream);
   }
-  if (err == hipSuccess)
+  if (err == hipSuccess && !fuse)
     err = prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel, nullptr, lse_all, out,
                               lse_sel, delta, tau, w + L.dec, stream);
   return finish(err, stream, "prhs_anchor_step");

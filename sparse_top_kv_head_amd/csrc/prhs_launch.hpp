@@ -52,12 +52,32 @@ struct SelectArgs {
   const uint32_t* cand_cnt = nullptr;
   float* theta_out = nullptr;     // next-step threshold hint (TOPN)
   const int* active = nullptr;    // per head; inactive heads are left untouched
+  // Fused decode (TOPN with scan partials, fp16 rows of 128): when v is given,
+  // each head's workgroup attends over its own selection and writes out,
+  // lse_sel and, when delta is given, delta (and tau).
+  const void* v = nullptr;
+  long long kv_sb = 0, kv_sh = 0, kv_st = 0;  // element strides of V
+  int hq = 0, hkv = 0;
+  float* out = nullptr;
+  float* lse_sel = nullptr;
+  float* delta = nullptr;
+  float* tau = nullptr;
   int t = 0;
   int ld = 0;
   int nchunks = 0;
 };
 
 hipError_t launch_select(const prhs_dims& d, const SelectArgs& a, hipStream_t stream);
+
+// Largest budget the fused select-and-decode takes, and the fewest heads for
+// which it beats the split decode (one workgroup per head must still cover
+// about half of the 256 CUs; budgets of one split never need more).
+constexpr int kFuseRows = 2048;
+constexpr int kFuseMinHeads = 128;
+inline bool fuse_decode(const prhs_dims& d, int mode, int n_budget) {
+  return mode == PRHS_TOPN && d.dtype == PRHS_F16 && d.head_dim == 128 && n_budget <= kFuseRows &&
+         (d.batch * d.n_q_heads >= kFuseMinHeads || n_budget <= kDecodeRows);
+}
 
 hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                       const int* anchor_count, int radius, const void* q_cur, const void* q_anchor,

@@ -484,18 +484,24 @@ __device__ __forceinline__ int out_slot(uint32_t i, const SelShared<NT, MASS>& s
   return (int)(sh.eq_bits[i >> 5] + __popc(m & ((1u << bit) - 1u)));
 }
 
+// Write one selected entry to its slot, and to the LDS mirror of the fused
+// decode (index, score bits) when there is one.
+__device__ __forceinline__ void put_sel(int* __restrict__ out, float* __restrict__ out_s,
+                                        uint2* mirror, uint32_t pos, uint32_t i, float s) {
+  out[pos] = (int)i;
+  if (out_s) out_s[pos] = s;
+  if (mirror != nullptr && pos < (uint32_t)kFuseRows) mirror[pos] = make_uint2(i, __float_as_uint(s));
+}
+
 // Write the selected entries of the LDS list (key, index) to their slots.
 template <int NT, bool MASS>
 __device__ __forceinline__ void scatter_list(uint32_t C, int* __restrict__ out,
                                              float* __restrict__ out_s, uint32_t cap,
-                                             const SelShared<NT, MASS>& sh) {
+                                             const SelShared<NT, MASS>& sh, uint2* mirror) {
   for (int c = threadIdx.x; c < (int)C; c += NT) {
     const uint2 ki = sh.cand[c];
     const int pos = out_slot<NT, MASS>(ki.y, sh);
-    if (pos >= 0 && (uint32_t)pos < cap) {
-      out[pos] = (int)ki.y;
-      if (out_s) out_s[pos] = key_to_score(ki.x);
-    }
+    if (pos >= 0 && (uint32_t)pos < cap) put_sel(out, out_s, mirror, pos, ki.y, key_to_score(ki.x));
   }
 }
 
@@ -503,13 +509,12 @@ __device__ __forceinline__ void scatter_list(uint32_t C, int* __restrict__ out,
 template <int NT, bool MASS>
 __device__ __forceinline__ void scatter_row(const float* __restrict__ row, int t,
                                             int* __restrict__ out, float* __restrict__ out_s,
-                                            uint32_t cap, const SelShared<NT, MASS>& sh) {
+                                            uint32_t cap, const SelShared<NT, MASS>& sh,
+                                            uint2* mirror) {
   for (int i = threadIdx.x; i < t; i += NT) {
     const int pos = out_slot<NT, MASS>((uint32_t)i, sh);
-    if (pos >= 0 && (uint32_t)pos < cap) {
-      out[pos] = i;
-      if (out_s) out_s[pos] = key_to_score(score_key(row[i]));
-    }
+    if (pos >= 0 && (uint32_t)pos < cap)
+      put_sel(out, out_s, mirror, pos, (uint32_t)i, key_to_score(score_key(row[i])));
   }
 }
 
@@ -712,7 +717,7 @@ __device__ __forceinline__ void mark_from_list(uint32_t C, uint32_t T, SelShared
 template <int NT, bool MASS>
 __device__ __forceinline__ void emit_list(uint32_t C, uint32_t T, uint32_t take_eq,
                                           int* __restrict__ out, float* __restrict__ out_s,
-                                          uint32_t cap, SelShared<NT, MASS>& sh) {
+                                          uint32_t cap, SelShared<NT, MASS>& sh, uint2* mirror) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -750,10 +755,7 @@ __device__ __forceinline__ void emit_list(uint32_t C, uint32_t T, uint32_t take_
       --eq_left;
     }
     if (sel) {
-      if (pos < cap) {
-        out[pos] = (int)ki.y;
-        if (out_s) out_s[pos] = key_to_score(ki.x);
-      }
+      if (pos < cap) put_sel(out, out_s, mirror, pos, ki.y, key_to_score(ki.x));
       ++pos;
     }
   }
@@ -888,15 +890,100 @@ template <int NT, bool MASS>
 __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const float* row,
                                             int* out, float* out_s, bool list, uint32_t C,
                                             uint32_t T, uint32_t take, int n_sel, int hit,
-                                            SelShared<NT, MASS>& sh) {
+                                            SelShared<NT, MASS>& sh, uint2* mirror) {
   const uint32_t cap = (uint32_t)a.idx_cap;
   emit_offsets<NT, MASS>(a.t, take, sh);
-  if (list) scatter_list<NT, MASS>(C, out, out_s, cap, sh);
-  else scatter_row<NT, MASS>(row, a.t, out, out_s, cap, sh);
+  if (list) scatter_list<NT, MASS>(C, out, out_s, cap, sh, mirror);
+  else scatter_row<NT, MASS>(row, a.t, out, out_s, cap, sh, mirror);
   if (threadIdx.x == 0) {
     a.count[head] = n_sel;
     if (a.cap_hit) a.cap_hit[head] = hit;
     if (!MASS && a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+  }
+}
+
+// Fused decode: attention of one head over its own selection, read from the
+// LDS mirror (index, score) that the emission filled in index order. Wave w
+// gathers the fp16 V rows (128 wide, 16 lanes of 16 bytes per row) of a
+// contiguous share of the selection, kFuseLoads rows in flight per lane, and
+// weighs them by exp(s - m). m is the head's top score, which is always
+// selected, so the waves share one maximum and their partials add without
+// rescaling. Finishes like the split decode's merge: out, lse_sel, and the
+// dropped mass from the dense log-sum-exp lse_all.
+constexpr int kFuseLoads = 8;
+template <int NT, bool MASS>
+__device__ __forceinline__ void fused_decode(const SelectArgs& a, int head, int n, uint32_t kmax,
+                                             float lse_all, SelShared<NT, MASS>& sh) {
+  constexpr int D = 128, LPR = 16, RPW = kWave / LPR, U = kFuseLoads, NW = NT / kWave;
+  static_assert(2 * kFuseRows + NW * (D + 1) <= kBins * kRep1, "fused decode overlays the histogram");
+  const uint2* sel = reinterpret_cast<const uint2*>(sh.hist);
+  float* so = reinterpret_cast<float*>(sh.hist) + 2 * kFuseRows;  // [NW][D] wave partials
+  float* sl = so + NW * D;                                        // [NW] wave weight sums
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int c = lane % LPR, rr = lane / LPR;
+  const int b = head / a.hq;
+  const int g = (head - b * a.hq) / (a.hq / a.hkv);
+  const char* vbase = static_cast<const char*>(a.v) +
+                      ((size_t)b * a.kv_sb + (size_t)g * a.kv_sh) * sizeof(__half) + c * 16;
+  const size_t row_bytes = (size_t)a.kv_st * sizeof(__half);
+  const float m = key_to_score(kmax);
+  const bool none = m == -INFINITY;
+  const int rw = ((n + NW - 1) / NW + RPW - 1) / RPW * RPW;
+  const int rb = w * rw;
+  const int re = min(n, rb + rw);
+  __syncthreads();  // the mirror is complete
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float l = 0.f;
+  for (int r0 = rb; r0 < re; r0 += U * RPW) {
+    uint4 x[U];
+    float p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * RPW + rr;
+      const uint2 e = r < re ? sel[r] : make_uint2(0u, 0u);
+      const bool ok = r < re && e.x < (uint32_t)a.t;  // every mirrored index is < t
+      x[u] = ok ? load16(vbase + (size_t)e.x * row_bytes) : make_uint4(0u, 0u, 0u, 0u);
+      p[u] = ok && !none ? __expf(__uint_as_float(e.y) - m) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      axpy16(p[u], x[u], acc, __half());
+      if (c == 0) l += p[u];
+    }
+  }
+  // the RPW row slots of the wave (lanes c, c + LPR, ...) hold one column block
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  }
+  l = wave_sum(l);
+  if (rr == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) so[w * D + c * 8 + e] = acc[e];
+  }
+  if (lane == 0) sl[w] = l;
+  __syncthreads();
+  if ((int)threadIdx.x < D) {
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      o += so[k * D + threadIdx.x];
+      L += sl[k];
+    }
+    a.out[(size_t)head * D + threadIdx.x] = L > 0.f ? o / L : 0.f;
+    if (threadIdx.x == 0) {
+      const float lse = L > 0.f ? m + __logf(L) : -INFINITY;
+      a.lse_sel[head] = lse;
+      if (a.delta != nullptr) {
+        const float dlt = fminf(fmaxf(-expm1f(lse - lse_all), 0.f), 1.f);
+        a.delta[head] = dlt;
+        if (a.tau != nullptr) a.tau[head] = 1.f - dlt;
+      }
+    }
   }
 }
 
@@ -905,10 +992,15 @@ __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const
 // (max, sum) partials of the score scan are merged here, the result used and
 // written to lse_all. TOPN with scan candidates (cand != NULL) selects from
 // them when they hold the answer and otherwise falls back to the full path.
-template <int KPT, int NT, int MODE>
+// FUSE (TOPN only): the workgroup then decodes its head (fused_decode).
+template <int KPT, int NT, int MODE, bool FUSE>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr bool MASS = MODE == PRHS_DELTA;
+  static_assert(!(FUSE && MASS), "the fused decode follows a top-N selection");
   __shared__ SelShared<NT, MASS> sh;
+  // LDS mirror of the selection for the fused decode; the histogram is free
+  // once the emission starts
+  uint2* const mirror = FUSE ? reinterpret_cast<uint2*>(sh.hist) : nullptr;
 
   const int head = blockIdx.x;
   if (a.active != nullptr && a.active[head] == 0) return;
@@ -954,12 +1046,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         gather_candidates<NT, MASS>(a.cand, ccount, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
       uint32_t T, take;
       cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
-      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh);
+      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh, mirror);
       if (threadIdx.x == 0) {
         a.count[head] = a.n_budget;
         if (a.cap_hit) a.cap_hit[head] = 0;
         if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
       }
+      if constexpr (FUSE) fused_decode<NT, MASS>(a, head, a.n_budget, sh.kmax, sh.lse, sh);
       return;
     }
   }
@@ -1019,16 +1112,17 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
   if (list) mark_from_list<NT, MASS>(C, T, sh);
   else mark_row<NT, MASS>(row, t, T, sh);
-  finish_head<NT, MASS>(a, head, row, out, out_s, list, C, T, take, n_sel, hit, sh);
+  finish_head<NT, MASS>(a, head, row, out, out_s, list, C, T, take, n_sel, hit, sh, mirror);
+  if constexpr (FUSE) fused_decode<NT, MASS>(a, head, n_sel, sh.kmax, sh.lse, sh);
 }
 
 constexpr int kSelThreads = 1024;
 
-template <int MODE>
+template <int MODE, bool FUSE>
 void launch_mode(int kpt, int nheads, const SelectArgs& a, hipStream_t stream) {
-#define PRHS_SEL(K)                                                                          \
-  hipLaunchKernelGGL((select_kernel<K, kSelThreads, MODE>), dim3(nheads), dim3(kSelThreads), 0, \
-                     stream, a)
+#define PRHS_SEL(K)                                                                    \
+  hipLaunchKernelGGL((select_kernel<K, kSelThreads, MODE, FUSE>), dim3(nheads),          \
+                     dim3(kSelThreads), 0, stream, a)
   switch (kpt) {
     case 1: PRHS_SEL(1); break;
     case 2: PRHS_SEL(2); break;
@@ -1051,8 +1145,9 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t
   a.t = d.ctx_len;
   a.ld = d.scores_ld;
   a.nchunks = score_nchunks(d);
-  if (a.mode == PRHS_DELTA) launch_mode<PRHS_DELTA>(kpt, nheads, a, stream);
-  else launch_mode<PRHS_TOPN>(kpt, nheads, a, stream);
+  if (a.mode == PRHS_DELTA) launch_mode<PRHS_DELTA, false>(kpt, nheads, a, stream);
+  else if (a.v != nullptr) launch_mode<PRHS_TOPN, true>(kpt, nheads, a, stream);
+  else launch_mode<PRHS_TOPN, false>(kpt, nheads, a, stream);
   return hipGetLastError();
 }
 

@@ -13,6 +13,12 @@ Tolerances:
 * Index sets: equal except for keys whose oracle score lies within 1e-4 of
   the N-th oracle score; sparse outputs within 2e-3 max-abs; delta within
   1e-4 absolute (the stated acceptance rules of the method's hot path).
+* Two decodes of one selection that add in a different order (the fused
+  select-and-decode against the split decode and its merge): each fp32 sum
+  of n non-negative-weighted terms lies within (n - 1)u of the exact sum, and
+  the two paths' exponentials (exp(s - m) against exp(s - m_split) *
+  exp(m_split - m)) differ by a few u. So the outputs differ by at most
+  (4(n - 1) + 8) u max|v|, and lse_sel (hence delta) by (2(n - 1) + 8) u.
 """
 
 import math
@@ -25,6 +31,19 @@ U32 = 2.0 ** -24
 SET_BAND = 1e-4
 OUT_TOL = 2e-3
 DELTA_TOL = 1e-4
+
+
+def reorder_tols(n, vmax):
+    """(output, lse) tolerances between two summation orders of n weighted rows."""
+    return (4 * (n - 1) + 8) * U32 * max(float(vmax), 1.0), (2 * (n - 1) + 8) * U32
+
+
+def fused_anchor_decode(dtype_f16, head_dim, n_heads, mode_topn, n_budget):
+    """Whether the anchor step decodes inside the select kernel (the library's
+    rule: top-N, fp16 rows of 128, N <= 2048, and >= 128 heads or a
+    one-split budget of <= 256)."""
+    return (mode_topn and dtype_f16 and head_dim == 128 and n_budget <= 2048
+            and (n_heads >= 128 or n_budget <= 256))
 
 
 def score_bound(q, K):

@@ -10,7 +10,8 @@ from oracle import prhs_oracle as O
 from sparse_top_kv_head_amd import prhs as P
 from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
 from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-from tests.parity_util import DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band
+from tests.parity_util import (DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band,
+                               fused_anchor_decode, reorder_tols)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,26 +76,99 @@ def test_anchor_step_shapes(B, Hq, Hkv, d, t, dtype, N, mode, ds):
                 assert abs(eng.lse_all[b, h].item() - lse) <= 1e-3
 
 
+FUSED_CASES = [
+    # kind, B, Hq, Hkv, t, N: every case decodes inside the select kernel
+    ("random", 2, 64, 8, 5003, 1000),    # 128 heads, ragged t
+    ("random", 1, 128, 32, 2048, 2048),  # N = t: every key
+    ("flat", 1, 128, 16, 10000, 2048),   # equal scores, t past the LDS list: streamed emission
+    ("ties", 2, 64, 16, 3000, 700),      # few distinct scores: boundary ties
+    ("random", 1, 8, 2, 2000, 256),      # one-split budget on few heads
+    ("random", 1, 128, 32, 1500, 1),     # N = 1
+]
+
+
+def _fused_inputs(kind, B, Hq, Hkv, t, g):
+    d = 128
+    if kind == "flat":
+        K = torch.randn((B, Hkv, 1, d), generator=g).expand(B, Hkv, t, d).contiguous()
+        q = torch.randn((B, Hq, d), generator=g)
+    elif kind == "ties":
+        K = torch.randint(-1, 2, (B, Hkv, t, d), generator=g).float()
+        q = torch.randint(-1, 2, (B, Hq, d), generator=g).float()
+    else:
+        K = torch.randn((B, Hkv, t, d), generator=g)
+        q = torch.randn((B, Hq, d), generator=g) * 2.5
+    V = torch.randn((B, Hkv, t, d), generator=g) * 3.0
+    return q.half(), K.half(), V.half()
+
+
+@pytest.mark.parametrize("kind,B,Hq,Hkv,t,N", FUSED_CASES)
+def test_fused_select_decode(kind, B, Hq, Hkv, t, N):
+    """Anchor steps that decode inside the select kernel, through each emission
+    (scan candidates with the carried hint, the sampled list, the streamed
+    row), against the oracle: the exact top-N, the attention output and delta."""
+    assert fused_anchor_decode(True, 128, B * Hq, True, N)
+    dev = _dev()
+    g = torch.Generator().manual_seed(7 * t + N)
+    q, K, V = _fused_inputs(kind, B, Hq, Hkv, t, g)
+    K, V = K.to(dev), V.to(dev)
+    K64, V64 = _np(K), _np(V)
+    eng = DecodeEngine(K, Hq, N)
+    G = Hq // Hkv
+    for step in range(2):
+        qs = (q if step == 0 else q.roll(1, dims=1)).to(dev)
+        eng.anchor_step(qs, K, V, P.PRHS_TOPN, N)
+        torch.cuda.synchronize()
+        s_all = O.attention_scores(_np(qs), K64)
+        for b in range(B):
+            for h in range(Hq):
+                s = s_all[b, h]
+                assert int(eng.count[b, h]) == N
+                gidx = eng.idx[b, h, :N].cpu().numpy()
+                assert np.all(np.diff(gidx) > 0) and gidx.min() >= 0 and gidx.max() < t
+                S = O.topn_select(s, N) if check_set_band(gidx, s, N) else gidx
+                o_ref, lse_ref = O.sparse_attention(s, V64[b, h // G], S)
+                d_ref, _ = O.dropped_mass(s, S)
+                assert np.max(np.abs(_np(eng.out[b, h]) - o_ref)) <= OUT_TOL, (step, b, h)
+                assert abs(eng.lse_sel[b, h].item() - lse_ref) <= 1e-3, (step, b, h)
+                assert abs(eng.delta[b, h].item() - d_ref) <= DELTA_TOL, (step, b, h)
+                assert abs(eng.tau[b, h].item() - (1.0 - d_ref)) <= DELTA_TOL
+
+
 def _small_cis(dev, batch=1, heads=8, ctx=4096, steps=8):
     cfg = CONFIGS["llama2_cis_8k"].replace(batch=batch, n_q_heads=heads, n_kv_heads=heads,
                                            ctx_len=ctx, budget=256, steps=steps)
     return cfg, make_workload(cfg, device=dev)
 
 
+def _same_decode(a, b, n, vmax, names=("out", "lse_sel", "delta", "tau")):
+    """Outputs of one selection decoded by two paths: bit-equal when both split
+    and merge, else equal up to summation order."""
+    fused = fused_anchor_decode(True, a.out.shape[-1], a.out.shape[0] * a.out.shape[1], True, n)
+    otol, ltol = reorder_tols(n, vmax) if fused else (0.0, 0.0)
+    for name in names:
+        x, y = getattr(a, name), getattr(b, name)
+        tol = otol if name == "out" else ltol
+        assert (x - y).abs().max().item() <= tol, name
+
+
 def test_adaptive_all_refresh_equals_anchor_steps():
     """A threshold above 1 refreshes every head at every step: the gated step then
-    gives bit-identical outputs to plain anchor steps."""
+    selects exactly what plain anchor steps select, and decodes to the same
+    outputs (bit-equal, or up to summation order where the anchor step decodes
+    inside its select kernel)."""
     dev = _dev()
     cfg, w = _small_cis(dev)
     ad = AdaptiveEngine(w.K, cfg.n_q_heads, cfg.budget, cfg.radius, 4, 2.0)
     an = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    vmax = w.V.abs().max().item()
     for step in range(cfg.steps):
         ad.step(w.q[step], w.K, w.V)
         an.anchor_step(w.q[step], w.K, w.V, P.PRHS_TOPN, cfg.budget)
         torch.cuda.synchronize()
         assert torch.all(ad.refresh == 1)
-        for name in ("out", "lse_sel", "delta", "tau", "lse_all"):
-            assert torch.equal(getattr(ad, name), getattr(an, name)), (step, name)
+        assert torch.equal(ad.lse_all, an.lse_all), step
+        _same_decode(ad, an, cfg.budget, vmax)
         assert torch.equal(ad.anchor_idx, an.idx) and torch.equal(ad.anchor_count, an.count)
 
 
@@ -115,8 +189,10 @@ def test_adaptive_never_gated_follows_period():
             reuse.reuse_step(w.q[step], w.K, w.V, anchor.idx, anchor.count, cfg.budget, cfg.radius)
         torch.cuda.synchronize()
         assert torch.all(ad.refresh == int(step % period == 0))
-        ref = anchor if step % period == 0 else reuse
-        assert torch.equal(ad.out, ref.out) and torch.equal(ad.lse_sel, ref.lse_sel), step
+        if step % period == 0:
+            _same_decode(ad, anchor, cfg.budget, w.V.abs().max().item(), ("out", "lse_sel"))
+        else:
+            assert torch.equal(ad.out, reuse.out) and torch.equal(ad.lse_sel, reuse.lse_sel), step
         if step % period:
             assert torch.equal(ad.dil_count, reuse.count)
 

@@ -16,6 +16,7 @@ from oracle import prhs_oracle as O
 from sparse_top_kv_head_amd import prhs as P
 from sparse_top_kv_head_amd.engine import DecodeEngine
 from tests.parity_util import (DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band,
+                               fused_anchor_decode, reorder_tols,
                                score_bound)
 
 pytestmark = pytest.mark.gpu
@@ -484,11 +485,20 @@ def test_engine_topn_step_small():
 # prhs_anchor_step: one call, same results as the three calls in sequence.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("mode", [P.PRHS_TOPN, P.PRHS_DELTA])
-def test_anchor_step_matches_separate_calls(mode):
+@pytest.mark.parametrize("mode,budget,heads", [
+    (P.PRHS_TOPN, 256, 8),     # one-split budget: decoded inside the select kernel
+    (P.PRHS_TOPN, 512, 8),     # split decode and merge
+    (P.PRHS_TOPN, 512, 128),   # 128 heads: fused again
+    (P.PRHS_DELTA, 256, 8),
+])
+def test_anchor_step_matches_separate_calls(mode, budget, heads):
+    """The one-call step selects exactly what the separate calls select; its
+    outputs are bit-equal when it decodes the same way (split and merge) and
+    equal up to summation order when the select kernel decodes too."""
     dev = _dev()
     from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-    cfg = CONFIGS["llama2_4k"].replace(steps=2, n_q_heads=8, n_kv_heads=2)
+    cfg = CONFIGS["llama2_4k"].replace(steps=2, n_q_heads=heads, n_kv_heads=heads // 4,
+                                       budget=budget)
     w = make_workload(cfg, device=dev)
     a = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
     b = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
@@ -505,8 +515,15 @@ def test_anchor_step_matches_separate_calls(mode):
     for h in range(cfg.n_q_heads):
         n = int(a.count[0, h])
         assert torch.equal(a.idx[0, h, :n], b.idx[0, h, :n])
-    for name in ("out", "lse_sel", "delta", "tau"):
-        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    fused = fused_anchor_decode(True, cfg.head_dim, heads, mode == P.PRHS_TOPN, budget)
+    if fused:
+        otol, ltol = reorder_tols(budget, w.V.abs().max().item())
+        assert (a.out - b.out).abs().max().item() <= otol
+        for name in ("lse_sel", "delta", "tau"):
+            assert (getattr(a, name) - getattr(b, name)).abs().max().item() <= ltol, name
+    else:
+        for name in ("out", "lse_sel", "delta", "tau"):
+            assert torch.equal(getattr(a, name), getattr(b, name)), name
     if mode == P.PRHS_DELTA:
         assert torch.equal(a.cap_hit, b.cap_hit)
 
