@@ -95,7 +95,6 @@ struct SelShared {
   uint2 cand[kCandCap + kWave];   // (key, index) of the fast path; key only otherwise; + dummies
   uint32_t gt_bits[kMaxWords];
   uint32_t eq_bits[kMaxWords];
-  uint32_t coff[kMaxWords / 8 + 1];   // candidate-chunk offsets (t / 256 chunks)
   uint32_t wtot[NT / kWave];
   uint32_t wtot2[NT / kWave];
   unsigned long long wmass[NT / kWave];
@@ -107,6 +106,8 @@ struct SelShared {
   uint32_t digit;
   uint32_t above;
   uint32_t cT;
+  uint32_t rT;                    // boundary key and its take from a ranked boundary bin
+  uint32_t rTake;
   int found;
   unsigned long long below;
   unsigned long long mT;
@@ -591,30 +592,64 @@ __device__ __forceinline__ void find_count_w0(uint32_t krem, SelShared<NT, MASS>
 }
 
 // Exact N-th largest key among the C candidate keys in sh.cand[].x, all of
-// them in [lo, hi]: radix passes with 12-bit digits of key - lo. Returns the
-// boundary key T and take_eq, the number of keys equal to T that are taken.
+// them in [lo, hi]: radix passes with 10-bit digits of key - lo until the
+// boundary bin holds at most 64 keys (or no digits are left). Those keys are
+// then compacted past the list and ranked by one wave, lane against lane.
+// Returns the boundary key T and take_eq, the number of keys equal to T that
+// are taken.
 template <int NT, bool MASS>
 __device__ __forceinline__ void cand_radix(uint32_t lo, uint32_t hi, uint32_t C, uint32_t N,
                                            uint32_t& T, uint32_t& take_eq,
                                            SelShared<NT, MASS>& sh) {
+  constexpr int DB = 10, NB = 1 << DB;
   const uint32_t range = hi - lo;
-  int shift = range ? 32 - __builtin_clz(range) - 12 : 0;
+  int shift = range ? 32 - __builtin_clz(range) - DB : 0;
   shift = shift > 0 ? shift : 0;
   uint32_t pre = 0, pmask = 0, krem = N;
 #pragma unroll 1
   while (true) {
-    if (threadIdx.x == 0) sh.digit = 0;
+    if (threadIdx.x == 0) sh.ncand_r = 0;
     for (int c = threadIdx.x; c < (int)C; c += NT) {
       const uint32_t o = sh.cand[c].x - lo;
-      if ((o & pmask) == pre) atomicAdd(&sh.hist[swz_slot<4096, 1>((o >> shift) & 4095u, 0)], 1u);
+      if ((o & pmask) == pre)
+        atomicAdd(&sh.hist[swz_slot<NB, 1>((o >> shift) & (uint32_t)(NB - 1), 0)], 1u);
     }
     __syncthreads();
-    find_count_w0<4096, 1, NT, MASS>(krem, sh);
+    // 1 <= krem <= the keys counted, so the find always sets digit / above / cT
+    find_count_w0<NB, 1, NT, MASS>(krem, sh);
     krem -= sh.above;
     pre |= sh.digit << shift;
-    pmask |= 4095u << shift;
+    pmask |= (uint32_t)(NB - 1) << shift;
     if (shift == 0) break;
-    shift = shift > 12 ? shift - 12 : 0;
+    if (sh.cT <= (uint32_t)kWave) {
+      // the boundary bin's keys, ranked directly
+      for (int c = threadIdx.x; c < (int)C; c += NT) {
+        const uint32_t key = sh.cand[c].x;
+        if (((key - lo) & pmask) == pre) sh.cand[kCandCap + atomicAdd(&sh.ncand_r, 1u)].x = key;
+      }
+      __syncthreads();
+      if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int n = (int)sh.cT;
+        const uint32_t x = lane < n ? sh.cand[kCandCap + lane].x : 0u;
+        uint32_t gt = 0, eq = 0;
+        for (int j = 0; j < n; ++j) {
+          const uint32_t y = lane_read(x, j);
+          gt += y > x;
+          eq += y == x;
+        }
+        // lanes holding the same key write the same values
+        if (lane < n && gt < krem && krem <= gt + eq) {
+          sh.rT = x;
+          sh.rTake = krem - gt;
+        }
+      }
+      __syncthreads();
+      T = sh.rT;
+      take_eq = sh.rTake;
+      return;
+    }
+    shift = shift > DB ? shift - DB : 0;
   }
   T = lo + pre;
   take_eq = krem;
@@ -761,52 +796,93 @@ __device__ __forceinline__ void emit_list(uint32_t C, uint32_t T, uint32_t take_
   }
 }
 
-// Gather the head's scan candidates (chunk by chunk, so in index order) into
-// sh.cand as (key, index). Returns false, with nothing written, when a chunk
-// carries no candidates or the total is outside [N, kCandCap].
-// `c` is this thread's chunk count (thread i holds chunk i's, loaded by the
-// caller ahead of other work; 0 past the last chunk).
+// Candidate chunks per wave: wave w owns chunks [w * cpw, (w + 1) * cpw) and
+// lane l < cpw loads the count of chunk w * cpw + l at kernel start.
+template <int NT>
+__device__ __forceinline__ int cand_cpw(int nch) {
+  return (nch + NT / kWave - 1) / (NT / kWave);
+}
+
+// Compact the scan's candidates of one head (keys >= its threshold hint, per
+// chunk in index order) into sh.cand in index order, with their keys, and set
+// sh.kmax / sh.kmin. `c` is this lane's chunk count (see cand_cpw). Each wave
+// requests the first entries of its own chunks as soon as its counts are in,
+// without waiting for the other waves: kSlots loads per lane cover R = 64-lane
+// rows of every chunk (R = kSlots / cpw, at most the chunk's 4 rows); rows past
+// that are fetched afterwards. The workgroup offsets are formed while those
+// loads are in flight. Returns false (nothing written) when a chunk has no
+// candidate list or the total is below N or above the LDS list capacity.
+constexpr int kSlots = 16;
 template <int NT, bool MASS>
 __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand, uint32_t c,
                                                   int head, int nch, uint32_t N, uint32_t& C,
                                                   SelShared<NT, MASS>& sh) {
+  constexpr int NW = NT / kWave;
+  static_assert((PRHS_MAX_SELECT_CTX / kScoreChunk + NW - 1) / NW <= kSlots, "chunks per wave");
   const int lane = threadIdx.x & (kWave - 1);
-  if (__syncthreads_or(c == kNoCand)) return false;
-  uint32_t total;
-  const uint32_t ex = block_exclusive_scan<NT>(c, sh.wtot, total);
-  if ((int)threadIdx.x < nch) sh.coff[threadIdx.x] = ex;
+  const int w = threadIdx.x / kWave;
+  const int cpw = cand_cpw<NT>(nch);
+  int rows = 1;  // 64-entry rows requested per chunk in the first round
+  while (rows < 4 && rows * 2 * cpw <= kSlots) rows *= 2;
+  const bool bad = __ballot(c == kNoCand) != 0ull;
+  const uint32_t cc = c == kNoCand ? 0u : c;
+  const uint32_t inc = wave_scan_u32(cc);
+  const uint32_t ex = inc - cc;
+  // the wave's chunks start at a wave-uniform address: one scalar base, and a
+  // 32-bit lane offset per load
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint2* src = cand + ((size_t)head * nch + (size_t)wu * cpw) * kScoreChunk;
+  uint2 e[kSlots];
+#pragma unroll
+  for (int sl = 0; sl < kSlots; ++sl) {
+    const int k = sl / rows, r = sl - k * rows;
+    e[sl] = make_uint2(0u, 0u);
+    if (k < cpw) {
+      const uint32_t j = (uint32_t)(lane + r * kWave);
+      if (j < lane_read(cc, k)) e[sl] = src[(uint32_t)k * kScoreChunk + j];
+    }
+  }
+  if (lane == kWave - 1) {
+    sh.wtot[w] = inc;
+    sh.wtot2[w] = bad ? 1u : 0u;
+  }
+  __syncthreads();
+  uint32_t base = 0, total = 0, anybad = 0;
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    const uint32_t v = sh.wtot[u];
+    if (u < w) base += v;
+    total += v;
+    anybad |= sh.wtot2[u];
+  }
   if (threadIdx.x == 0) {
-    sh.coff[nch] = total;
     sh.kmax = 0;
     sh.kmin = 0xFFFFFFFFu;
   }
-  __syncthreads();
+  __syncthreads();  // every wave has read wtot; kmax / kmin are reset
   C = total;
-  if (C < N || C > (uint32_t)kCandCap) return false;
-  // all of a thread's loads are issued before any is used
-  constexpr int PER = (kCandCap + NT - 1) / NT;
-  uint2 e[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const uint32_t p = threadIdx.x + (uint32_t)j * NT;
-    e[j] = make_uint2(0, 0);
-    if (p < C) {
-      int a = 0, b = nch - 1;  // last chunk whose offset <= p
-      while (a < b) {
-        const int mid = (a + b + 1) >> 1;
-        if (sh.coff[mid] <= p) a = mid;
-        else b = mid - 1;
-      }
-      e[j] = cand[((size_t)head * nch + a) * kScoreChunk + (p - sh.coff[a])];
-    }
-  }
+  if (anybad || C < N || C > (uint32_t)kCandCap) return false;
   uint32_t kmx = 0, kmn = 0xFFFFFFFFu;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const uint32_t p = threadIdx.x + (uint32_t)j * NT;
-    if (p < C) {
-      const uint32_t key = score_key(__uint_as_float(e[j].x));
-      sh.cand[p] = make_uint2(key, e[j].y);
+  for (int sl = 0; sl < kSlots; ++sl) {
+    const int k = sl / rows, r = sl - k * rows;
+    if (k < cpw) {
+      const uint32_t j = (uint32_t)(lane + r * kWave);
+      if (j < lane_read(cc, k)) {
+        const uint32_t key = score_key(__uint_as_float(e[sl].x));
+        sh.cand[base + lane_read(ex, k) + j] = make_uint2(key, e[sl].y);
+        kmx = key > kmx ? key : kmx;
+        kmn = key < kmn ? key : kmn;
+      }
+    }
+  }
+  // rows past the first round (chunks holding more than rows * 64 candidates)
+  for (int k = 0; k < cpw; ++k) {
+    const uint32_t n = lane_read(cc, k);
+    for (uint32_t j = (uint32_t)(lane + rows * kWave); j < n; j += kWave) {
+      const uint2 x = src[(size_t)k * kScoreChunk + j];
+      const uint32_t key = score_key(__uint_as_float(x.x));
+      sh.cand[base + lane_read(ex, k) + j] = make_uint2(key, x.y);
       kmx = key > kmx ? key : kmx;
       kmn = key < kmn ? key : kmn;
     }
@@ -1013,10 +1089,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const bool from_scan = !MASS && a.cand != nullptr;
   Keys<KPT> K;
   if (!from_scan) load_keys_raw<KPT>(K, row, t);
-  // the chunk counts of the scan's candidates, in flight under the partial merge
-  const uint32_t ccount = from_scan && (int)threadIdx.x < a.nchunks
-                              ? a.cand_cnt[(size_t)head * a.nchunks + threadIdx.x]
-                              : 0u;
+  // the chunk counts of the scan's candidates (lane l of wave w: chunk
+  // w * cpw + l), in flight under the partial merge
+  uint32_t ccount = 0u;
+  if (from_scan) {
+    const int cpw = cand_cpw<NT>(a.nchunks);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ch = (int)(threadIdx.x / kWave) * cpw + lane;
+    if (lane < cpw && ch < a.nchunks) ccount = a.cand_cnt[(size_t)head * a.nchunks + ch];
+  }
   if (a.part != nullptr && threadIdx.x < kWave) {
     float m = -INFINITY, l = 0.f;
     for (int c = threadIdx.x; c < a.nchunks; c += kWave) {
@@ -1041,23 +1122,28 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 
   if constexpr (!MASS) {
-    uint32_t C = 0;
-    if (from_scan &&
-        gather_candidates<NT, MASS>(a.cand, ccount, head, a.nchunks, (uint32_t)a.n_budget, C, sh)) {
-      uint32_t T, take;
-      cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
-      emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh, mirror);
-      if (threadIdx.x == 0) {
-        a.count[head] = a.n_budget;
-        if (a.cap_hit) a.cap_hit[head] = 0;
-        if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+    if (from_scan) {
+      uint32_t C = 0;
+      if (gather_candidates<NT, MASS>(a.cand, ccount, head, a.nchunks, (uint32_t)a.n_budget, C,
+                                      sh)) {
+        uint32_t T, take;
+        cand_radix<NT, MASS>(sh.kmin, sh.kmax, C, (uint32_t)a.n_budget, T, take, sh);
+        emit_list<NT, MASS>(C, T, take, out, out_s, (uint32_t)a.idx_cap, sh, mirror);
+        if (threadIdx.x == 0) {
+          a.count[head] = a.n_budget;
+          if (a.cap_hit) a.cap_hit[head] = 0;
+          if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+        }
+        if constexpr (FUSE) fused_decode<NT, MASS>(a, head, a.n_budget, sh.kmax, sh.lse, sh);
+        return;
       }
-      if constexpr (FUSE) fused_decode<NT, MASS>(a, head, a.n_budget, sh.kmax, sh.lse, sh);
-      return;
+      // the candidates do not hold the answer: the full path, on keys loaded
+      // now (inside this branch, so that the keys of the other branch are not
+      // live across the gather)
+      load_keys_raw<KPT>(K, row, t);
     }
   }
 
-  if (from_scan) load_keys_raw<KPT>(K, row, t);
   finish_keys<KPT>(K);
   __syncthreads();
 
