@@ -259,6 +259,168 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
                 lse_all, delta, tau, mix, head);
 }
 
+// The whole decode of one head in one 1024-thread workgroup, used when the
+// heads alone fill the chip (or a set fits one split): no partials and no
+// merge launch. The index list is staged in LDS first. Wave w takes a
+// contiguous share of the head's rows: it forms their scores (given, gathered
+// from the score row, or computed from gathered K rows, kHeadLoads rows in
+// flight per lane) into LDS, then at once gathers their V rows and weighs them
+// by exp(s - m_w) with its own maximum m_w, so no barrier separates the two
+// phases. The 16 wave partials are then rescaled to the head's maximum and
+// added, as the online softmax merges. Sources, index checks and outputs are
+// those of the split kernel and its merge.
+constexpr int kHeadThreads = 1024;
+constexpr int kHeadLoads = 8;
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int* __restrict__ idx, int idx_cap, const int* __restrict__ count,
+    const float* __restrict__ sel_scores, const float* __restrict__ scores,
+    const int* __restrict__ idx2, int idx2_cap, const int* __restrict__ count2,
+    const int* __restrict__ mix, int Hq, int Hkv, int t, long long sb, long long sh,
+    long long st, int ld, float scale, float* __restrict__ out, float* __restrict__ lse_sel,
+    const float* __restrict__ lse_all, float* __restrict__ delta, float* __restrict__ tau) {
+  constexpr int NW = kHeadThreads / kWave;
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  constexpr int RPW = kWave / LPR;
+  constexpr int U = kHeadLoads;
+  __shared__ int sidx[kDecodeHeadRows];
+  __shared__ float sp[kDecodeHeadRows];
+  __shared__ float sm[NW];
+  __shared__ float sl[NW];
+  __shared__ __align__(16) float so[NW][D];
+
+  const int head = blockIdx.x;
+  const int b = head / Hq;
+  const int g = (head - b * Hq) / (Hq / Hkv);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int c = lane % LPR;
+  const int rr = lane / LPR;
+
+  const bool has_scores = MODE == kModeScores || (MODE == kModeMixed && mix[head] != 0);
+  const bool first = has_scores || MODE == kModeGather;
+  const int* ih = first ? idx : idx2;
+  const int icap = first ? idx_cap : idx2_cap;
+  const int* ch = first ? count : count2;
+  const int n = max(0, min(ch[head], icap));
+  const int* irow = ih + (size_t)head * icap;
+  const int rw = ((n + NW - 1) / NW + RPW - 1) / RPW * RPW;
+  const int rb = w * rw;
+  const int re = min(n, rb + rw);
+  const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
+  const size_t row_bytes = (size_t)st * sizeof(T);
+
+  // the index list in LDS (indices outside [0, t) become -1), then the
+  // scores of the wave's rows
+  for (int r = threadIdx.x; r < n; r += kHeadThreads) {
+    const int id = irow[r];
+    sidx[r] = id >= 0 && id < t ? id : -1;
+  }
+  __syncthreads();
+  float mw = -INFINITY;
+  if (has_scores) {
+    for (int r = rb + lane; r < re; r += kWave) {
+      const int id = sidx[r];
+      const float sv = id < 0 ? -INFINITY
+                              : sel_scores ? sel_scores[(size_t)head * idx_cap + r]
+                                           : scores[(size_t)head * ld + id];
+      sp[r] = sv;
+      mw = fmaxf(mw, sv);
+    }
+  } else {
+    const uint4 qv = load16(q + (size_t)head * D + c * E);
+    const char* kbase = reinterpret_cast<const char*>(k + kv_off) + c * 16;
+    for (int r0 = rb; r0 < re; r0 += U * RPW) {
+      uint4 kv[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RPW + rr;
+        const int id = r < re ? sidx[r] : -1;
+        ok[u] = id >= 0;
+        kv[u] = ok[u] ? load16(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u * RPW + rr;
+        const float sv = ok[u] ? group_sum<LPR>(dot16(kv[u], qv, 0.f, T())) * scale : -INFINITY;
+        if (c == 0 && r < re) sp[r] = sv;
+        mw = fmaxf(mw, sv);
+      }
+    }
+  }
+  const float m = wave_max(mw);
+  // the wave reads back rows that other lanes of the same wave scored
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+  // weighted V rows against the wave's own maximum (rows with a skipped index
+  // carry -inf, so weight 0)
+  const char* vbase = reinterpret_cast<const char*>(v + kv_off) + c * 16;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float l = 0.f;
+  for (int r0 = rb; r0 < re; r0 += U * RPW) {
+    uint4 vv[U];
+    float p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * RPW + rr;
+      const float sv = r < re ? sp[r] : -INFINITY;
+      const bool ok = sv != -INFINITY;
+      const int id = ok ? sidx[r] : 0;
+      vv[u] = ok ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+      p[u] = ok ? __expf(sv - m) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      axpy16(p[u], vv[u], acc, T());
+      if (c == 0) l += p[u];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o);
+  }
+  l = wave_sum(l);
+  if (rr == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) so[w][c * E + e] = acc[e];
+  }
+  if (lane == 0) {
+    sm[w] = m;
+    sl[w] = l;
+  }
+  __syncthreads();
+  // the wave partials, rescaled to the head's maximum
+  if ((int)threadIdx.x < D) {
+    float mh = sm[0];
+#pragma unroll
+    for (int k2 = 1; k2 < NW; ++k2) mh = fmaxf(mh, sm[k2]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < NW; ++k2) {
+      const float f = sm[k2] == -INFINITY ? 0.f : __expf(sm[k2] - mh);
+      o += so[k2][threadIdx.x] * f;
+      L += sl[k2] * f;
+    }
+    out[(size_t)head * D + threadIdx.x] = L > 0.f ? o / L : 0.f;
+    if (threadIdx.x == 0) {
+      const float lse = L > 0.f ? mh + __logf(L) : -INFINITY;
+      lse_sel[head] = lse;
+      if (lse_all != nullptr && delta != nullptr && (mix == nullptr || mix[head] != 0)) {
+        const float dlt = fminf(fmaxf(-expm1f(lse - lse_all[head]), 0.f), 1.f);
+        delta[head] = dlt;
+        if (tau != nullptr) tau[head] = 1.f - dlt;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void dropped_mass_kernel(const float* __restrict__ lse_sel,
                                                            const float* __restrict__ lse_all,
                                                            float* __restrict__ delta,
@@ -298,6 +460,41 @@ void launch_split_mode(const prhs_dims& d, const SplitArgs& a, float* part, int 
                      d.scores_ld, scale, part, nsplit);
 }
 
+template <typename T, int D, int MODE>
+void launch_head_mode(const prhs_dims& d, const SplitArgs& a, float* out, float* lse_sel,
+                      const float* lse_all, float* delta, float* tau, hipStream_t stream) {
+  const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
+  hipLaunchKernelGGL((decode_head_kernel<T, D, MODE>), dim3(d.batch * d.n_q_heads),
+                     dim3(kHeadThreads), 0, stream, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.idx, a.idx_cap,
+                     a.count, a.sel_scores, a.scores, a.idx2, a.idx2_cap, a.count2, a.mix,
+                     d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
+                     (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale, out,
+                     lse_sel, lse_all, delta, tau);
+}
+
+template <typename T, int D>
+void launch_head(const prhs_dims& d, const SplitArgs& a, float* out, float* lse_sel,
+                 const float* lse_all, float* delta, float* tau, hipStream_t stream) {
+  if (a.mix != nullptr)
+    launch_head_mode<T, D, kModeMixed>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+  else if (a.scores || a.sel_scores)
+    launch_head_mode<T, D, kModeScores>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+  else
+    launch_head_mode<T, D, kModeGather>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+}
+
+void launch_head_any(const prhs_dims& d, const SplitArgs& a, float* out, float* lse_sel,
+                     const float* lse_all, float* delta, float* tau, hipStream_t stream) {
+  if (d.dtype == PRHS_F16) {
+    if (d.head_dim == 128) launch_head<__half, 128>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+    else launch_head<__half, 64>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+  } else {
+    if (d.head_dim == 128) launch_head<float, 128>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+    else launch_head<float, 64>(d, a, out, lse_sel, lse_all, delta, tau, stream);
+  }
+}
+
 template <typename T, int D>
 void launch_split(const prhs_dims& d, const SplitArgs& a, float* part, int nsplit,
                   hipStream_t stream) {
@@ -323,9 +520,13 @@ hipError_t launch_decode(const prhs_dims& d, const void* q, const void* k, const
                          const int* idx, int idx_cap, const int* count, const float* sel_scores,
                          const float* scores, const float* lse_all, float* out, float* lse_sel,
                          float* delta, float* tau, void* ws, hipStream_t stream) {
+  const SplitArgs a{q, k, v, idx, idx_cap, count, sel_scores, scores, nullptr, 0, nullptr, nullptr};
+  if (decode_per_head(d, idx_cap)) {
+    launch_head_any(d, a, out, lse_sel, lse_all, delta, tau, stream);
+    return hipGetLastError();
+  }
   const int nsplit = decode_nsplit(idx_cap);
   float* part = static_cast<float*>(ws);
-  const SplitArgs a{q, k, v, idx, idx_cap, count, sel_scores, scores, nullptr, 0, nullptr, nullptr};
   launch_split_any(d, a, part, nsplit, stream);
   return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream);
 }
@@ -336,9 +537,14 @@ hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k,
                                const int* count2, const float* lse_all, float* out,
                                float* lse_sel, float* delta, float* tau, void* ws,
                                hipStream_t stream) {
-  const int nsplit = decode_nsplit(idx_cap > idx2_cap ? idx_cap : idx2_cap);
-  float* part = static_cast<float*>(ws);
+  const int cap = idx_cap > idx2_cap ? idx_cap : idx2_cap;
   const SplitArgs a{q, k, v, idx, idx_cap, count, sel_scores, nullptr, idx2, idx2_cap, count2, mix};
+  if (decode_per_head(d, cap)) {
+    launch_head_any(d, a, out, lse_sel, lse_all, delta, tau, stream);
+    return hipGetLastError();
+  }
+  const int nsplit = decode_nsplit(cap);
+  float* part = static_cast<float*>(ws);
   launch_split_any(d, a, part, nsplit, stream);
   return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream, mix);
 }

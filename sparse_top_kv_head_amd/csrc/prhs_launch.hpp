@@ -14,6 +14,13 @@ constexpr int kDecodeRows = 256;
 
 inline int score_nchunks(const prhs_dims& d) { return (d.ctx_len + kScoreChunk - 1) / kScoreChunk; }
 inline int decode_nsplit(int cap) { return (cap + kDecodeRows - 1) / kDecodeRows; }
+// Rows the one-workgroup-per-head decode holds (their scores in LDS), and
+// whether a decode runs that way: the heads alone fill about half of the 256
+// CUs, or the set fits one split anyway.
+constexpr int kDecodeHeadRows = 8192;
+inline bool decode_per_head(const prhs_dims& d, int cap) {
+  return cap <= kDecodeHeadRows && (d.batch * d.n_q_heads >= 128 || cap <= kDecodeRows);
+}
 
 // Count marking a (head, chunk) for which no candidates were written.
 constexpr uint32_t kNoCand = 0xFFFFFFFFu;

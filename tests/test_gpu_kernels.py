@@ -291,6 +291,12 @@ DECODE_CASES = [
     (2, 8, 1, 64, 1537, torch.float16, 1537),
     (1, 4, 4, 128, 4096, torch.float16, 1),
     (1, 8, 4, 128, 9000, torch.float16, 2048),
+    # >= 128 heads: one workgroup per head, no merge
+    (2, 64, 8, 128, 5000, torch.float16, 2048),
+    (1, 128, 32, 64, 3001, torch.float16, 700),
+    (1, 128, 16, 128, 2000, torch.float32, 500),
+    (4, 32, 8, 128, 9000, torch.float16, 8000),    # capacity 8003, near the per-head limit
+    (1, 128, 16, 128, 9000, torch.float16, 8190),  # capacity 8193: past it, split and merge
 ]
 
 
@@ -429,18 +435,21 @@ def test_random_expand_exact(t, n, m, bits):
         assert np.array_equal(out[0, h].cpu().numpy(), ref), h
 
 
-def test_sparse_decode_edge_counts():
-    """Empty sets, counts above the capacity, out-of-range indices."""
+@pytest.mark.parametrize("H,cap", [(4, 300), (4, 256), (128, 300)])
+def test_sparse_decode_edge_counts(H, cap):
+    """Empty sets, counts above the capacity, out-of-range indices; split and
+    merge (4 heads, 300 rows) and one workgroup per head (a one-split
+    capacity, or 128 heads)."""
     dev = _dev()
-    B, H, d, t = 1, 4, 128, 600
+    B, d, t = 1, 128, 600
     K = _kv(B, H, t, d, torch.float16, 31)
     V = _kv(B, H, t, d, torch.float16, 32)
     q = torch.randn((B, H, d), generator=torch.Generator().manual_seed(33)).half().to(dev)
-    cap = 300
     idx = torch.arange(cap, dtype=torch.int32).repeat(B, H, 1)
     idx[0, 2, 5] = -3        # skipped
     idx[0, 2, 6] = t + 10    # skipped
-    cnt = torch.tensor([[0, 1000, 10, cap]], dtype=torch.int32)   # empty, clamped, with bad ids, full
+    cnt = torch.full((B, H), cap, dtype=torch.int32)
+    cnt[0, :4] = torch.tensor([0, 1000, 10, cap], dtype=torch.int32)   # empty, clamped, bad ids, full
     dims = P.make_dims(K, H)
     out = torch.empty((B, H, d), device=dev)
     lse_sel = torch.empty((B, H), device=dev)
