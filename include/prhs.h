@@ -179,6 +179,25 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * prhs_reuse_step -- one CIS reuse step in a single call: the dilation of
+ * prhs_cis_reuse (without its similarity gate) followed by prhs_sparse_decode
+ * over the dilated set, with K and V rows gathered (Fig. 4: the set of an
+ * earlier query serves the next queries, grown around its clusters; Table
+ * VIII: radius r).
+ *
+ * Results are those of the two calls in sequence, bit for bit: out_idx,
+ * out_count, out and lse_sel. Argument rules are the union of the two calls'
+ * rules; q, k and v are required. No dropped mass is formed, since a reuse
+ * step has no dense log-sum-exp. When the heads fill the chip (or out_cap <=
+ * 256), out_cap <= 8192 and 2r + 1 <= 64, one kernel per step does both.
+ * ws: at least prhs_workspace_bytes(dims, PRHS_OP_DECODE, out_cap) bytes.
+ */
+int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                    const int32_t* anchor_count, int32_t radius, const void* q, const void* k,
+                    const void* v, int32_t* out_idx, int32_t out_cap, int32_t* out_count,
+                    float* out, float* lse_sel, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * prhs_anchor_step -- one exact-retrieval decode step in a single call: the
  * score scan, the selection (TOPN or DELTA, as prhs_select_topk) and the
  * sparse decode with the fused dropped mass, enqueued back to back on

@@ -23,16 +23,6 @@ namespace {
 constexpr int kCisThreads = 512;
 constexpr int kShortWindow = 64;
 
-__device__ __forceinline__ int wave_inclusive_max(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x = x > y ? x : y;
-  }
-  return x;
-}
-
 template <typename T>
 __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
     const int* __restrict__ anchor_idx, int anchor_cap, const int* __restrict__ anchor_count,

@@ -77,6 +77,7 @@ __device__ __forceinline__ void merge_head(const float* __restrict__ p, int nspl
 constexpr int kModeScores = 0;  // scores of the selected rows are given
 constexpr int kModeGather = 1;  // scores are computed from gathered K rows
 constexpr int kModeMixed = 2;   // per head, by mix[head]: given (idx) or gathered (idx2)
+constexpr int kModeDilate = 3;  // idx: anchor sets, dilated in the kernel; K rows gathered
 
 // One split of one head. With given scores, the scores of the selected rows are
 // read from sel_scores (compact, in idx order) when it is given, else gathered
@@ -271,6 +272,77 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 // those of the split kernel and its merge.
 constexpr int kHeadThreads = 1024;
 constexpr int kHeadLoads = 8;
+constexpr int kShortWindow = 64;
+
+// CIS dilation of one head's anchor list src[0:n) into the LDS list sidx and
+// the output dst[0:out_cap), as the dilation kernel defines it: anchor i
+// proposes [i - r, i + r] clipped to [0, t), starting after the largest end of
+// every earlier window (a running maximum over the list), so the output is the
+// sorted union for an ascending list and strictly ascending for any list;
+// prefix sums of the window lengths give the offsets. Windows of at most
+// kShortWindow keys, written by their own thread. out_cap must not exceed the
+// LDS list. Returns min(total, out_cap).
+// `first` is src[threadIdx.x] (or anything past n), loaded by the caller
+// together with the count.
+__device__ __forceinline__ int dilate_to_lds(const int* __restrict__ src, int n, int first, int r,
+                                             int t, int* sidx, int* __restrict__ dst, int out_cap,
+                                             int (*s_wmax)[kHeadThreads / kWave],
+                                             uint32_t (*s_wsum)[kHeadThreads / kWave]) {
+  constexpr int NT = kHeadThreads, NW = NT / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  int base = 0;
+  int prev_end = -1;
+  int next = tid < n ? first : -1;
+  for (int tile = 0, par = 0; tile < n; tile += NT, par ^= 1) {
+    const int j = tile + tid;
+    const int i = next;
+    next = j + NT < n ? src[j + NT] : -1;
+    int lo = 0, hi = -1;
+    if (j < n && i >= 0 && i < t) {
+      lo = i - r > 0 ? i - r : 0;
+      hi = i < t - 1 - r ? i + r : t - 1;
+    }
+    const int incl_max = wave_inclusive_max(hi);
+    if (lane == kWave - 1) s_wmax[par][w] = incl_max;
+    __syncthreads();
+    int before = prev_end;
+    int tile_max = prev_end;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int v = s_wmax[par][k];
+      if (k < w) before = before > v ? before : v;
+      tile_max = tile_max > v ? tile_max : v;
+    }
+    int excl_max = __shfl_up(incl_max, 1);
+    if (lane == 0) excl_max = -1;
+    if (excl_max > before) before = excl_max;
+    if (lo < before + 1) lo = before + 1;
+    const uint32_t len = hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
+    const uint32_t incl = wave_scan_u32(len);
+    if (lane == kWave - 1) s_wsum[par][w] = incl;
+    __syncthreads();
+    uint32_t off = 0, tile_total = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const uint32_t v = s_wsum[par][k];
+      if (k < w) off += v;
+      tile_total += v;
+    }
+    off += incl - len;
+    for (uint32_t k = 0; k < len; ++k) {
+      const uint32_t o = (uint32_t)base + off + k;
+      if (o < (uint32_t)out_cap) {
+        dst[o] = lo + (int)k;
+        sidx[o] = lo + (int)k;
+      }
+    }
+    base += (int)tile_total;
+    prev_end = tile_max;
+  }
+  return base < out_cap ? base : out_cap;
+}
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
@@ -280,7 +352,8 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
     const int* __restrict__ idx2, int idx2_cap, const int* __restrict__ count2,
     const int* __restrict__ mix, int Hq, int Hkv, int t, long long sb, long long sh,
     long long st, int ld, float scale, float* __restrict__ out, float* __restrict__ lse_sel,
-    const float* __restrict__ lse_all, float* __restrict__ delta, float* __restrict__ tau) {
+    const float* __restrict__ lse_all, float* __restrict__ delta, float* __restrict__ tau,
+    int radius, int* __restrict__ dil_idx, int dil_cap, int* __restrict__ dil_count) {
   constexpr int NW = kHeadThreads / kWave;
   constexpr int E = Elem<T>::kPer16B;
   constexpr int LPR = D / E;
@@ -291,6 +364,8 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   __shared__ float sm[NW];
   __shared__ float sl[NW];
   __shared__ __align__(16) float so[NW][D];
+  __shared__ int s_wmax[2][NW];
+  __shared__ uint32_t s_wsum[2][NW];
 
   const int head = blockIdx.x;
   const int b = head / Hq;
@@ -301,25 +376,35 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   const int rr = lane / LPR;
 
   const bool has_scores = MODE == kModeScores || (MODE == kModeMixed && mix[head] != 0);
-  const bool first = has_scores || MODE == kModeGather;
-  const int* ih = first ? idx : idx2;
-  const int icap = first ? idx_cap : idx2_cap;
-  const int* ch = first ? count : count2;
-  const int n = max(0, min(ch[head], icap));
+  const bool primary = has_scores || MODE == kModeGather || MODE == kModeDilate;
+  const int* ih = primary ? idx : idx2;
+  const int icap = primary ? idx_cap : idx2_cap;
+  const int* ch = primary ? count : count2;
   const int* irow = ih + (size_t)head * icap;
+  // the list's first entries are requested with the count (the capacity
+  // bounds the buffer), so the two loads share one round trip
+  const int first = (int)threadIdx.x < icap ? irow[threadIdx.x] : -1;
+  int n = max(0, min(ch[head], icap));
+  // the index list in LDS (indices outside [0, t) become -1): the given list,
+  // or the dilation of the anchor list
+  if constexpr (MODE == kModeDilate) {
+    n = dilate_to_lds(irow, n, first, radius < t ? radius : t, t, sidx,
+                      dil_idx + (size_t)head * dil_cap, dil_cap, s_wmax, s_wsum);
+    if (threadIdx.x == 0) dil_count[head] = n;
+  } else {
+    for (int r = threadIdx.x; r < n; r += kHeadThreads) {
+      const int id = r < kHeadThreads ? first : irow[r];
+      sidx[r] = id >= 0 && id < t ? id : -1;
+    }
+  }
+  __syncthreads();
   const int rw = ((n + NW - 1) / NW + RPW - 1) / RPW * RPW;
   const int rb = w * rw;
   const int re = min(n, rb + rw);
   const size_t kv_off = (size_t)b * sb + (size_t)g * sh;
   const size_t row_bytes = (size_t)st * sizeof(T);
 
-  // the index list in LDS (indices outside [0, t) become -1), then the
-  // scores of the wave's rows
-  for (int r = threadIdx.x; r < n; r += kHeadThreads) {
-    const int id = irow[r];
-    sidx[r] = id >= 0 && id < t ? id : -1;
-  }
-  __syncthreads();
+  // the scores of the wave's rows
   float mw = -INFINITY;
   if (has_scores) {
     for (int r = rb + lane; r < re; r += kWave) {
@@ -460,9 +545,18 @@ void launch_split_mode(const prhs_dims& d, const SplitArgs& a, float* part, int 
                      d.scores_ld, scale, part, nsplit);
 }
 
+// Dilation output of the fused reuse step (kModeDilate only).
+struct DilateArgs {
+  int radius = 0;
+  int* idx = nullptr;
+  int cap = 0;
+  int* count = nullptr;
+};
+
 template <typename T, int D, int MODE>
 void launch_head_mode(const prhs_dims& d, const SplitArgs& a, float* out, float* lse_sel,
-                      const float* lse_all, float* delta, float* tau, hipStream_t stream) {
+                      const float* lse_all, float* delta, float* tau, hipStream_t stream,
+                      const DilateArgs& dl = DilateArgs()) {
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
   hipLaunchKernelGGL((decode_head_kernel<T, D, MODE>), dim3(d.batch * d.n_q_heads),
                      dim3(kHeadThreads), 0, stream, static_cast<const T*>(a.q),
@@ -470,7 +564,13 @@ void launch_head_mode(const prhs_dims& d, const SplitArgs& a, float* out, float*
                      a.count, a.sel_scores, a.scores, a.idx2, a.idx2_cap, a.count2, a.mix,
                      d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b,
                      (long long)d.kv_stride_h, (long long)d.kv_stride_t, d.scores_ld, scale, out,
-                     lse_sel, lse_all, delta, tau);
+                     lse_sel, lse_all, delta, tau, dl.radius, dl.idx, dl.cap, dl.count);
+}
+
+template <typename T, int D>
+void launch_reuse_head(const prhs_dims& d, const SplitArgs& a, float* out, float* lse_sel,
+                       const DilateArgs& dl, hipStream_t stream) {
+  launch_head_mode<T, D, kModeDilate>(d, a, out, lse_sel, nullptr, nullptr, nullptr, stream, dl);
 }
 
 template <typename T, int D>
@@ -547,6 +647,35 @@ hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k,
   float* part = static_cast<float*>(ws);
   launch_split_any(d, a, part, nsplit, stream);
   return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream, mix);
+}
+
+hipError_t launch_reuse(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
+                        const int* anchor_count, int radius, const void* q, const void* k,
+                        const void* v, int* out_idx, int out_cap, int* out_count, float* out,
+                        float* lse_sel, void* ws, hipStream_t stream) {
+  const int r = radius < d.ctx_len ? radius : d.ctx_len;
+  if (decode_per_head(d, out_cap) && 2 * r + 1 <= kShortWindow) {
+    const SplitArgs a{q, k, v, anchor_idx, anchor_cap, anchor_count, nullptr, nullptr,
+                      nullptr, 0, nullptr, nullptr};
+    DilateArgs dl;
+    dl.radius = radius;
+    dl.idx = out_idx;
+    dl.cap = out_cap;
+    dl.count = out_count;
+    if (d.dtype == PRHS_F16) {
+      if (d.head_dim == 128) launch_reuse_head<__half, 128>(d, a, out, lse_sel, dl, stream);
+      else launch_reuse_head<__half, 64>(d, a, out, lse_sel, dl, stream);
+    } else {
+      if (d.head_dim == 128) launch_reuse_head<float, 128>(d, a, out, lse_sel, dl, stream);
+      else launch_reuse_head<float, 64>(d, a, out, lse_sel, dl, stream);
+    }
+    return hipGetLastError();
+  }
+  hipError_t err = launch_cis(d, anchor_idx, anchor_cap, anchor_count, radius, nullptr, nullptr,
+                              0.f, out_idx, out_cap, out_count, nullptr, stream);
+  if (err != hipSuccess) return err;
+  return launch_decode(d, q, k, v, out_idx, out_cap, out_count, nullptr, nullptr, nullptr, out,
+                       lse_sel, nullptr, nullptr, ws, stream);
 }
 
 hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float* out,

@@ -249,6 +249,34 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                 stream, "prhs_sparse_decode");
 }
 
+int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,
+                    const int32_t* anchor_count, int32_t radius, const void* q, const void* k,
+                    const void* v, int32_t* out_idx, int32_t out_cap, int32_t* out_count,
+                    float* out, float* lse_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!anchor_idx || !anchor_count || !out_idx || !out_count)
+    return fail(PRHS_E_NULL, "anchor_idx, anchor_count, out_idx and out_count are required");
+  if (!q || !k || !v || !out || !lse_sel)
+    return fail(PRHS_E_NULL, "q, k, v, out and lse_sel are required");
+  if (radius < 0) return fail(PRHS_E_BUDGET, "radius must be >= 0");
+  if (anchor_cap < 1) return fail(PRHS_E_CAPACITY, "anchor_cap must be >= 1");
+  const long long need_ll = (2LL * radius + 1) * (long long)anchor_cap;
+  const long long need = need_ll < dims->ctx_len ? need_ll : dims->ctx_len;
+  if (out_cap < need)
+    return fail(PRHS_E_CAPACITY, "out_cap %d < min(t, (2r+1)*anchor_cap) = %lld", out_cap, need);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(PRHS_E_ALIGN, "q, k and v must be 16-byte aligned");
+  if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
+  if (ws_bytes < decode_ws(dims, out_cap))
+    return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", decode_ws(dims, out_cap),
+                ws_bytes);
+  if (!aligned16(ws)) return fail(PRHS_E_ALIGN, "workspace must be 16-byte aligned");
+  return finish(prhs::launch_reuse(*dims, anchor_idx, anchor_cap, anchor_count, radius, q, k, v,
+                                   out_idx, out_cap, out_count, out, lse_sel, ws, stream),
+                stream, "prhs_reuse_step");
+}
+
 int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
                        int32_t force_refresh, float sim_tau, const void* q, const void* k,
                        const void* v, float* scores, float* lse_all, int32_t* anchor_idx,

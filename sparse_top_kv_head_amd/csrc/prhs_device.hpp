@@ -140,6 +140,17 @@ __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
   return x;
 }
 
+// Inclusive running maximum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_max(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x = x > y ? x : y;
+  }
+  return x;
+}
+
 __device__ __forceinline__ uint32_t lane_read(uint32_t x, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
 }

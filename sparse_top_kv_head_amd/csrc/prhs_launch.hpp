@@ -120,6 +120,15 @@ hipError_t launch_merge(const prhs_dims& d, const float* part, int nsplit, float
 // Decode where head h attends over (idx, count, sel_scores) when mix[h] != 0
 // and over (idx2, count2) with scores from gathered K rows otherwise; delta
 // and tau are written for the mix[h] != 0 heads only.
+// CIS reuse step: dilation of the anchor sets, then the decode over gathered
+// K and V rows; in one kernel when the per-head decode applies, out_cap fits
+// its LDS and the windows are short, else dilation and decode back to back.
+// Results equal those of the two steps in sequence, bit for bit.
+hipError_t launch_reuse(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
+                        const int* anchor_count, int radius, const void* q, const void* k,
+                        const void* v, int* out_idx, int out_cap, int* out_count, float* out,
+                        float* lse_sel, void* ws, hipStream_t stream);
+
 hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k, const void* v,
                                const int* mix, const int* idx, int idx_cap, const int* count,
                                const float* sel_scores, const int* idx2, int idx2_cap,

@@ -97,10 +97,15 @@ class DecodeEngine:
 
     def reuse_step(self, q, K, V, anchor_idx, anchor_count, anchor_cap, radius,
                    q_anchor=None, sim_tau=0.0, stream=None):
-        """CIS reuse step: dilate the anchor's set, then attend with gathered K and V rows."""
-        P.prhs_cis_reuse(self.dims, anchor_idx, anchor_cap, anchor_count, radius,
-                         q if q_anchor is not None else None, q_anchor, sim_tau, self.idx, self.cap,
-                         self.count, self.reuse_ok if q_anchor is not None else None, stream=stream)
+        """CIS reuse step: dilate the anchor's set, then attend with gathered K and V rows
+        (one call; with q_anchor, the dilation call also evaluates the similarity gate)."""
+        if q_anchor is None:
+            P.prhs_reuse_step(self.dims, anchor_idx, anchor_cap, anchor_count, radius, q, K, V,
+                              self.idx, self.cap, self.count, self.out, self.lse_sel, self.ws,
+                              stream=stream)
+            return
+        P.prhs_cis_reuse(self.dims, anchor_idx, anchor_cap, anchor_count, radius, q, q_anchor,
+                         sim_tau, self.idx, self.cap, self.count, self.reuse_ok, stream=stream)
         self.decode(q, K, V, use_scores=False, stream=stream)
 
     def dense_step(self, q, K, V, stream=None):

@@ -41,7 +41,7 @@ PRHS_OP_EXPAND = 5
 PRHS_MAX_SELECT_CTX = 65536
 
 EXPORTED = (
-    "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
+    "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step", "prhs_sparse_decode",
     "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step", "prhs_dense_decode",
     "prhs_random_expand", "prhs_workspace_bytes",
     "prhs_status_string", "prhs_last_error",
@@ -87,6 +87,8 @@ def lib():
         L.prhs_score.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_select_topk.argtypes = [dp, vp, vp, i32, i32, f32, vp, i32, vp, vp, vp, vp]
         L.prhs_cis_reuse.argtypes = [dp, vp, i32, vp, i32, vp, vp, f32, vp, i32, vp, vp, vp]
+        L.prhs_reuse_step.argtypes = [dp, vp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                                      sz, vp]
         L.prhs_sparse_decode.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp]
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
@@ -104,7 +106,8 @@ def lib():
         L.prhs_status_string.restype = ctypes.c_char_p
         L.prhs_last_error.argtypes = []
         L.prhs_last_error.restype = ctypes.c_char_p
-        for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_sparse_decode",
+        for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step",
+                     "prhs_sparse_decode",
                      "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode",
                      "prhs_adaptive_step", "prhs_random_expand"):
             getattr(L, name).restype = ctypes.c_int
@@ -182,6 +185,15 @@ def prhs_cis_reuse(dims, anchor_idx, anchor_cap, anchor_count, radius, q_cur, q_
     _check(lib().prhs_cis_reuse(ctypes.byref(dims), _p(anchor_idx), anchor_cap, _p(anchor_count),
                                 radius, _p(q_cur), _p(q_anchor), sim_tau, _p(out_idx), out_cap,
                                 _p(out_count), _p(reuse_ok), _stream(stream)))
+
+
+def prhs_reuse_step(dims, anchor_idx, anchor_cap, anchor_count, radius, q, k, v, out_idx, out_cap,
+                    out_count, out, lse_sel, ws=None, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
+    _check(lib().prhs_reuse_step(ctypes.byref(dims), _p(anchor_idx), anchor_cap, _p(anchor_count),
+                                 radius, _p(q), _p(k), _p(v), _p(out_idx), out_cap, _p(out_count),
+                                 _p(out), _p(lse_sel), _p(ws), ws_bytes, _stream(stream)))
 
 
 def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out, lse_sel,

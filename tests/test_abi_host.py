@@ -65,6 +65,14 @@ def _cis(L, d, a=FAKE, acap=64, acnt=FAKE, r=2, qc=None, qa=None, tau=0.8, o=FAK
                             tau, o, ocap, ocnt, ok, None)
 
 
+def _reuse(L, d, a=FAKE, acap=64, acnt=FAKE, r=2, q=FAKE, k=FAKE, v=FAKE, o=FAKE, ocap=320,
+           ocnt=FAKE, out=FAKE, lsel=FAKE, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 1 << 30
+    return L.prhs_reuse_step(ctypes.byref(d) if d is not None else None, a, acap, acnt, r, q, k, v,
+                             o, ocap, ocnt, out, lsel, ws, wsb, None)
+
+
 def _decode(L, d, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cap=64, cnt=FAKE, s=FAKE, lse=FAKE, out=FAKE,
             lsel=FAKE, dl=FAKE, tau=FAKE, ws=FAKE, wsb=None, sel=None):
     if wsb is None:
@@ -100,6 +108,7 @@ def test_bad_dims_rejected_by_every_call(L, field, value, code):
     assert _score(L, d) == code
     assert _select(L, d) == code
     assert _cis(L, d) == code
+    assert _reuse(L, d) == code
     assert _decode(L, d) == code
     assert _dense(L, d) == code
     assert _adaptive(L, d) == code
@@ -113,6 +122,7 @@ def test_null_dims(L):
     assert _score(L, None) == P.PRHS_E_NULL
     assert _select(L, None) == P.PRHS_E_NULL
     assert _cis(L, None) == P.PRHS_E_NULL
+    assert _reuse(L, None) == P.PRHS_E_NULL
     assert _decode(L, None) == P.PRHS_E_NULL
     assert L.prhs_dropped_mass(None, FAKE, FAKE, FAKE, None, None) == P.PRHS_E_NULL
 
@@ -160,6 +170,22 @@ def test_cis_argument_checks(L):
     assert _cis(L, d, r=100, ocap=999) == P.PRHS_E_CAPACITY   # min(t, ...) = 1000
     assert _cis(L, d, ok=FAKE) == P.PRHS_E_NULL
     assert _cis(L, d, ok=FAKE, qc=FAKE, qa=FAKE, tau=math.nan) == P.PRHS_E_BUDGET
+
+
+def test_reuse_step_argument_checks(L):
+    d = _dims()
+    need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DECODE, 320)
+    for name in ("a", "acnt", "o", "ocnt", "q", "k", "v", "out", "lsel"):
+        assert _reuse(L, d, **{name: None}) == P.PRHS_E_NULL, name
+    assert _reuse(L, d, r=-1) == P.PRHS_E_BUDGET
+    assert _reuse(L, d, acap=0) == P.PRHS_E_CAPACITY
+    assert _reuse(L, d, ocap=319) == P.PRHS_E_CAPACITY           # (2r+1)*64 = 320 < t
+    assert _reuse(L, d, r=100, ocap=999) == P.PRHS_E_CAPACITY    # min(t, ...) = 1000
+    for name in ("q", "k", "v"):
+        assert _reuse(L, d, **{name: FAKE_MIS}) == P.PRHS_E_ALIGN, name
+    assert _reuse(L, d, ws=None) == P.PRHS_E_WORKSPACE
+    assert _reuse(L, d, wsb=need - 4) == P.PRHS_E_WORKSPACE
+    assert _reuse(L, d, ws=FAKE_MIS, wsb=need) == P.PRHS_E_ALIGN
 
 
 def test_decode_argument_checks(L):

@@ -135,6 +135,99 @@ def test_fused_select_decode(kind, B, Hq, Hkv, t, N):
                 assert abs(eng.tau[b, h].item() - (1.0 - d_ref)) <= DELTA_TOL
 
 
+REUSE_CASES = [
+    # B, Hq, Hkv, d, t, dtype, anchor cap, radius, anchor lists
+    (2, 64, 8, 128, 5000, torch.float16, 512, 2, "sorted"),    # 128 heads: one kernel
+    (1, 128, 32, 64, 3001, torch.float16, 300, 0, "sorted"),   # radius 0, d = 64
+    (1, 128, 16, 128, 2000, torch.float32, 200, 31, "sorted"), # 2r + 1 = 63, fp32
+    (1, 128, 16, 128, 2000, torch.float16, 100, 40, "sorted"), # 2r + 1 = 81: dilation kernel first
+    (1, 8, 2, 128, 3000, torch.float16, 256, 2, "sorted"),     # 8 heads: split decode and merge
+    (1, 128, 32, 128, 4000, torch.float16, 700, 2, "edges"),   # empty, clamped, ends, unsorted
+]
+
+
+def _anchor_lists(kind, B, H, t, cap, g):
+    idx = torch.zeros((B, H, cap), dtype=torch.int32)
+    cnt = torch.zeros((B, H), dtype=torch.int32)
+    for b in range(B):
+        for h in range(H):
+            n = int(torch.randint(cap // 2, cap + 1, (1,), generator=g))
+            sel = torch.randperm(t, generator=g)[:n].sort().values.to(torch.int32)
+            idx[b, h, :n] = sel
+            cnt[b, h] = n
+    if kind == "edges":
+        cnt[0, 0] = 0                                   # empty
+        idx[0, 1] = torch.randperm(t, generator=g)[:cap].sort().values.to(torch.int32)
+        cnt[0, 1] = cap + 50                            # clamped to cap
+        idx[0, 2, :3] = torch.tensor([0, 1, t - 1], dtype=torch.int32)
+        cnt[0, 2] = 3                                   # both ends of the context
+        idx[0, 3, :6] = torch.tensor([40, 10, 10, 900, 5, t + 7], dtype=torch.int32)
+        cnt[0, 3] = 6                                   # unsorted, repeated, out of range
+    return idx, cnt
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,t,dtype,cap,r,kind", REUSE_CASES)
+def test_reuse_step_matches_two_calls(B, Hq, Hkv, d, t, dtype, cap, r, kind):
+    """The one-call reuse step equals prhs_cis_reuse followed by a gathered-K
+    prhs_sparse_decode, bit for bit, and the oracle on well-formed heads."""
+    dev = _dev()
+    g = torch.Generator().manual_seed(t + cap + r)
+    K = torch.randn((B, Hkv, t, d), generator=g).to(dtype).to(dev)
+    V = torch.randn((B, Hkv, t, d), generator=g).to(dtype).to(dev)
+    q = (torch.randn((B, Hq, d), generator=g) * 2.0).to(dtype).to(dev)
+    aidx, acnt = _anchor_lists(kind, B, Hq, t, cap, g)
+    aidx, acnt = aidx.to(dev), acnt.to(dev)
+    dims = P.make_dims(K, Hq)
+    ocap = min(t, (2 * r + 1) * cap)
+    res = []
+    for one_call in (True, False):
+        o_idx = torch.full((B, Hq, ocap), -7, dtype=torch.int32, device=dev)
+        o_cnt = torch.full((B, Hq), -7, dtype=torch.int32, device=dev)
+        out = torch.full((B, Hq, d), 7.0, device=dev)
+        lse = torch.full((B, Hq), 7.0, device=dev)
+        ws = P.alloc_workspace(dims, P.PRHS_OP_DECODE, ocap, device=dev)
+        if one_call:
+            P.prhs_reuse_step(dims, aidx, cap, acnt, r, q, K, V, o_idx, ocap, o_cnt, out, lse, ws)
+        else:
+            P.prhs_cis_reuse(dims, aidx, cap, acnt, r, None, None, 0.0, o_idx, ocap, o_cnt)
+            P.prhs_sparse_decode(dims, q, K, V, o_idx, ocap, o_cnt, None, None, out, lse, ws=ws)
+        torch.cuda.synchronize()
+        res.append((o_idx, o_cnt, out, lse))
+    (i1, c1, o1, l1), (i2, c2, o2, l2) = res
+    assert torch.equal(c1, c2)
+    for b in range(B):
+        for h in range(Hq):
+            n = int(c1[b, h])
+            assert torch.equal(i1[b, h, :n], i2[b, h, :n]), (b, h)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # the oracle on well-formed heads
+    s_all = O.attention_scores(_np(q), _np(K))
+    V64 = _np(V)
+    G = Hq // Hkv
+    a_cpu, n_cpu = aidx.cpu().numpy(), acnt.cpu().numpy()
+    for b in range(B):
+        for h in range(0, Hq, 7):
+            if kind == "edges" and b == 0 and h in (0, 1, 3):
+                continue
+            n = int(min(n_cpu[b, h], cap))
+            D_ref = O.cis_dilate(a_cpu[b, h, :n], r, t)
+            assert int(c1[b, h]) == len(D_ref)
+            assert np.array_equal(i1[b, h, :len(D_ref)].cpu().numpy(), D_ref)
+            if len(D_ref):
+                o_ref, l_ref = O.sparse_attention(s_all[b, h], V64[b, h // G], D_ref)
+                assert np.max(np.abs(_np(o1[b, h]) - o_ref)) <= OUT_TOL
+                assert abs(l1[b, h].item() - l_ref) <= 1e-3
+    if kind == "edges":
+        assert int(c1[0, 0]) == 0 and o1[0, 0].abs().max().item() == 0.0
+        assert l1[0, 0].item() == -float("inf")
+        D1 = O.cis_dilate(a_cpu[0, 1, :cap], r, t)
+        assert int(c1[0, 1]) == len(D1) and np.array_equal(i1[0, 1, :len(D1)].cpu().numpy(), D1)
+        # unsorted input: strictly ascending output inside [0, t)
+        n3 = int(c1[0, 3])
+        got = i1[0, 3, :n3].cpu().numpy()
+        assert n3 > 0 and np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < t
+
+
 def _small_cis(dev, batch=1, heads=8, ctx=4096, steps=8):
     cfg = CONFIGS["llama2_cis_8k"].replace(batch=batch, n_q_heads=heads, n_kv_heads=heads,
                                            ctx_len=ctx, budget=256, steps=steps)
@@ -197,11 +290,13 @@ def test_adaptive_never_gated_follows_period():
             assert torch.equal(ad.dil_count, reuse.count)
 
 
-def test_adaptive_graph_replay():
+@pytest.mark.parametrize("batch", [2, 16])
+def test_adaptive_graph_replay(batch):
     """The gated step captured as a HIP graph replays to the eager results, replay
-    after replay, with the state reset and eager work in between."""
+    after replay, with the state reset and eager work in between (16 heads:
+    split decode and merge; 128 heads: one workgroup per head)."""
     dev = _dev()
-    cfg, w = _small_cis(dev, batch=2)
+    cfg, w = _small_cis(dev, batch=batch)
     steps = 6
 
     def fresh():
@@ -230,6 +325,42 @@ def test_adaptive_graph_replay():
         torch.cuda.synchronize()
         for n in names:
             assert torch.equal(getattr(eng, n), ref[n]), (r, n)
+
+
+@pytest.mark.parametrize("batch", [1, 16])
+def test_reuse_step_graph_replay(batch):
+    """A captured CIS reuse step (dilation, then decode over gathered K and V
+    rows) replays to the eager results; at 128 heads the decode runs one
+    workgroup per head."""
+    dev = _dev()
+    cfg, w = _small_cis(dev, batch=batch)
+    H, N = cfg.n_q_heads, cfg.budget
+    anchor = DecodeEngine(w.K, H, N)
+    anchor.anchor_step(w.q[0], w.K, w.V, P.PRHS_TOPN, N)
+    cap = (2 * cfg.radius + 1) * N
+    eng = DecodeEngine(w.K, H, cap)
+    eng.reuse_step(w.q[1], w.K, w.V, anchor.idx, anchor.count, N, cfg.radius)
+    torch.cuda.synchronize()
+    names = ("idx", "count", "out", "lse_sel")
+    ref = {n: getattr(eng, n).clone() for n in names}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        eng.reuse_step(w.q[1], w.K, w.V, anchor.idx, anchor.count, N, cfg.radius)
+    other = DecodeEngine(w.K, H, cap)
+    for r in range(3):
+        other.reuse_step(w.q[2 + r], w.K, w.V, anchor.idx, anchor.count, N, cfg.radius)
+        for n in names:
+            getattr(eng, n).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ("count", "out", "lse_sel"):
+            assert torch.equal(getattr(eng, n), ref[n]), (r, n)
+        # the dilation writes the first count entries of each row
+        for b in range(cfg.batch):
+            for h in range(H):
+                c = int(ref["count"][b, h])
+                assert torch.equal(eng.idx[b, h, :c], ref["idx"][b, h, :c]), (r, b, h)
 
 
 def test_dense_decode_deterministic_and_graph():

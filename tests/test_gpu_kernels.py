@@ -537,12 +537,14 @@ def test_anchor_step_matches_separate_calls(mode, budget, heads):
         assert torch.equal(a.cap_hit, b.cap_hit)
 
 
-def test_anchor_step_graph_replay_matches_eager():
+@pytest.mark.parametrize("batch", [1, 4])
+def test_anchor_step_graph_replay_matches_eager(batch):
     """A captured step replays to the eager results, replay after replay, with
-    eager work and synchronisations between the replays."""
+    eager work and synchronisations between the replays (32 heads: split
+    decode and merge; 128 heads: decoded inside the select kernel)."""
     dev = _dev()
     from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=1, ctx_len=8192, budget=512, steps=3,
+    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=batch, ctx_len=8192, budget=512, steps=3,
                                              n_clusters=(64, 64))
     w = make_workload(cfg, device=dev)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
