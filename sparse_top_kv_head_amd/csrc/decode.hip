@@ -78,6 +78,8 @@ constexpr int kModeScores = 0;  // scores of the selected rows are given
 constexpr int kModeGather = 1;  // scores are computed from gathered K rows
 constexpr int kModeMixed = 2;   // per head, by mix[head]: given (idx) or gathered (idx2)
 constexpr int kModeDilate = 3;  // idx: anchor sets, dilated in the kernel; K rows gathered
+constexpr int kModeMixedDilate = 4;  // per head, by mix[head]: idx with its scores, or idx
+                                     // dilated in the kernel with K rows gathered
 
 // One split of one head. With given scores, the scores of the selected rows are
 // read from sel_scores (compact, in idx order) when it is given, else gathered
@@ -375,8 +377,12 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   const int c = lane % LPR;
   const int rr = lane / LPR;
 
-  const bool has_scores = MODE == kModeScores || (MODE == kModeMixed && mix[head] != 0);
-  const bool primary = has_scores || MODE == kModeGather || MODE == kModeDilate;
+  const bool has_scores =
+      MODE == kModeScores ||
+      ((MODE == kModeMixed || MODE == kModeMixedDilate) && mix[head] != 0);
+  const bool primary =
+      has_scores || MODE == kModeGather || MODE == kModeDilate || MODE == kModeMixedDilate;
+  const bool dilate = MODE == kModeDilate || (MODE == kModeMixedDilate && !has_scores);
   const int* ih = primary ? idx : idx2;
   const int icap = primary ? idx_cap : idx2_cap;
   const int* ch = primary ? count : count2;
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   int n = max(0, min(ch[head], icap));
   // the index list in LDS (indices outside [0, t) become -1): the given list,
   // or the dilation of the anchor list
-  if constexpr (MODE == kModeDilate) {
+  if (dilate) {  // uniform over the workgroup
     n = dilate_to_lds(irow, n, first, radius < t ? radius : t, t, sidx,
                       dil_idx + (size_t)head * dil_cap, dil_cap, s_wmax, s_wsum);
     if (threadIdx.x == 0) dil_count[head] = n;
@@ -647,6 +653,48 @@ hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k,
   float* part = static_cast<float*>(ws);
   launch_split_any(d, a, part, nsplit, stream);
   return launch_merge(d, part, nsplit, out, lse_sel, lse_all, delta, tau, stream, mix);
+}
+
+hipError_t launch_adaptive_decode(const prhs_dims& d, const void* q, const void* k,
+                                  const void* v, const int* mix, const int* anchor_idx,
+                                  int anchor_cap, const int* anchor_count,
+                                  const float* sel_scores, int radius, int* dil_idx, int dil_cap,
+                                  int* dil_count, const float* lse_all, float* out,
+                                  float* lse_sel, float* delta, float* tau, void* ws,
+                                  hipStream_t stream) {
+  const int r = radius < d.ctx_len ? radius : d.ctx_len;
+  const int cap = anchor_cap > dil_cap ? anchor_cap : dil_cap;
+  if (decode_per_head(d, cap) && 2 * r + 1 <= kShortWindow) {
+    const SplitArgs a{q, k, v, anchor_idx, anchor_cap, anchor_count, sel_scores, nullptr,
+                      nullptr, 0, nullptr, mix};
+    DilateArgs dl;
+    dl.radius = radius;
+    dl.idx = dil_idx;
+    dl.cap = dil_cap;
+    dl.count = dil_count;
+    if (d.dtype == PRHS_F16) {
+      if (d.head_dim == 128)
+        launch_head_mode<__half, 128, kModeMixedDilate>(d, a, out, lse_sel, lse_all, delta, tau,
+                                                        stream, dl);
+      else
+        launch_head_mode<__half, 64, kModeMixedDilate>(d, a, out, lse_sel, lse_all, delta, tau,
+                                                       stream, dl);
+    } else {
+      if (d.head_dim == 128)
+        launch_head_mode<float, 128, kModeMixedDilate>(d, a, out, lse_sel, lse_all, delta, tau,
+                                                       stream, dl);
+      else
+        launch_head_mode<float, 64, kModeMixedDilate>(d, a, out, lse_sel, lse_all, delta, tau,
+                                                      stream, dl);
+    }
+    return hipGetLastError();
+  }
+  hipError_t err = launch_cis(d, anchor_idx, anchor_cap, anchor_count, radius, nullptr, nullptr,
+                              0.f, dil_idx, dil_cap, dil_count, nullptr, stream, mix);
+  if (err != hipSuccess) return err;
+  return launch_decode_mixed(d, q, k, v, mix, anchor_idx, anchor_cap, anchor_count, sel_scores,
+                             dil_idx, dil_cap, dil_count, lse_all, out, lse_sel, delta, tau, ws,
+                             stream);
 }
 
 hipError_t launch_reuse(const prhs_dims& d, const int* anchor_idx, int anchor_cap,

@@ -340,12 +340,9 @@ int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
     err = prhs::launch_select(*dims, a, stream);
   }
   if (err == hipSuccess)
-    err = prhs::launch_cis(*dims, anchor_idx, n_budget, anchor_count, radius, nullptr, nullptr, 0.f,
-                           dil_idx, dil_cap, dil_count, nullptr, stream, refresh);
-  if (err == hipSuccess)
-    err = prhs::launch_decode_mixed(*dims, q, k, v, refresh, anchor_idx, n_budget, anchor_count,
-                                    sel, dil_idx, dil_cap, dil_count, lse_all, out, lse_sel, delta,
-                                    tau, w + L.dec, stream);
+    err = prhs::launch_adaptive_decode(*dims, q, k, v, refresh, anchor_idx, n_budget, anchor_count,
+                                       sel, radius, dil_idx, dil_cap, dil_count, lse_all, out,
+                                       lse_sel, delta, tau, w + L.dec, stream);
   return finish(err, stream, "prhs_adaptive_step");
 }
 

@@ -129,6 +129,20 @@ hipError_t launch_reuse(const prhs_dims& d, const int* anchor_idx, int anchor_ca
                         const void* v, int* out_idx, int out_cap, int* out_count, float* out,
                         float* lse_sel, void* ws, hipStream_t stream);
 
+// Adaptive step's decode: heads with mix[head] != 0 attend over their fresh
+// selection with its scores; the others dilate their anchor set (into
+// dil_idx / dil_count, which fresh heads leave untouched) and attend with
+// gathered K rows. One kernel when the per-head decode applies and the windows
+// are short, else the masked dilation and the mixed decode; the results are the
+// same bit for bit.
+hipError_t launch_adaptive_decode(const prhs_dims& d, const void* q, const void* k,
+                                  const void* v, const int* mix, const int* anchor_idx,
+                                  int anchor_cap, const int* anchor_count,
+                                  const float* sel_scores, int radius, int* dil_idx, int dil_cap,
+                                  int* dil_count, const float* lse_all, float* out,
+                                  float* lse_sel, float* delta, float* tau, void* ws,
+                                  hipStream_t stream);
+
 hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k, const void* v,
                                const int* mix, const int* idx, int idx_cap, const int* count,
                                const float* sel_scores, const int* idx2, int idx2_cap,

@@ -265,11 +265,13 @@ def test_adaptive_all_refresh_equals_anchor_steps():
         assert torch.equal(ad.anchor_idx, an.idx) and torch.equal(ad.anchor_count, an.count)
 
 
-def test_adaptive_never_gated_follows_period():
+@pytest.mark.parametrize("batch", [1, 16])
+def test_adaptive_never_gated_follows_period(batch):
     """A threshold below -1 never fires: heads refresh exactly on the forced steps,
-    and the shared steps equal the plain CIS reuse step."""
+    and the shared steps equal the plain CIS reuse step bit for bit (8 heads:
+    dilation, then split decode; 128 heads: dilation inside the decode kernel)."""
     dev = _dev()
-    cfg, w = _small_cis(dev)
+    cfg, w = _small_cis(dev, batch=batch)
     period = 3
     ad = AdaptiveEngine(w.K, cfg.n_q_heads, cfg.budget, cfg.radius, period, -2.0)
     anchor = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
@@ -288,6 +290,10 @@ def test_adaptive_never_gated_follows_period():
             assert torch.equal(ad.out, reuse.out) and torch.equal(ad.lse_sel, reuse.lse_sel), step
         if step % period:
             assert torch.equal(ad.dil_count, reuse.count)
+            for b in range(cfg.batch):
+                for h in range(cfg.n_q_heads):
+                    c = int(reuse.count[b, h])
+                    assert torch.equal(ad.dil_idx[b, h, :c], reuse.idx[b, h, :c]), (step, b, h)
 
 
 @pytest.mark.parametrize("batch", [2, 16])
