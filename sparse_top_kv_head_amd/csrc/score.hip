@@ -17,6 +17,71 @@ namespace prhs {
 namespace {
 
 constexpr int kScoreThreads = 256;
+
+// The G partial dot products of a 16-lane row group (lane c holds its slice's
+// share of every head) reduced and scattered: exchanges between lanes c and
+// 15 - c, then c and 7 - c, then within quads, each halving the heads a lane
+// carries, so that every lane ends with the full sum of one head, head_of(c).
+// 5 DPP additions for G = 4 and 8 for G = 8, against 4 G for separate sums.
+template <int G>
+__device__ __forceinline__ int rs16_head(int c) {
+  if constexpr (G == 1) return 0;
+  else if constexpr (G == 2) return c < 8 ? 0 : 1;
+  else if constexpr (G == 4) return (c < 8 ? 0 : 2) + ((c & 7) < 4 ? 0 : 1);
+  else return (c < 8 ? 0 : 4) + ((c & 7) < 4 ? 0 : 2) + ((c & 2) ? 1 : 0);
+}
+
+// acc[] must come from the query heads in lane order: lanes c >= 8 take the
+// two halves of the head list swapped (rs16_qorder), so that every lane keeps
+// acc[0 : G/2) and sends acc[G/2 : G) in the first exchange.
+template <int G>
+__device__ __forceinline__ int rs16_qorder(int j, int c) {
+  return (G > 1 && c >= 8) ? (j + G / 2) % G : j;
+}
+
+template <int G>
+__device__ __forceinline__ float rs16(const float (&acc)[G], int c) {
+  if constexpr (G == 1) {
+    return group_sum<16>(acc[0]);
+  } else {
+    // exchange with lane 15 - c: the low half keeps the first G/2 heads
+    constexpr int H1 = G / 2;
+    float k1[H1];
+#pragma unroll
+    for (int i = 0; i < H1; ++i) k1[i] = acc[i] + dpp<kDppRowMirror>(acc[H1 + i]);
+    if constexpr (G == 2) {
+      float x = k1[0];
+      x += dpp<kDppRowHalfMirror>(x);
+      x += dpp<kDppXor2>(x);
+      x += dpp<kDppXor1>(x);
+      return x;
+    } else {
+      // exchange with lane 7 - c inside each half
+      constexpr int H2 = H1 / 2;
+      float k2[H2];
+      const bool lo2 = (c & 7) < 4;
+#pragma unroll
+      for (int i = 0; i < H2; ++i) {
+        const float keep = lo2 ? k1[i] : k1[H2 + i];
+        const float send = lo2 ? k1[H2 + i] : k1[i];
+        k2[i] = keep + dpp<kDppRowHalfMirror>(send);
+      }
+      float x;
+      if constexpr (G == 4) {
+        x = k2[0];
+        x += dpp<kDppXor2>(x);
+      } else {
+        // G == 8: exchange with lane c ^ 2
+        const bool lo3 = (c & 2) == 0;
+        const float keep = lo3 ? k2[0] : k2[1];
+        const float send = lo3 ? k2[1] : k2[0];
+        x = keep + dpp<kDppXor2>(send);
+      }
+      x += dpp<kDppXor1>(x);
+      return x;
+    }
+  }
+}
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
 // With `active` (per query head), a workgroup whose group has no active head
@@ -67,34 +132,51 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
 
   uint4 qv[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) qv[j] = load16(q + ((size_t)(b * Hq + h0 + j) * D + c * E));
+  for (int j = 0; j < G; ++j) {
+    const int hj = LPR == 16 ? rs16_qorder<G>(j, c) : j;
+    qv[j] = load16(q + ((size_t)(b * Hq + h0 + hj) * D + c * E));
+  }
 
   const char* kbase = reinterpret_cast<const char*>(k + b * sb + g * sh) + c * 16;
   const size_t row_bytes = (size_t)st * sizeof(T);
   const int wrow0 = w * RW;
   const int grow0 = chunk * CHUNK + wrow0;
+  // every chunk but the last lies inside [0, t): its loads need no checks
+  const bool full = (chunk + 1) * CHUNK <= t;
 
 #pragma unroll 1
   for (int it = 0; it < ITERS; ++it) {
     uint4 kv[U];
+    const char* p0 = kbase + (size_t)(grow0 + it * U * RPW + rr) * row_bytes;
+    const size_t step = (size_t)RPW * row_bytes;
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = grow0 + it * U * RPW + u * RPW + rr;
-      if (r < t) {
-        kv[u] = load16_stream(kbase + (size_t)r * row_bytes);
-      } else {
-        kv[u] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < U; ++u) kv[u] = load16_stream(p0 + u * step);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = grow0 + it * U * RPW + u * RPW + rr;
+        kv[u] = r < t ? load16_stream(p0 + u * step) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float acc[G];
+      if constexpr (LPR == 16) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) acc[j] = group_sum<LPR>(dot16(kv[u], qv[j], 0.f, T()));
-      float val = acc[0];
+        for (int j = 0; j < G; ++j) acc[j] = dot16(kv[u], qv[j], 0.f, T());
+        const float val = rs16<G>(acc, c);
+        // lanes holding the same head carry the same sum: one writes it
+        if ((c & (16 / G - 1)) == 0)
+          sc[rs16_head<G>(c)][wrow0 + it * U * RPW + u * RPW + rr] = val * scale;
+      } else {
 #pragma unroll
-      for (int j = 1; j < G; ++j) val = (c == j) ? acc[j] : val;
-      if (c < G) sc[c][wrow0 + it * U * RPW + u * RPW + rr] = val * scale;
+        for (int j = 0; j < G; ++j) acc[j] = group_sum<LPR>(dot16(kv[u], qv[j], 0.f, T()));
+        float val = acc[0];
+#pragma unroll
+        for (int j = 1; j < G; ++j) val = (c == j) ? acc[j] : val;
+        if (c < G) sc[c][wrow0 + it * U * RPW + u * RPW + rr] = val * scale;
+      }
     }
   }
   __syncthreads();
