@@ -84,6 +84,7 @@ FUSED_CASES = [
     ("ties", 2, 64, 16, 3000, 700),      # few distinct scores: boundary ties
     ("random", 1, 8, 2, 2000, 256),      # one-split budget on few heads
     ("random", 1, 128, 32, 1500, 1),     # N = 1
+    ("random", 1, 128, 16, 40000, 2048), # past 32K keys: the 64-keys-per-thread select
 ]
 
 
