@@ -229,6 +229,41 @@ def test_reuse_step_matches_two_calls(B, Hq, Hkv, d, t, dtype, cap, r, kind):
         assert n3 > 0 and np.all(np.diff(got) > 0) and got.min() >= 0 and got.max() < t
 
 
+@pytest.mark.parametrize("q_scale", [(1.0, 1.0), (1.0, 4.0)])
+def test_delta_consecutive_steps(q_scale):
+    """Consecutive DELTA anchor steps over a drifting query: every head of every
+    step matches the oracle (smallest N with delta <= target, capped), and a
+    call given a threshold hint selects exactly what a call without one does."""
+    dev = _dev()
+    cfg = CONFIGS["delta_16k"].replace(batch=2, n_q_heads=8, n_kv_heads=8, ctx_len=8192,
+                                       budget=1024, steps=4, q_scale=q_scale)
+    w = make_workload(cfg, device=dev, layer=3)
+    hinted = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    plain = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    K64, V64 = _np(w.K), _np(w.V)
+    for step in range(cfg.steps):
+        hinted.anchor_step(w.q[step], w.K, w.V, P.PRHS_DELTA, cfg.budget, cfg.delta_star)
+        plain.anchor_step(w.q[step], w.K, w.V, P.PRHS_DELTA, cfg.budget, cfg.delta_star,
+                          hint=False)
+        torch.cuda.synchronize()
+        assert torch.equal(hinted.count, plain.count) and torch.equal(hinted.cap_hit, plain.cap_hit)
+        s_all = O.attention_scores(_np(w.q[step]), K64)
+        for b in range(cfg.batch):
+            for h in range(cfg.n_q_heads):
+                n = int(hinted.count[b, h])
+                gidx = hinted.idx[b, h, :n].cpu().numpy()
+                assert np.array_equal(gidx, plain.idx[b, h, :n].cpu().numpy()), (step, b, h)
+                s = s_all[b, h]
+                _, lse = O.dense_softmax(s)
+                exact = check_delta_choice(gidx, n, s, float(lse), cfg.budget, cfg.delta_star,
+                                           cap_hit=int(hinted.cap_hit[b, h]))
+                S = O.topn_select(s, n) if exact else gidx
+                o_ref, _ = O.sparse_attention(s, V64[b, h], S)
+                d_ref, _ = O.dropped_mass(s, S)
+                assert np.max(np.abs(_np(hinted.out[b, h]) - o_ref)) <= OUT_TOL, (step, b, h)
+                assert abs(hinted.delta[b, h].item() - d_ref) <= DELTA_TOL
+
+
 def _small_cis(dev, batch=1, heads=8, ctx=4096, steps=8):
     cfg = CONFIGS["llama2_cis_8k"].replace(batch=batch, n_q_heads=heads, n_kv_heads=heads,
                                            ctx_len=ctx, budget=256, steps=steps)
