@@ -163,8 +163,11 @@ int prhs_cis_reuse(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anc
  * (fp32 [B, H_q, idx_cap] in idx order, as prhs_select_topk writes it), else
  * gathered from `scores` when that is non-NULL (the scores of the same step
  * from prhs_score); otherwise the K rows at S are gathered and scored (q and
- * k must then be non-NULL). The set is split over workgroups and the partial
- * (max, sum, output) triples are merged exactly.
+ * k must then be non-NULL). With >= 128 (b, h) heads, or idx_cap <= 256, one
+ * workgroup attends over a head's whole set (idx_cap <= 8192); otherwise the
+ * set is split over workgroups and the partial (max, sum, output) triples are
+ * merged exactly. Either way the result is the same up to the order of the
+ * fp32 sums.
  * Indices outside [0, t) are skipped; counts are clamped to [0, idx_cap]; an
  * empty set gives out = 0, lse_sel = -inf.
  * Fused dropped mass: when lse_all and delta are non-NULL,

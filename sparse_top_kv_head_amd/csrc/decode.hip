@@ -2,16 +2,23 @@
 // via Pre-hoc Sparsity for Long-Context Inference": Abstract and the Table V
 // caption's fused sparse-attention kernel; Table I tau(.) / delta(.)).
 //
-// Split-budget decode: the selected list of a head is cut into splits of
-// kDecodeRows entries, one 256-thread workgroup each, so even a few heads fill
-// the chip. A workgroup reads its entries' scores (compact from the selection,
-// gathered from the score scan, or recomputed from gathered K rows on steps
-// without a scan), requests all of its V rows with 16-byte lane loads (LPR
-// lanes per row, up to 16 rows in flight per lane) while it turns the scores
-// into weights, and accumulates weight * v in fp32. Each split leaves a
-// partial (max, sum, output) triple; the merge kernel combines them exactly
-// as the online softmax does and, when the dense log-sum-exp is given, writes
-// the dropped mass delta and the retained mass tau of the set.
+// Two shapes of the same computation:
+//
+// Split-budget decode (few heads): the selected list of a head is cut into
+// splits of kDecodeRows entries, one 256-thread workgroup each, so even a few
+// heads fill the chip. A workgroup reads its entries' scores (compact from the
+// selection, gathered from the score scan, or recomputed from gathered K rows
+// on steps without a scan), requests its first V rows with 16-byte lane loads
+// (LPR lanes per row, 8 rows in flight per lane) while it turns the scores into
+// weights, and accumulates weight * v in fp32. Each split leaves a partial
+// (max, sum, output) triple; the merge kernel combines them exactly as the
+// online softmax does and, when the dense log-sum-exp is given, writes the
+// dropped mass delta and the retained mass tau of the set.
+//
+// One workgroup per head (decode_head_kernel), when the heads alone fill the
+// chip or a set fits one split: the same sources and outputs without partials
+// or a merge launch; in its dilation modes it also builds the CIS-dilated set
+// itself.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
