@@ -77,9 +77,12 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 
+// Every control used with this helper permutes lanes inside a 16-lane row, so
+// each lane has a source lane; bound_ctrl only lets the compiler fold the move
+// into the consuming VALU instruction (v_add_f32_dpp and the like).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over aligned groups of LPR consecutive lanes; every lane of the group

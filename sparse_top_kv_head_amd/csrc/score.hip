@@ -20,68 +20,74 @@ constexpr int kScoreThreads = 256;
 
 // The G partial dot products of a 16-lane row group (lane c holds its slice's
 // share of every head) reduced and scattered: exchanges between lanes c and
-// 15 - c, then c and 7 - c, then within quads, each halving the heads a lane
-// carries, so that every lane ends with the full sum of one head, head_of(c).
-// 5 DPP additions for G = 4 and 8 for G = 8, against 4 G for separate sums.
+// 15 - c, then c and 7 - c, then c and c ^ 2, each halving the heads a lane
+// carries, until every lane holds one head's sum over the lanes it met; the
+// lanes of that head then finish with plain exchanges. Every lane ends with
+// the full sum of head rs16_head(c) = c / (16 / G). 5 DPP additions for
+// G = 4 and 8 for G = 8, against 4 G for separate sums.
 template <int G>
 __device__ __forceinline__ int rs16_head(int c) {
-  if constexpr (G == 1) return 0;
-  else if constexpr (G == 2) return c < 8 ? 0 : 1;
-  else if constexpr (G == 4) return (c < 8 ? 0 : 2) + ((c & 7) < 4 ? 0 : 1);
-  else return (c < 8 ? 0 : 4) + ((c & 7) < 4 ? 0 : 2) + ((c & 2) ? 1 : 0);
+  return G == 1 ? 0 : c / (16 / G);
 }
 
-// acc[] must come from the query heads in lane order: lanes c >= 8 take the
-// two halves of the head list swapped (rs16_qorder), so that every lane keeps
-// acc[0 : G/2) and sends acc[G/2 : G) in the first exchange.
+// The query head in acc[j] of lane c. Each exchange keeps the first half of
+// a lane's heads and sends the second half, with no selects, when the heads
+// run in this order: XOR-ing the group index of c with
+// tau = (0, 1, 3, 2, 7, 6, 4, 5) pairs head j of one lane with head j + G/2 of
+// its 15 - c partner (group index ^ (G - 1)), head j with head j + G/4 of its
+// 7 - c partner (^ (G/2 - 1)), and head 0 with head 1 of its c ^ 2 partner
+// (^ 1).
 template <int G>
 __device__ __forceinline__ int rs16_qorder(int j, int c) {
-  return (G > 1 && c >= 8) ? (j + G / 2) % G : j;
+  constexpr int kTau[8] = {0, 1, 3, 2, 7, 6, 4, 5};
+  return G == 1 ? 0 : (rs16_head<G>(c) ^ kTau[j]);
 }
 
 template <int G>
-__device__ __forceinline__ float rs16(const float (&acc)[G], int c) {
+__device__ __forceinline__ float rs16(const float (&acc)[G]) {
   if constexpr (G == 1) {
     return group_sum<16>(acc[0]);
   } else {
-    // exchange with lane 15 - c: the low half keeps the first G/2 heads
     constexpr int H1 = G / 2;
     float k1[H1];
 #pragma unroll
     for (int i = 0; i < H1; ++i) k1[i] = acc[i] + dpp<kDppRowMirror>(acc[H1 + i]);
+    float x;
     if constexpr (G == 2) {
-      float x = k1[0];
+      x = k1[0];
       x += dpp<kDppRowHalfMirror>(x);
       x += dpp<kDppXor2>(x);
-      x += dpp<kDppXor1>(x);
-      return x;
     } else {
-      // exchange with lane 7 - c inside each half
       constexpr int H2 = H1 / 2;
       float k2[H2];
-      const bool lo2 = (c & 7) < 4;
 #pragma unroll
-      for (int i = 0; i < H2; ++i) {
-        const float keep = lo2 ? k1[i] : k1[H2 + i];
-        const float send = lo2 ? k1[H2 + i] : k1[i];
-        k2[i] = keep + dpp<kDppRowHalfMirror>(send);
-      }
-      float x;
-      if constexpr (G == 4) {
-        x = k2[0];
-        x += dpp<kDppXor2>(x);
-      } else {
-        // G == 8: exchange with lane c ^ 2
-        const bool lo3 = (c & 2) == 0;
-        const float keep = lo3 ? k2[0] : k2[1];
-        const float send = lo3 ? k2[1] : k2[0];
-        x = keep + dpp<kDppXor2>(send);
-      }
-      x += dpp<kDppXor1>(x);
-      return x;
+      for (int i = 0; i < H2; ++i) k2[i] = k1[i] + dpp<kDppRowHalfMirror>(k1[H2 + i]);
+      x = k2[0];
+      if constexpr (G == 4) x += dpp<kDppXor2>(x);
+      else x += dpp<kDppXor2>(k2[1]);
     }
+    x += dpp<kDppXor1>(x);
+    return x;
   }
 }
+// dot16 from a zero accumulator. For fp16 the first pair goes through the
+// three-operand v_dot2_f32_f16 with an inline-constant 0, which the compiler
+// would otherwise form as a register clear plus the two-operand v_dot2c.
+__device__ __forceinline__ float dot16_zero(const uint4 a, const uint4 b, float /*tag*/) {
+  return dot16(a, b, 0.f, 0.f);
+}
+
+__device__ __forceinline__ float dot16_zero(const uint4 a, const uint4 b, __half /*tag*/) {
+  const half2_t* x = reinterpret_cast<const half2_t*>(&a);
+  const half2_t* y = reinterpret_cast<const half2_t*>(&b);
+  float acc;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(acc) : "v"(x[0]), "v"(y[0]));
+  acc = __builtin_amdgcn_fdot2(x[1], y[1], acc, false);
+  acc = __builtin_amdgcn_fdot2(x[2], y[2], acc, false);
+  acc = __builtin_amdgcn_fdot2(x[3], y[3], acc, false);
+  return acc;
+}
+
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
 // With `active` (per query head), a workgroup whose group has no active head
@@ -130,6 +136,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
     if (!any) return;
   }
 
+  // The thresholds are read now, so that their latency hides behind the K
+  // loads instead of stalling the workgroup's tail.
+  float th[G] = {};
+  if (theta != nullptr) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) th[j] = theta[b * Hq + h0 + j];
+  }
+
   uint4 qv[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -164,8 +178,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
       float acc[G];
       if constexpr (LPR == 16) {
 #pragma unroll
-        for (int j = 0; j < G; ++j) acc[j] = dot16(kv[u], qv[j], 0.f, T());
-        const float val = rs16<G>(acc, c);
+        for (int j = 0; j < G; ++j) acc[j] = dot16_zero(kv[u], qv[j], T());
+        float val = rs16<G>(acc);
+        // The last exchange must run on every lane (its DPP source lanes
+        // are the other lanes of the head): keep it ahead of the branch.
+        asm volatile("" : "+v"(val));
         // lanes holding the same head carry the same sum: one writes it
         if ((c & (16 / G - 1)) == 0)
           sc[rs16_head<G>(c)][wrow0 + it * U * RPW + u * RPW + rr] = val * scale;
@@ -183,25 +200,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
 
   const int base_row = chunk * CHUNK;
   const int nrows = min(CHUNK, t - base_row);
+  // write-back: one float4 of one head's row per thread and pass
+  constexpr int V4 = CHUNK / 4;
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
+  for (int e = threadIdx.x; e < G * V4; e += kScoreThreads) {
+    const int j = e / V4;
+    const int i = (e - j * V4) * 4;
     float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
-    for (int i = threadIdx.x * 4; i < nrows; i += kScoreThreads * 4) {
-      if (i + 4 <= nrows) {
-        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
-      } else {
-        for (int e = 0; i + e < nrows; ++e) dst[i + e] = sc[j][i + e];
-      }
+    if (i + 4 <= nrows) {
+      *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
+    } else {
+      for (int x = i; x < nrows; ++x) dst[x] = sc[j][x];
     }
   }
   if (theta != nullptr) {
     // index-ordered compaction of the keys >= theta: ballot per wave, then
     // the waves' counts give each wave its offset in the chunk's slot range
     uint64_t hits[G];
-    float th[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      th[j] = theta[b * Hq + h0 + j];
       const int r = w * kWave + lane;
       const bool hit = __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
       hits[j] = __ballot(hit);
