@@ -658,7 +658,7 @@ def main():
         "config": {"workload": f"{cfg.name}: Mistral-7B-shaped GQA decode layer, B={B}, H_q={Hq}, "
                                f"H_kv={Hkv}, d={d}, t={t}, top-N={N}, fp16 K/V",
                    "batch": B, "ctx_len": t, "budget": N, "kv_copies_rotated": a.rotate},
-        "roofline": {"bound": "hbm", "kernel": "score_scan_kernel<__half,128,4,256,16> (K scan GEMV, timed in its own loop)",
+        "roofline": {"bound": "hbm", "kernel": "score_scan_mfma_kernel<4> (K scan on the matrix cores, timed in its own loop)",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_bytes_per_launch": traffic_bytes,

@@ -4,14 +4,21 @@
 // Inference", Table I: query q, keys K, per-head dimension d, attention weight A).
 //
 // HBM-bound GEMV: every K row is read exactly once, by one wave, with 16-byte
-// loads, and is scored against all G query heads of its group in registers.
-// Layout on the wave: LPR lanes cover one row (LPR = 16 for d=128 fp16), so
-// one load instruction covers RPW = 64/LPR rows; the LPR partial dot products
-// of a row are summed with DPP row operations. Scores are staged in LDS and
-// written back coalesced; the chunk's softmax partials come from the staged
-// values.
+// loads, and is scored against all G query heads of its group. Layout on the
+// wave: LPR lanes cover one row (LPR = 16 for d=128 fp16), so one load
+// instruction covers RPW = 64/LPR rows. Scores are staged in LDS and written
+// back coalesced; the chunk's softmax partials come from the staged values.
+//
+// Two kernels. For fp16 rows of d = 128 (every LLaMA/Mistral-shaped layer),
+// score_scan_mfma_kernel: each wave passes its loaded rows, 16 at a time,
+// through a 4 KiB LDS tile into the operand layout of v_mfma_f32_16x16x32_f16
+// and scores them on the matrix cores. Otherwise (fp32, d = 64)
+// score_scan_kernel: the LPR partial dot products of a row are summed with
+// DPP row operations.
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
+
+#include <type_traits>
 
 namespace prhs {
 namespace {
@@ -89,6 +96,79 @@ __device__ __forceinline__ float dot16_zero(const uint4 a, const uint4 b, __half
 }
 
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
+
+// The chunk's outputs from the staged scores sc[j][0:CHUNK) of its G heads:
+// the scores themselves, the keys >= theta as (score bits, index) candidates
+// (index-ordered: a ballot per wave, then the waves' counts give each wave its
+// offset), and the (max, sum-of-exp) partial of each head. Contains one
+// barrier; the caller has synchronised after filling sc.
+template <int G, int NW, int CHUNK, int PITCH>
+__device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t (&wcnt)[G][NW],
+                                          const float (&th)[G], float* __restrict__ scores,
+                                          float2* __restrict__ part, uint2* __restrict__ cand,
+                                          uint32_t* __restrict__ cand_cnt, const bool use_theta,
+                                          int b, int Hq, int h0, int t, int ld, int nchunks,
+                                          int chunk, int w, int lane) {
+  const int base_row = chunk * CHUNK;
+  const int nrows = min(CHUNK, t - base_row);
+  // write-back: one float4 of one head's row per thread and pass
+  constexpr int V4 = CHUNK / 4;
+#pragma unroll
+  for (int e = threadIdx.x; e < G * V4; e += kScoreThreads) {
+    const int j = e / V4;
+    const int i = (e - j * V4) * 4;
+    float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
+    if (i + 4 <= nrows) {
+      *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
+    } else {
+      for (int x = i; x < nrows; ++x) dst[x] = sc[j][x];
+    }
+  }
+  if (use_theta) {
+    uint64_t hits[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int r = w * kWave + lane;
+      const bool hit = __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
+      hits[j] = __ballot(hit);
+      if (lane == 0) wcnt[j][w] = (uint32_t)__popcll(hits[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
+      if (!__builtin_isfinite(th[j])) {
+        if (threadIdx.x == 0) cand_cnt[hc] = kNoCand;
+        continue;
+      }
+      uint32_t base = 0, total = 0;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        const uint32_t c = wcnt[j][u];
+        base += u < w ? c : 0u;
+        total += c;
+      }
+      const int r = w * kWave + lane;
+      if ((hits[j] >> lane) & 1ull) {
+        const uint32_t pos = base + (uint32_t)__popcll(hits[j] & ((1ull << lane) - 1ull));
+        cand[hc * CHUNK + pos] = make_uint2(__float_as_uint(sc[j][r]), (uint32_t)(base_row + r));
+      }
+      if (threadIdx.x == 0) cand_cnt[hc] = total;
+    }
+  }
+  if (part != nullptr) {
+    for (int j = w; j < G; j += NW) {
+      float m = -INFINITY;
+      for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
+      m = wave_max(m);
+      float l = 0.f;
+      if (m != -INFINITY)
+        for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
+      l = wave_sum(l);
+      if (lane == 0) part[(size_t)(b * Hq + h0 + j) * nchunks + chunk] = make_float2(m, l);
+    }
+  }
+}
 
 // With `active` (per query head), a workgroup whose group has no active head
 // does nothing. With `theta` (a per-head score threshold), the chunk's keys whose score is
@@ -198,67 +278,125 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   }
   __syncthreads();
 
-  const int base_row = chunk * CHUNK;
-  const int nrows = min(CHUNK, t - base_row);
-  // write-back: one float4 of one head's row per thread and pass
-  constexpr int V4 = CHUNK / 4;
+  scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b, Hq, h0, t, ld,
+                                 nchunks, chunk, w, lane);
+}
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Matrix-core scan of fp16 rows with d = 128; same outputs and grid as
+// score_scan_kernel (one 256-key chunk per workgroup, 64 rows per wave).
+//
+// Operands: a 16x16x32 product takes from lane l the 8 consecutive
+// k-elements 8 (l / 16) .. + 7 of A's row l % 16 and of B's column l % 16, and
+// returns D[4 (l / 16) + r][l % 16] in element r. A holds the query heads
+// (rows 0 .. G-1, the rest zero) and B the keys: key n of a 16-key group in
+// column n, feature block j (features 32 j .. 32 j + 31, the 16-byte segments
+// 4 j .. 4 j + 3) in the j-th of four products.
+//
+// Transpose: the coalesced loads give lane l segment l % 16 of key
+// 4 (u % 4) + l / 16 of the group. Each wave moves its 16 keys through its
+// own 4 KiB LDS tile, segment s of key n at 16-byte slot 16 n + (s ^ n), so
+// the 16 lanes of one row write and the 16 lanes of one operand read each hit
+// 16 distinct slots of a 256-byte bank row (no bank conflicts).
+//
+// Rows at or past t (last chunk only) load row t - 1 instead, so every load
+// is in bounds and branch-free; their scores are never written.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
+    const __half* __restrict__ q, const __half* __restrict__ k, float* __restrict__ scores,
+    float2* __restrict__ part, const float* __restrict__ theta, uint2* __restrict__ cand,
+    uint32_t* __restrict__ cand_cnt, const int* __restrict__ active, int Hq, int Hkv, int t,
+    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, float scale) {
+  constexpr int D = 128;
+  constexpr int E = 8;
+  constexpr int NW = kScoreThreads / kWave;
+  constexpr int CHUNK = kScoreChunk;
+  constexpr int RW = CHUNK / NW;  // rows per wave and chunk
+  constexpr int U = RW / 4;       // 16-byte loads per lane and chunk
+  constexpr int PITCH = CHUNK + 4;
+  constexpr int NR = G < 4 ? G : 4;  // heads per lane in the product
+  static_assert(U == 16, "four 16-key groups per wave and chunk");
+  __shared__ __align__(16) float sc[G][PITCH];
+  __shared__ uint32_t wcnt[G][NW];
+  __shared__ __align__(16) uint4 xt[NW][256];
+
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv;
+  const int g = unit - b * Hkv;
+  const int h0 = g * (Hq / Hkv) + g_off;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c = lane & 15;   // segment of the loaded row; key of the operand
+  const int rr = lane >> 4;  // row of the load; k-block of the operand
+  if (active != nullptr) {
+    bool any = false;
 #pragma unroll
-  for (int e = threadIdx.x; e < G * V4; e += kScoreThreads) {
-    const int j = e / V4;
-    const int i = (e - j * V4) * 4;
-    float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
-    if (i + 4 <= nrows) {
-      *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
-    } else {
-      for (int x = i; x < nrows; ++x) dst[x] = sc[j][x];
-    }
+    for (int j = 0; j < G; ++j) any |= active[b * Hq + h0 + j] != 0;
+    if (!any) return;
   }
+  float th[G] = {};
   if (theta != nullptr) {
-    // index-ordered compaction of the keys >= theta: ballot per wave, then
-    // the waves' counts give each wave its offset in the chunk's slot range
-    uint64_t hits[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int r = w * kWave + lane;
-      const bool hit = __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
-      hits[j] = __ballot(hit);
-      if (lane == 0) wcnt[j][w] = (uint32_t)__popcll(hits[j]);
-    }
-    __syncthreads();
+    for (int j = 0; j < G; ++j) th[j] = theta[b * Hq + h0 + j];
+  }
+
+  half8_t qa[4];
+  {
+    const int m = c < G ? c : G - 1;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
-      if (!__builtin_isfinite(th[j])) {
-        if (threadIdx.x == 0) cand_cnt[hc] = kNoCand;
-        continue;
-      }
-      uint32_t base = 0, total = 0;
-#pragma unroll
-      for (int u = 0; u < NW; ++u) {
-        const uint32_t c = wcnt[j][u];
-        base += u < w ? c : 0u;
-        total += c;
-      }
-      const int r = w * kWave + lane;
-      if ((hits[j] >> lane) & 1ull) {
-        const uint32_t pos = base + (uint32_t)__popcll(hits[j] & ((1ull << lane) - 1ull));
-        cand[hc * CHUNK + pos] = make_uint2(__float_as_uint(sc[j][r]), (uint32_t)(base_row + r));
-      }
-      if (threadIdx.x == 0) cand_cnt[hc] = total;
+    for (int j = 0; j < 4; ++j) {
+      uint4 v = load16(q + ((size_t)(b * Hq + h0 + m) * D + (4 * j + rr) * E));
+      if (c >= G) v = make_uint4(0, 0, 0, 0);
+      qa[j] = __builtin_bit_cast(half8_t, v);
     }
   }
-  if (part != nullptr) {
-    for (int j = w; j < G; j += NW) {
-      float m = -INFINITY;
-      for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
-      m = wave_max(m);
-      float l = 0.f;
-      if (m != -INFINITY)
-        for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
-      l = wave_sum(l);
-      if (lane == 0) part[(size_t)(b * Hq + h0 + j) * nchunks + chunk] = make_float2(m, l);
+
+  // The unit's rows span less than 4 GiB (checked by the launcher), so a
+  // load address is the unit's base plus a 32-bit byte offset.
+  const char* kunit = reinterpret_cast<const char*>(k + b * sb + g * sh);
+  const uint32_t rb = (uint32_t)st * (uint32_t)sizeof(__half);
+  const int chunk = blockIdx.x;
+  const int row0 = chunk * CHUNK + w * RW + rr;
+  uint4 kv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = min(row0 + 4 * u, t - 1);
+    kv[u] = load16_stream(kunit + ((uint32_t)c * 16u + (uint32_t)r * rb));
+  }
+
+  uint4* tile = xt[w];
+#pragma unroll
+  for (int a = 0; a < U / 4; ++a) {
+#pragma unroll
+    for (int mq = 0; mq < 4; ++mq) {
+      const int nk = 4 * mq + rr;
+      tile[nk * 16 + (c ^ nk)] = kv[4 * a + mq];
+    }
+    // The tile is shared by the lanes of this wave only, and LDS operations
+    // of one wave complete in order: a wave-scope fence, which only orders
+    // the compiler's accesses, is all the exchange needs.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half8_t bk = __builtin_bit_cast(half8_t, tile[c * 16 + ((4 * j + rr) ^ c)]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], bk, acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane l holds heads 4 (l / 16) + r of key l % 16
+    if (rr < (G + 3) / 4) {
+      const int row = w * RW + 16 * a + c;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) sc[4 * rr + r][row] = acc[r] * scale;
     }
   }
+  __syncthreads();
+  scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b,
+                                 Hq, h0, t, ld, nchunks, chunk, w, lane);
 }
 
 // Merge the per-chunk partials of each head into its dense log-sum-exp: one
@@ -282,8 +420,21 @@ template <typename T, int D, int G>
 void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores, float2* part,
                  const ScanCand& cd, int g_off, hipStream_t stream) {
   const int nchunks = score_nchunks(d);
-  dim3 grid(nchunks, d.batch * d.n_kv_heads);
+  const int units = d.batch * d.n_kv_heads;
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
+  // the matrix-core kernel addresses a unit's rows with 32-bit byte offsets
+  const bool offsets32 = (unsigned long long)d.ctx_len * (unsigned long long)d.kv_stride_t *
+                             sizeof(T) < (1ull << 32);
+  if (std::is_same<T, __half>::value && D == 128 && offsets32) {
+    dim3 grid(nchunks, units);
+    hipLaunchKernelGGL((score_scan_mfma_kernel<G>), grid, dim3(kScoreThreads), 0, stream,
+                       static_cast<const __half*>(q), static_cast<const __half*>(k), scores, part,
+                       cd.theta, cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads,
+                       d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
+                       (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
+    return;
+  }
+  dim3 grid(nchunks, units);
   hipLaunchKernelGGL((score_scan_kernel<T, D, G>), grid, dim3(kScoreThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), scores, part, cd.theta,
                      cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
