@@ -207,9 +207,9 @@ int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t an
  * `stream` (Fig. 4: the query whose critical set is computed exactly; the
  * Abstract: selection ahead of attention with the dropped mass controlled).
  *
- * Results are those of the three calls in sequence: scores, lse_all, idx,
- * count, cap_hit (nullable), out, lse_sel, delta and tau (nullable; tau
- * needs delta). The dense log-sum-exp is merged inside the selection kernel
+ * Results are those of the three calls in sequence: scores (but see theta
+ * below), lse_all, idx, count, cap_hit (nullable), out, lse_sel, delta and
+ * tau (nullable; tau needs delta). The dense log-sum-exp is merged inside the selection kernel
  * from the scan's per-chunk partials, so no separate merge runs. Argument
  * rules are the union of the three calls' rules.
  *
@@ -227,6 +227,11 @@ int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t an
  * means no hint. On return theta holds a hint for the next step of the same
  * heads: this step's boundary score less a margin (adjacent decode queries
  * are highly similar: Fig. 2, Fig. 10). Initialise it to NaN.
+ * With fp16 rows of head_dim 128 (and ctx_len * kv_stride_t * 2 < 2^32), a
+ * head with a finite hint gets no scores row from the scan: its row is left
+ * as it was, unless its hinted keys miss the answer, in which case the
+ * selection recomputes the row (bit-identical to the scan's) before its full
+ * search. Heads without a hint, and every other shape, get their rows.
  * ws: at least prhs_workspace_bytes(dims, PRHS_OP_ANCHOR_STEP, idx_cap) bytes.
  */
 int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,

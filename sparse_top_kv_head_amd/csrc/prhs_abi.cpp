@@ -431,6 +431,9 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     cd.theta = theta;
     cd.cand = reinterpret_cast<uint2*>(w + L.cand);
     cd.cand_cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
+    // hinted heads get no score row from a matrix-core scan; the selection
+    // recomputes the row of a head whose candidates miss
+    cd.skip_hinted = prhs::scan_uses_mfma(*dims);
   }
   // With enough heads (or a one-split budget) each head's select workgroup
   // also decodes its head: no split partials and no merge launch.
@@ -452,6 +455,17 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     a.cand = cd.cand;
     a.cand_cnt = cd.cand_cnt;
     a.theta_out = hint ? theta : nullptr;
+    a.kv_sb = dims->kv_stride_b;
+    a.kv_sh = dims->kv_stride_h;
+    a.kv_st = dims->kv_stride_t;
+    a.hq = dims->n_q_heads;
+    a.hkv = dims->n_kv_heads;
+    if (cd.skip_hinted) {
+      a.rescore_q = q;
+      a.rescore_k = k;
+      a.rescore_row = scores;
+      a.rescore_scale = (float)(1.0 / std::sqrt((double)dims->head_dim));
+    }
     if (fuse) {
       a.v = v;
       a.kv_sb = dims->kv_stride_b;

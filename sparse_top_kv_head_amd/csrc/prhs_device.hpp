@@ -69,6 +69,85 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core scoring of fp16 key rows with d = 128 (the scan, and the
+// selection's recomputation of a row the scan did not write; both use these
+// helpers, so their scores are bit-identical).
+//
+// A 16x16x32 product takes from lane l the 8 consecutive k-elements
+// 8 (l / 16) .. + 7 of A's row l % 16 and of B's column l % 16, and returns
+// D[4 (l / 16) + r][l % 16] in element r. A holds up to 16 query heads (one
+// per row, the rest zero) and B 16 keys (key n in column n); feature block j
+// (features 32 j .. 32 j + 31, i.e. 16-byte segments 4 j .. 4 j + 3) is the
+// j-th of four chained products.
+// ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// The A operands of the nq (<= 16) consecutive query rows starting at q0:
+// lane l holds head min(l % 16, nq - 1) (zeroed when l % 16 >= nq), segment
+// 4 j + l / 16 of feature block j.
+__device__ __forceinline__ void mfma_query_operand(const __half* q0, int nq, int lane,
+                                                   half8_t (&qa)[4]) {
+  const int c = lane & 15;
+  const int rr = lane >> 4;
+  const int m = c < nq ? c : nq - 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 v = *reinterpret_cast<const uint4*>(q0 + (size_t)m * 128 + (4 * j + rr) * 8);
+    if (c >= nq) v = make_uint4(0, 0, 0, 0);
+    qa[j] = __builtin_bit_cast(half8_t, v);
+  }
+}
+
+// Scores of one 16-key group against the heads of qa. On entry lane l holds,
+// in k[mq], segment l % 16 of key 4 mq + l / 16 (the coalesced load layout:
+// one load instruction covers four whole rows). The keys pass through the
+// wave's own 4 KiB LDS tile, segment s of key n at 16-byte slot 16 n + (s ^ n),
+// so the 16 lanes of one row write and the 16 lanes of one operand read each
+// hit 16 distinct slots of a 256-byte bank row. Returns D (heads x keys) in
+// the product's layout, unscaled.
+__device__ __forceinline__ float4_t mfma_score16(const uint4 k0, const uint4 k1, const uint4 k2,
+                                                 const uint4 k3, const half8_t (&qa)[4],
+                                                 uint4* tile, int lane) {
+  const int c = lane & 15;
+  const int rr = lane >> 4;
+  const uint4 kk[4] = {k0, k1, k2, k3};
+#pragma unroll
+  for (int mq = 0; mq < 4; ++mq) {
+    const int nk = 4 * mq + rr;
+    tile[nk * 16 + (c ^ nk)] = kk[mq];
+  }
+  // The tile is shared by the lanes of this wave only, and LDS operations of
+  // one wave complete in order: a wave-scope fence, which only orders the
+  // compiler's accesses, is all the exchange needs.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half8_t bk = __builtin_bit_cast(half8_t, tile[c * 16 + ((4 * j + rr) ^ c)]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], bk, acc, 0, 0, 0);
+  }
+  // the next group may overwrite the tile only after these reads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  return acc;
+}
+
+// The query sub-group of head h_local within a GQA group of G heads, as the
+// scan launches them: power-of-two sub-groups of 8, 4, 2 and 1 heads in
+// order. Returns the sub-group's first head (within the group) and size.
+__host__ __device__ inline void scan_subgroup(int G, int h_local, int& off, int& sub) {
+  off = 0;
+  for (;;) {
+    const int rest = G - off;
+    sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
+    if (h_local < off + sub) return;
+    off += sub;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane data movement
 // ---------------------------------------------------------------------------
 // DPP controls (GFX9 encoding).

@@ -33,7 +33,17 @@ struct ScanCand {
   uint2* cand = nullptr;
   uint32_t* cand_cnt = nullptr;
   const int* active = nullptr;   // per query head; a KV group with no active head is skipped
+  // Matrix-core scan only: no score row for heads with a finite theta (the
+  // selection recomputes it when the candidates miss).
+  bool skip_hinted = false;
 };
+
+// The scan scores on the matrix cores: fp16 rows of 128, and a unit's rows
+// addressable with 32-bit byte offsets.
+inline bool scan_uses_mfma(const prhs_dims& d) {
+  return d.dtype == PRHS_F16 && d.head_dim == 128 &&
+         (unsigned long long)d.ctx_len * (unsigned long long)d.kv_stride_t * 2ull < (1ull << 32);
+}
 
 // Writes scores; with ws, also the per-chunk (max, sum) partials of the dense
 // softmax; with lse_all (needs ws), also merges them into lse_all.
@@ -58,6 +68,13 @@ struct SelectArgs {
   const uint2* cand = nullptr;    // scan candidates (TOPN)
   const uint32_t* cand_cnt = nullptr;
   float* theta_out = nullptr;     // next-step threshold hint (TOPN)
+  // Score rows skipped by a hinted matrix-core scan: when the candidates of
+  // such a head miss, its row is recomputed from q and K (strides kv_*,
+  // heads hq / hkv) into rescore_row before the full search.
+  const void* rescore_q = nullptr;
+  const void* rescore_k = nullptr;
+  float* rescore_row = nullptr;
+  float rescore_scale = 0.f;
   const int* active = nullptr;    // per head; inactive heads are left untouched
   // Fused decode (TOPN with scan partials, fp16 rows of 128): when v is given,
   // each head's workgroup attends over its own selection and writes out,

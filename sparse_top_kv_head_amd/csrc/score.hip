@@ -18,8 +18,6 @@
 #include "prhs_device.hpp"
 #include "prhs_launch.hpp"
 
-#include <type_traits>
-
 namespace prhs {
 namespace {
 
@@ -98,7 +96,8 @@ __device__ __forceinline__ float dot16_zero(const uint4 a, const uint4 b, __half
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
 // The chunk's outputs from the staged scores sc[j][0:CHUNK) of its G heads:
-// the scores themselves, the keys >= theta as (score bits, index) candidates
+// the scores themselves (not for heads with a finite theta under
+// skip_hinted), the keys >= theta as (score bits, index) candidates
 // (index-ordered: a ballot per wave, then the waves' counts give each wave its
 // offset), and the (max, sum-of-exp) partial of each head. Contains one
 // barrier; the caller has synchronised after filling sc.
@@ -108,7 +107,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
                                           float2* __restrict__ part, uint2* __restrict__ cand,
                                           uint32_t* __restrict__ cand_cnt, const bool use_theta,
                                           int b, int Hq, int h0, int t, int ld, int nchunks,
-                                          int chunk, int w, int lane) {
+                                          int chunk, int w, int lane, bool skip_hinted = false) {
   const int base_row = chunk * CHUNK;
   const int nrows = min(CHUNK, t - base_row);
   // write-back: one float4 of one head's row per thread and pass
@@ -117,6 +116,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
   for (int e = threadIdx.x; e < G * V4; e += kScoreThreads) {
     const int j = e / V4;
     const int i = (e - j * V4) * 4;
+    if (skip_hinted && __builtin_isfinite(th[j])) continue;
     float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
     if (i + 4 <= nrows) {
       *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
@@ -282,35 +282,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
                                  nchunks, chunk, w, lane);
 }
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
 // Matrix-core scan of fp16 rows with d = 128; same outputs and grid as
-// score_scan_kernel (one 256-key chunk per workgroup, 64 rows per wave).
-//
-// Operands: a 16x16x32 product takes from lane l the 8 consecutive
-// k-elements 8 (l / 16) .. + 7 of A's row l % 16 and of B's column l % 16, and
-// returns D[4 (l / 16) + r][l % 16] in element r. A holds the query heads
-// (rows 0 .. G-1, the rest zero) and B the keys: key n of a 16-key group in
-// column n, feature block j (features 32 j .. 32 j + 31, the 16-byte segments
-// 4 j .. 4 j + 3) in the j-th of four products.
-//
-// Transpose: the coalesced loads give lane l segment l % 16 of key
-// 4 (u % 4) + l / 16 of the group. Each wave moves its 16 keys through its
-// own 4 KiB LDS tile, segment s of key n at 16-byte slot 16 n + (s ^ n), so
-// the 16 lanes of one row write and the 16 lanes of one operand read each hit
-// 16 distinct slots of a 256-byte bank row (no bank conflicts).
-//
-// Rows at or past t (last chunk only) load row t - 1 instead, so every load
-// is in bounds and branch-free; their scores are never written.
+// score_scan_kernel (one 256-key chunk per workgroup, 64 rows per wave),
+// scored 16 keys at a time by mfma_score16 (query heads as the rows of A,
+// keys as the columns of B). Rows at or past t (last chunk only) load row
+// t - 1 instead, so every load is in bounds and branch-free; their scores are
+// never written. With skip_hinted, a head whose threshold is finite gets its
+// candidates but no score row (the selection recomputes the row with the same
+// helpers if the candidates do not hold its answer).
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
     const __half* __restrict__ q, const __half* __restrict__ k, float* __restrict__ scores,
     float2* __restrict__ part, const float* __restrict__ theta, uint2* __restrict__ cand,
     uint32_t* __restrict__ cand_cnt, const int* __restrict__ active, int Hq, int Hkv, int t,
-    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, float scale) {
+    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, float scale,
+    int skip_hinted) {
   constexpr int D = 128;
-  constexpr int E = 8;
   constexpr int NW = kScoreThreads / kWave;
   constexpr int CHUNK = kScoreChunk;
   constexpr int RW = CHUNK / NW;  // rows per wave and chunk
@@ -343,15 +330,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
   }
 
   half8_t qa[4];
-  {
-    const int m = c < G ? c : G - 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 v = load16(q + ((size_t)(b * Hq + h0 + m) * D + (4 * j + rr) * E));
-      if (c >= G) v = make_uint4(0, 0, 0, 0);
-      qa[j] = __builtin_bit_cast(half8_t, v);
-    }
-  }
+  mfma_query_operand(q + (size_t)(b * Hq + h0) * D, G, lane, qa);
 
   // The unit's rows span less than 4 GiB (checked by the launcher), so a
   // load address is the unit's base plus a 32-bit byte offset.
@@ -369,24 +348,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
   uint4* tile = xt[w];
 #pragma unroll
   for (int a = 0; a < U / 4; ++a) {
-#pragma unroll
-    for (int mq = 0; mq < 4; ++mq) {
-      const int nk = 4 * mq + rr;
-      tile[nk * 16 + (c ^ nk)] = kv[4 * a + mq];
-    }
-    // The tile is shared by the lanes of this wave only, and LDS operations
-    // of one wave complete in order: a wave-scope fence, which only orders
-    // the compiler's accesses, is all the exchange needs.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const half8_t bk = __builtin_bit_cast(half8_t, tile[c * 16 + ((4 * j + rr) ^ c)]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[j], bk, acc, 0, 0, 0);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float4_t acc = mfma_score16(kv[4 * a], kv[4 * a + 1], kv[4 * a + 2], kv[4 * a + 3], qa,
+                                      tile, lane);
     // lane l holds heads 4 (l / 16) + r of key l % 16
     if (rr < (G + 3) / 4) {
       const int row = w * RW + 16 * a + c;
@@ -396,7 +359,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
   }
   __syncthreads();
   scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b,
-                                 Hq, h0, t, ld, nchunks, chunk, w, lane);
+                                 Hq, h0, t, ld, nchunks, chunk, w, lane,
+                                 skip_hinted != 0 && theta != nullptr);
 }
 
 // Merge the per-chunk partials of each head into its dense log-sum-exp: one
@@ -422,16 +386,14 @@ void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores
   const int nchunks = score_nchunks(d);
   const int units = d.batch * d.n_kv_heads;
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
-  // the matrix-core kernel addresses a unit's rows with 32-bit byte offsets
-  const bool offsets32 = (unsigned long long)d.ctx_len * (unsigned long long)d.kv_stride_t *
-                             sizeof(T) < (1ull << 32);
-  if (std::is_same<T, __half>::value && D == 128 && offsets32) {
+  if (scan_uses_mfma(d)) {
     dim3 grid(nchunks, units);
     hipLaunchKernelGGL((score_scan_mfma_kernel<G>), grid, dim3(kScoreThreads), 0, stream,
                        static_cast<const __half*>(q), static_cast<const __half*>(k), scores, part,
                        cd.theta, cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads,
                        d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
-                       (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
+                       (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale,
+                       cd.skip_hinted ? 1 : 0);
     return;
   }
   dim3 grid(nchunks, units);

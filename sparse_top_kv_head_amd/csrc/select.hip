@@ -92,7 +92,9 @@ template <int NT, bool MASS>
 struct SelShared {
   uint32_t hist[kBins * kRep1];
   typename std::conditional<MASS, unsigned long long[kBins], char>::type mhist;
-  uint2 cand[kCandCap + kWave];   // (key, index) of the fast path; key only otherwise; + dummies
+  // (key, index) of the fast path; key only otherwise; + dummies. Also the
+  // waves' transpose tiles while a skipped score row is recomputed.
+  __align__(16) uint2 cand[kCandCap + kWave];
   uint32_t gt_bits[kMaxWords];
   uint32_t eq_bits[kMaxWords];
   uint32_t wtot[NT / kWave];
@@ -1063,6 +1065,60 @@ __device__ __forceinline__ void fused_decode(const SelectArgs& a, int head, int 
   }
 }
 
+// Recompute the score row of `head` that a hinted matrix-core scan skipped,
+// with the scan's own operands and helpers (the same query sub-group in the
+// rows of A, the same products and scaling), so the row is bit-identical to
+// the one the scan would have written. Wave w scores RG consecutive 16-key
+// groups per pass (4 RG loads in flight per lane) through its 4 KiB tile;
+// RG is kept small so that this rare path adds no registers to the kernel.
+template <int NT>
+__device__ __forceinline__ void rescore_row(const SelectArgs& a, int head, uint4* tiles) {
+  constexpr int NWV = NT / kWave;
+  constexpr int RG = 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int c = lane & 15;
+  const int rr = lane >> 4;
+  const int t = a.t;
+  const int b = head / a.hq;
+  const int h = head - b * a.hq;
+  const int G = a.hq / a.hkv;
+  const int g = h / G;
+  int off, sub;
+  scan_subgroup(G, h - g * G, off, sub);
+  const int m = h - g * G - off;  // the head's row of A
+  half8_t qa[4];
+  mfma_query_operand(static_cast<const __half*>(a.rescore_q) + (size_t)(b * a.hq + g * G + off) * 128,
+                     sub, lane, qa);
+  const char* kunit = reinterpret_cast<const char*>(static_cast<const __half*>(a.rescore_k) +
+                                                    b * a.kv_sb + g * a.kv_sh);
+  const uint32_t rb = (uint32_t)a.kv_st * 2u;
+  float* row = a.rescore_row + (size_t)head * a.ld;
+  uint4* tile = tiles + w * 256;
+  const int ngroups = (t + 15) / 16;
+  for (int g0 = RG * w; g0 < ngroups; g0 += RG * NWV) {
+    uint4 kv[4 * RG];
+#pragma unroll
+    for (int i = 0; i < RG; ++i)
+#pragma unroll
+      for (int mq = 0; mq < 4; ++mq) {
+        const int r = min((g0 + i) * 16 + 4 * mq + rr, t - 1);
+        kv[4 * i + mq] = load16_stream(kunit + ((uint32_t)c * 16u + (uint32_t)r * rb));
+      }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const float4_t acc = mfma_score16(kv[4 * i], kv[4 * i + 1], kv[4 * i + 2], kv[4 * i + 3], qa,
+                                        tile, lane);
+      const int key = (g0 + i) * 16 + c;
+      if (rr == (m >> 2) && key < t) {
+        const int e = m & 3;
+        const float v = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
+        row[key] = v * a.rescore_scale;
+      }
+    }
+  }
+}
+
 // Heads with a zero `active` flag (when given) are left untouched.
 // lse_all is read (DELTA) unless `part` is given: then the head's per-chunk
 // (max, sum) partials of the score scan are merged here, the result used and
@@ -1139,7 +1195,13 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       }
       // the candidates do not hold the answer: the full path, on keys loaded
       // now (inside this branch, so that the keys of the other branch are not
-      // live across the gather)
+      // live across the gather). A hinted head's row is not written by the
+      // scan and is recomputed first (the list's LDS serves as the tiles).
+      if (a.rescore_k != nullptr && a.cand_cnt[(size_t)head * a.nchunks] != kNoCand) {
+        __syncthreads();
+        rescore_row<NT>(a, head, reinterpret_cast<uint4*>(sh.cand));
+        __syncthreads();
+      }
       load_keys_raw<KPT>(K, row, t);
     }
   }

@@ -549,7 +549,9 @@ def test_anchor_step_graph_replay_matches_eager(batch):
     w = make_workload(cfg, device=dev)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
     other = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
-    names = ("scores", "lse_all", "idx", "count", "out", "lse_sel", "delta", "tau")
+    # scores are not compared: the captured step carries a finite threshold
+    # hint, and a hinted head whose candidates hold its answer gets no score row
+    names = ("lse_all", "idx", "count", "out", "lse_sel", "delta", "tau")
     eng.anchor_step(w.q[1], w.K, w.V, P.PRHS_TOPN, cfg.budget)
     torch.cuda.synchronize()
     ref = {n: getattr(eng, n).clone() for n in names}
@@ -573,7 +575,9 @@ def test_anchor_step_graph_replay_matches_eager(batch):
 @pytest.mark.parametrize("ctx", [32768, 4096])
 def test_anchor_step_hint_exact(ctx):
     """Steps with the carried hint, and with hints forced too high, too low and
-    absent, give the same indices, scores and outputs as steps without a hint."""
+    absent, give the same indices and outputs as steps without a hint. Where a
+    forced hint misses on every head, the selection recomputes each skipped
+    score row: the rows must be bit-identical to the scan's."""
     dev = _dev()
     from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
     cfg = CONFIGS["mistral_gqa_32k"].replace(batch=1, ctx_len=ctx, budget=min(2048, ctx // 8),
@@ -598,3 +602,8 @@ def test_anchor_step_hint_exact(ctx):
                     assert torch.equal(a[0, h, :c], b[0, h, :c]), (step, h)
             else:
                 assert torch.equal(a, b), (step, n)
+        # a hint of 1e30 lists no key; one of -1e30 lists every key, more
+        # than the selection's 8192-entry list beyond 8K keys
+        if step == 2 or (step == 3 and cfg.ctx_len > 8192):
+            t = cfg.ctx_len
+            assert torch.equal(hinted.scores[..., :t], plain.scores[..., :t]), step
