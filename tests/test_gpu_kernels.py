@@ -607,3 +607,37 @@ def test_anchor_step_hint_exact(ctx):
         if step == 2 or (step == 3 and cfg.ctx_len > 8192):
             t = cfg.ctx_len
             assert torch.equal(hinted.scores[..., :t], plain.scores[..., :t]), step
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,t,pad,N", [
+    (1, 6, 2, 3001, 0, 128),     # G = 3: sub-groups of 2 and 1, ragged t
+    (2, 12, 2, 2048, 8, 256),    # G = 6: sub-groups of 4 and 2, strided rows
+    (1, 16, 1, 1537, 0, 64),     # G = 16: two sub-groups of 8
+    (1, 4, 4, 9000, 0, 512),     # MHA, t past the selection's 8192-entry list
+])
+def test_anchor_step_recomputed_rows(B, Hq, Hkv, t, pad, N):
+    """A hinted anchor step whose hints miss (too high: no key listed; too low:
+    every key listed, beyond 8K keys more than the list holds) recomputes each
+    skipped score row inside the selection. The rows, and everything selected
+    and attended from them, equal those of an unhinted step bit for bit, for
+    every query sub-group shape the scan launches."""
+    dev = _dev()
+    K = _kv(B, Hkv, t, 128, torch.float16, 11, pad_t=pad)
+    V = _kv(B, Hkv, t, 128, torch.float16, 12, pad_t=pad)
+    g = torch.Generator().manual_seed(13)
+    q = torch.randn((B, Hq, 128), generator=g).to(torch.float16).to(dev)
+    hinted = DecodeEngine(K, Hq, N)
+    plain = DecodeEngine(K, Hq, N)
+    plain.anchor_step(q, K, V, P.PRHS_TOPN, N, hint=False)
+    lows = (-1e30,) if t > 8192 else ()
+    for th in (1e30,) + lows:
+        hinted.scores.fill_(float("nan"))
+        hinted.theta.fill_(th)
+        hinted.anchor_step(q, K, V, P.PRHS_TOPN, N)
+        torch.cuda.synchronize()
+        assert torch.equal(hinted.scores[..., :t], plain.scores[..., :t]), th
+        for n in ("count", "lse_all", "out", "lse_sel", "delta", "tau"):
+            assert torch.equal(getattr(hinted, n), getattr(plain, n)), (th, n)
+        for b in range(B):
+            for h in range(Hq):
+                assert torch.equal(hinted.idx[b, h, :N], plain.idx[b, h, :N]), (th, b, h)
