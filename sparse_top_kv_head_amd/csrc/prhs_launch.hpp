@@ -76,7 +76,7 @@ struct SelectArgs {
   float* rescore_row = nullptr;
   float rescore_scale = 0.f;
   const int* active = nullptr;    // per head; inactive heads are left untouched
-  // Fused decode (TOPN with scan partials, fp16 rows of 128): when v is given,
+  // Fused decode (TOPN or DELTA with scan partials, fp16 rows of 128): when v is given,
   // each head's workgroup attends over its own selection and writes out,
   // lse_sel and, when delta is given, delta (and tau).
   const void* v = nullptr;
@@ -99,7 +99,8 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& a, hipStream_t st
 constexpr int kFuseRows = 2048;
 constexpr int kFuseMinHeads = 128;
 inline bool fuse_decode(const prhs_dims& d, int mode, int n_budget) {
-  return mode == PRHS_TOPN && d.dtype == PRHS_F16 && d.head_dim == 128 && n_budget <= kFuseRows &&
+  return (mode == PRHS_TOPN || mode == PRHS_DELTA) && d.dtype == PRHS_F16 && d.head_dim == 128 &&
+         n_budget <= kFuseRows &&
          (d.batch * d.n_q_heads >= kFuseMinHeads || n_budget <= kDecodeRows);
 }
 

@@ -1124,11 +1124,11 @@ __device__ __forceinline__ void rescore_row(const SelectArgs& a, int head, uint4
 // (max, sum) partials of the score scan are merged here, the result used and
 // written to lse_all. TOPN with scan candidates (cand != NULL) selects from
 // them when they hold the answer and otherwise falls back to the full path.
-// FUSE (TOPN only): the workgroup then decodes its head (fused_decode).
+// FUSE: the workgroup then decodes its head (fused_decode), over the top-N
+// or the delta-budgeted set.
 template <int KPT, int NT, int MODE, bool FUSE>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr bool MASS = MODE == PRHS_DELTA;
-  static_assert(!(FUSE && MASS), "the fused decode follows a top-N selection");
   __shared__ SelShared<NT, MASS> sh;
   // LDS mirror of the selection for the fused decode; the histogram is free
   // once the emission starts
@@ -1293,9 +1293,14 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t
   a.t = d.ctx_len;
   a.ld = d.scores_ld;
   a.nchunks = score_nchunks(d);
-  if (a.mode == PRHS_DELTA) launch_mode<PRHS_DELTA, false>(kpt, nheads, a, stream);
-  else if (a.v != nullptr) launch_mode<PRHS_TOPN, true>(kpt, nheads, a, stream);
-  else launch_mode<PRHS_TOPN, false>(kpt, nheads, a, stream);
+  if (a.mode == PRHS_DELTA) {
+    if (a.v != nullptr) launch_mode<PRHS_DELTA, true>(kpt, nheads, a, stream);
+    else launch_mode<PRHS_DELTA, false>(kpt, nheads, a, stream);
+  } else if (a.v != nullptr) {
+    launch_mode<PRHS_TOPN, true>(kpt, nheads, a, stream);
+  } else {
+    launch_mode<PRHS_TOPN, false>(kpt, nheads, a, stream);
+  }
   return hipGetLastError();
 }
 

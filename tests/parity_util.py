@@ -40,9 +40,11 @@ def reorder_tols(n, vmax):
 
 def fused_anchor_decode(dtype_f16, head_dim, n_heads, mode_topn, n_budget):
     """Whether the anchor step decodes inside the select kernel (the library's
-    rule: top-N, fp16 rows of 128, N <= 2048, and >= 128 heads or a
-    one-split budget of <= 256)."""
-    return (mode_topn and dtype_f16 and head_dim == 128 and n_budget <= 2048
+    rule, the same for top-N and for the delta budget, where n_budget is the
+    cap: fp16 rows of 128, n_budget <= 2048, and >= 128 heads or a one-split
+    budget of <= 256). mode_topn is accepted for the callers' clarity only."""
+    del mode_topn
+    return (dtype_f16 and head_dim == 128 and n_budget <= 2048
             and (n_heads >= 128 or n_budget <= 256))
 
 
