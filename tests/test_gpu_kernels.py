@@ -641,3 +641,39 @@ def test_anchor_step_recomputed_rows(B, Hq, Hkv, t, pad, N):
         for b in range(B):
             for h in range(Hq):
                 assert torch.equal(hinted.idx[b, h, :N], plain.idx[b, h, :N]), (th, b, h)
+
+
+def test_scan_wide_rows_fall_back():
+    """A KV head whose rows span 4 GiB or more (here a row stride of 2^20 + 128
+    fp16 elements over 2048 keys) is scanned by the dot-product kernel, since
+    the matrix-core kernel addresses a head's rows with 32-bit offsets; the
+    scores still meet the rounding bound against the fp64 oracle, and a hinted
+    anchor step still writes every score row (no row is skipped)."""
+    dev = _dev()
+    B, Hq, Hkv, d, t, N = 1, 4, 1, 128, 2048, 64
+    st = (1 << 20) + 128
+    assert t * st * 2 >= 1 << 32
+    base = torch.empty((B, Hkv, t, st), dtype=torch.float16, device=dev)
+    K = base[..., :d]
+    g = torch.Generator().manual_seed(21)
+    K.copy_(torch.randn((B, Hkv, t, d), generator=g).to(torch.float16))
+    V = base[..., d:2 * d]
+    V.copy_(torch.randn((B, Hkv, t, d), generator=g).to(torch.float16))
+    q = torch.randn((B, Hq, d), generator=g).to(torch.float16).to(dev)
+    eng = DecodeEngine(K, Hq, N)
+    assert eng.dims.kv_stride_t == st
+    eng.scores.fill_(float("nan"))
+    eng.theta.fill_(-1e30)          # a finite hint on every head
+    eng.anchor_step(q, K, V, P.PRHS_TOPN, N)
+    torch.cuda.synchronize()
+    bound, s_ref = score_bound(_np(q), _np(K))
+    err = np.abs(_np(eng.scores)[..., :t] - s_ref)
+    assert np.all(err <= bound), float(np.nanmax(err / bound))
+    for h in range(Hq):
+        sN = np.sort(s_ref[0, h])[::-1][N - 1]
+        gidx = eng.idx[0, h, :N].cpu().numpy()
+        ref = np.sort(np.argsort(-s_ref[0, h], kind="stable")[:N])
+        diff = np.setxor1d(gidx, ref)
+        assert np.all(np.abs(s_ref[0, h][diff] - sN) <= 1e-4), h
+    del base, K, V, eng
+    torch.cuda.empty_cache()
