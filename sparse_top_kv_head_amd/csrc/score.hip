@@ -12,7 +12,8 @@
 // Two kernels. For fp16 rows of d = 128 (every LLaMA/Mistral-shaped layer),
 // score_scan_mfma_kernel: each wave passes its loaded rows, 16 at a time,
 // through a 4 KiB LDS tile into the operand layout of v_mfma_f32_16x16x32_f16
-// and scores them on the matrix cores. Otherwise (fp32, d = 64)
+// and scores them on the matrix cores. Otherwise (fp32 rows, d = 64, or a
+// KV head whose rows span 4 GiB or more)
 // score_scan_kernel: the LPR partial dot products of a row are summed with
 // DPP row operations.
 #include "prhs_device.hpp"
