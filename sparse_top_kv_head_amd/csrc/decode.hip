@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       for (int u = 0; u < U; ++u) {
         const int i = w * RW + (it * U + u) * RPW + rr;
         const int id = i < nr ? sidx[i] : -1;
-        kv[u] = id >= 0 ? load16(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+        kv[u] = id >= 0 ? load16_stream(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   for (int u = 0; u < U; ++u) {
     const int i = w * RW + u * RPW + rr;
     const int id = i < nr ? sidx[i] : -1;
-    vv[u] = id >= 0 ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+    vv[u] = id >= 0 ? load16_stream(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
   }
 
   // split maximum
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       for (int u = 0; u < U; ++u) {
         const int i = w * RW + (it * U + u) * RPW + rr;
         const int id = i < nr ? sidx[i] : -1;
-        vv[u] = id >= 0 ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+        vv[u] = id >= 0 ? load16_stream(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
         const int r = r0 + u * RPW + rr;
         const int id = r < re ? sidx[r] : -1;
         ok[u] = id >= 0;
-        kv[u] = ok[u] ? load16(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+        kv[u] = ok[u] ? load16_stream(kbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
       const float sv = r < re ? sp[r] : -INFINITY;
       const bool ok = sv != -INFINITY;
       const int id = ok ? sidx[r] : 0;
-      vv[u] = ok ? load16(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
+      vv[u] = ok ? load16_stream(vbase + (size_t)id * row_bytes) : make_uint4(0, 0, 0, 0);
       p[u] = ok ? __expf(sv - m) : 0.f;
     }
 #pragma unroll
