@@ -826,22 +826,36 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
   const int cpw = cand_cpw<NT>(nch);
   int rows = 1;  // 64-entry rows requested per chunk in the first round
   while (rows < 4 && rows * 2 * cpw <= kSlots) rows *= 2;
-  const bool bad = __ballot(c == kNoCand) != 0ull;
-  const uint32_t cc = c == kNoCand ? 0u : c;
-  const uint32_t inc = wave_scan_u32(cc);
-  const uint32_t ex = inc - cc;
   // the wave's chunks start at a wave-uniform address: one scalar base, and a
   // 32-bit lane offset per load
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint2* src = cand + ((size_t)head * nch + (size_t)wu * cpw) * kScoreChunk;
   uint2 e[kSlots];
+  // Up to 4K keys (one chunk per wave, all of its slots in the first round)
+  // the wave requests its whole chunk before its count is in: 2 KiB per wave
+  // read ahead, one dependent round trip saved. Slots past the count hold
+  // stale entries and are never used.
+  const bool ahead = cpw == 1 && rows == 4;
+  if (ahead) {
 #pragma unroll
-  for (int sl = 0; sl < kSlots; ++sl) {
-    const int k = sl / rows, r = sl - k * rows;
-    e[sl] = make_uint2(0u, 0u);
-    if (k < cpw) {
-      const uint32_t j = (uint32_t)(lane + r * kWave);
-      if (j < lane_read(cc, k)) e[sl] = src[(uint32_t)k * kScoreChunk + j];
+    for (int sl = 0; sl < kSlots; ++sl) {
+      e[sl] = make_uint2(0u, 0u);
+      if (sl < rows && wu < nch) e[sl] = src[(uint32_t)(lane + sl * kWave)];
+    }
+  }
+  const bool bad = __ballot(c == kNoCand) != 0ull;
+  const uint32_t cc = c == kNoCand ? 0u : c;
+  const uint32_t inc = wave_scan_u32(cc);
+  const uint32_t ex = inc - cc;
+  if (!ahead) {
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int k = sl / rows, r = sl - k * rows;
+      e[sl] = make_uint2(0u, 0u);
+      if (k < cpw) {
+        const uint32_t j = (uint32_t)(lane + r * kWave);
+        if (j < lane_read(cc, k)) e[sl] = src[(uint32_t)k * kScoreChunk + j];
+      }
     }
   }
   if (lane == kWave - 1) {
