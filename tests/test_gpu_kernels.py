@@ -614,6 +614,7 @@ def test_anchor_step_hint_exact(ctx):
     (2, 12, 2, 2048, 8, 256),    # G = 6: sub-groups of 4 and 2, strided rows
     (1, 16, 1, 1537, 0, 64),     # G = 16: two sub-groups of 8
     (1, 4, 4, 9000, 0, 512),     # MHA, t past the selection's 8192-entry list
+    (1, 4, 1, 65536, 0, 1024),   # G = 4 at the largest context the selection takes
 ])
 def test_anchor_step_recomputed_rows(B, Hq, Hkv, t, pad, N):
     """A hinted anchor step whose hints miss (too high: no key listed; too low:
