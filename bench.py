@@ -285,8 +285,8 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
 
 
 def bench_growing(P, cfg, dev, stream, copies, n_steps):
-    """Growing cache on the CIS workload's shape: step s appends one K/V row
-    (a row copy into the cache, timed) and attends over t = t0 + s keys, with
+    """Growing cache on the CIS workload's shape: step s appends its K/V rows
+    (prhs_append_kv, timed) and attends over t = t0 + s keys, with
     exact retrieval every refresh_period-th step and dilated reuse otherwise."""
     from sparse_top_kv_head_amd.engine import DecodeEngine
     from sparse_top_kv_head_amd.synth import make_workload
@@ -294,8 +294,11 @@ def bench_growing(P, cfg, dev, stream, copies, n_steps):
     big = cfg.replace(ctx_len=t0 + n_steps)
     w = make_workload(big, device=dev)
     Ks, Vs = _rotated(w, copies)
-    src_k, src_v = w.K.clone(), w.V.clone()   # rows appended step by step
     N, r, Pd = cfg.budget, cfg.radius, cfg.refresh_period
+    # the rows step i appends (row t0 + i - 1), contiguous [B, H_kv, d] as a
+    # projection would produce them
+    new_rows = [(w.K[:, :, t0 + i - 1].contiguous(), w.V[:, :, t0 + i - 1].contiguous())
+                for i in range(max(n_steps, Pd))]
     anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
     reuse = DecodeEngine(w.K, cfg.n_q_heads, min(big.ctx_len, (2 * r + 1) * N))
 
@@ -303,11 +306,11 @@ def bench_growing(P, cfg, dev, stream, copies, n_steps):
         t = t0 + i
         K, V = Ks[i % copies], Vs[i % copies]
         q = w.q[i % cfg.steps]
+        kn, vn = new_rows[i]
 
         def step():
-            K[:, :, t - 1].copy_(src_k[:, :, t - 1])
-            V[:, :, t - 1].copy_(src_v[:, :, t - 1])
             anchor.set_ctx_len(t)
+            anchor.append_kv(kn, vn, K, V, t - 1)
             reuse.set_ctx_len(t)
             if i % Pd == 0:
                 anchor.anchor_step(q, K, V, P.PRHS_TOPN, N)
@@ -327,9 +330,9 @@ def bench_growing(P, cfg, dev, stream, copies, n_steps):
                    {"t0": t0, "t_final": t0 + n_steps, "budget": N, "radius": r, "refresh_period": Pd,
                     "anchor_ms_p50": round(float(np.median(per[is_a])), 5),
                     "reuse_ms_p50": round(float(np.median(per[~is_a])), 5),
-                    "note": "one K/V row appended per step (timed); hbm bytes are approximate "
+                    "note": "one K/V row per KV head appended per step by prhs_append_kv (timed); hbm bytes are approximate "
                             "(scan at the mean t, reused rows of the last step)"})
-    del w, Ks, Vs, src_k, src_v, anchor, reuse
+    del w, Ks, Vs, new_rows, anchor, reuse
     torch.cuda.empty_cache()
     return res
 

@@ -322,6 +322,20 @@ int prhs_random_expand(const prhs_dims* dims, const int32_t* anchor_idx, int32_t
 int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
                       float* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * prhs_append_kv -- append one decode step's key and value rows to the cache
+ * (Table I: t counts the decode steps, so the cache gains one row per step):
+ * for every b < batch and g < n_kv_heads
+ *   k[b, g, pos, :] = k_new[b, g, :],   v[b, g, pos, :] = v_new[b, g, :]
+ * k and v are laid out as dims describes (kv_stride_*, d contiguous, shared by
+ * k and v); k_new and v_new are contiguous [batch, n_kv_heads, head_dim] in
+ * dims->dtype. pos must lie in [0, ctx_len) (grow ctx_len to t, then append
+ * at pos = t - 1); the caller guarantees that row pos exists in its
+ * allocation. Every pointer is required and 16-byte aligned.
+ */
+int prhs_append_kv(const prhs_dims* dims, const void* k_new, const void* v_new, void* k, void* v,
+                   int32_t pos, hipStream_t stream);
+
 /* Workspace bytes needed by `op` (PRHS_OP_*) for these dims; `cap` is the
  * idx_cap of prhs_sparse_decode / prhs_anchor_step and is ignored otherwise.
  * Returns 0 for invalid dims. */

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprhs.so")
 
-SOURCES = ["score.hip", "select.hip", "cis.hip", "decode.hip", "dense.hip", "probe.hip", "prhs_abi.cpp"]
+SOURCES = ["score.hip", "select.hip", "cis.hip", "decode.hip", "dense.hip", "append.hip", "probe.hip",
+           "prhs_abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -395,6 +395,19 @@ int prhs_dense_decode(const prhs_dims* dims, const void* q, const void* k, const
                 "prhs_dense_decode");
 }
 
+int prhs_append_kv(const prhs_dims* dims, const void* k_new, const void* v_new, void* k, void* v,
+                   int32_t pos, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!k_new || !v_new || !k || !v) return fail(PRHS_E_NULL, "k_new, v_new, k and v are required");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(v))
+    return fail(PRHS_E_ALIGN, "k_new, v_new, k and v must be 16-byte aligned");
+  if (pos < 0 || pos >= dims->ctx_len)
+    return fail(PRHS_E_DIMS, "pos %d outside [0, %d)", pos, dims->ctx_len);
+  return finish(prhs::launch_append_kv(*dims, k_new, v_new, k, v, pos, stream), stream,
+                "prhs_append_kv");
+}
+
 int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, float delta_target,
                      const void* q, const void* k, const void* v, float* scores, float* lse_all,
                      int32_t* idx, int32_t idx_cap, int32_t* count, int32_t* cap_hit, float* out,

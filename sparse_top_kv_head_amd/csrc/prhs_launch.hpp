@@ -169,6 +169,10 @@ hipError_t launch_decode_mixed(const prhs_dims& d, const void* q, const void* k,
                                hipStream_t stream);
 
 // Dense attention over all ctx_len keys: split partials in ws, then the merge.
+// k[b, g, pos, :] = k_new[b, g, :] and v[b, g, pos, :] = v_new[b, g, :].
+hipError_t launch_append_kv(const prhs_dims& d, const void* k_new, const void* v_new, void* k,
+                            void* v, int pos, hipStream_t stream);
+
 hipError_t launch_dense(const prhs_dims& d, const void* q, const void* k, const void* v,
                         float* out, float* lse, void* ws, hipStream_t stream);
 

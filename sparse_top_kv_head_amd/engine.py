@@ -108,6 +108,11 @@ class DecodeEngine:
                          sim_tau, self.idx, self.cap, self.count, self.reuse_ok, stream=stream)
         self.decode(q, K, V, use_scores=False, stream=stream)
 
+    def append_kv(self, k_new, v_new, K, V, pos, stream=None):
+        """Growing cache: write one step's K and V rows (contiguous [B, H_kv, d])
+        into row ``pos`` of the cache (pos < the current ctx_len)."""
+        P.prhs_append_kv(self.dims, k_new, v_new, K, V, pos, stream=stream)
+
     def dense_step(self, q, K, V, stream=None):
         """Dense attention over every key (the baseline): out and lse_all."""
         P.prhs_dense_decode(self.dims, q, K, V, self.out, self.lse_all, self.ws, stream=stream)

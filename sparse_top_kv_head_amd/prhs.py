@@ -43,7 +43,7 @@ PRHS_MAX_SELECT_CTX = 65536
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step", "prhs_sparse_decode",
     "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step", "prhs_dense_decode",
-    "prhs_random_expand", "prhs_workspace_bytes",
+    "prhs_random_expand", "prhs_append_kv", "prhs_workspace_bytes",
     "prhs_status_string", "prhs_last_error",
 )
 # measurement aid (include/prhs_probe.h)
@@ -96,6 +96,7 @@ def lib():
                                        vp, vp, vp, vp, vp, sz, vp]
         L.prhs_dense_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_random_expand.argtypes = [dp, vp, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]
+        L.prhs_append_kv.argtypes = [dp, vp, vp, vp, vp, i32, vp]
         L.prhs_adaptive_step.argtypes = [dp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.prhs_probe_stream_read.argtypes = [vp, sz, vp, vp]
@@ -109,7 +110,7 @@ def lib():
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step",
                      "prhs_sparse_decode",
                      "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode",
-                     "prhs_adaptive_step", "prhs_random_expand"):
+                     "prhs_adaptive_step", "prhs_random_expand", "prhs_append_kv"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -239,6 +240,11 @@ def prhs_dense_decode(dims, q, k, v, out, lse, ws=None, ws_bytes=None, stream=No
         ws_bytes = ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else 0
     _check(lib().prhs_dense_decode(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(out), _p(lse),
                                    _p(ws), ws_bytes, _stream(stream)))
+
+
+def prhs_append_kv(dims, k_new, v_new, k, v, pos, stream=None):
+    _check(lib().prhs_append_kv(ctypes.byref(dims), _p(k_new), _p(v_new), _p(k), _p(v), pos,
+                                _stream(stream)))
 
 
 def prhs_anchor_step(dims, mode, n_budget, delta_target, q, k, v, scores, lse_all, idx, idx_cap,

@@ -210,6 +210,21 @@ def test_decode_argument_checks(L):
     assert L.prhs_dropped_mass(ctypes.byref(d), None, FAKE, FAKE, None, None) == P.PRHS_E_NULL
 
 
+def test_append_argument_checks(L):
+    d = _dims()
+
+    def app(dims, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, pos=5):
+        return L.prhs_append_kv(ctypes.byref(dims) if dims is not None else None, kn, vn, k, v,
+                                pos, None)
+    assert app(None) == P.PRHS_E_NULL
+    for kw in ("kn", "vn", "k", "v"):
+        assert app(d, **{kw: None}) == P.PRHS_E_NULL, kw
+        assert app(d, **{kw: FAKE_MIS}) == P.PRHS_E_ALIGN, kw
+    assert app(d, pos=-1) == P.PRHS_E_DIMS
+    assert app(d, pos=d.ctx_len) == P.PRHS_E_DIMS
+    assert app(_dims(head_dim=96)) == P.PRHS_E_DIMS
+
+
 def test_dense_argument_checks(L):
     d = _dims()
     need = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DENSE, 0)

@@ -195,15 +195,20 @@ def test_growing_cache_cis_schedule():
     """Growing cache (t = t0 + step: one more key visible each step) with the
     CIS schedule of the LLaMA2 reuse workload: exact top-N at anchor steps (the
     threshold hint carried across the growth) and the anchor's set dilated and
-    clipped to the current t at reuse steps. Sets, outputs and delta against the
-    oracle on the first t keys of every step."""
+    clipped to the current t at reuse steps. Each step first appends its key
+    and value rows (prhs_append_kv) to a cache whose rows from t0 - 1 on start
+    zeroed. Sets, outputs and delta against the oracle on the first t keys of
+    every step."""
     dev = _dev()
     t0, steps = 3000, 10
     cfg = CONFIGS["llama2_cis_8k"].replace(batch=1, ctx_len=t0 + steps, steps=steps)
     w = make_workload(cfg, device=dev)
     N, r, Pd = cfg.budget, cfg.radius, cfg.refresh_period
-    anchor = DecodeEngine(w.K, cfg.n_q_heads, N)
-    reuse = DecodeEngine(w.K, cfg.n_q_heads, min(cfg.ctx_len, (2 * r + 1) * N))
+    Kc, Vc = w.K.clone(), w.V.clone()
+    Kc[:, :, t0 - 1:] = 0
+    Vc[:, :, t0 - 1:] = 0
+    anchor = DecodeEngine(Kc, cfg.n_q_heads, N)
+    reuse = DecodeEngine(Kc, cfg.n_q_heads, min(cfg.ctx_len, (2 * r + 1) * N))
     cache = _KVCache(w)
     heads = _sample_heads(cfg, 8, 5)
     anchor_sets = {}
@@ -211,9 +216,10 @@ def test_growing_cache_cis_schedule():
         t = t0 + step
         anchor.set_ctx_len(t)
         reuse.set_ctx_len(t)
+        anchor.append_kv(w.K[:, :, t - 1].contiguous(), w.V[:, :, t - 1].contiguous(), Kc, Vc, t - 1)
         q64 = _np(w.q[step])
         if step % Pd == 0:
-            anchor.topn_step(w.q[step], w.K, w.V, N)
+            anchor.topn_step(w.q[step], Kc, Vc, N)
             torch.cuda.synchronize()
             for (b, h) in heads:
                 s_full, V = _oracle_scores(cache, q64, b, h, cfg.group)
@@ -229,8 +235,8 @@ def test_growing_cache_cis_schedule():
                 assert abs(anchor.delta[b, h].item() - d_ref) <= DELTA_TOL
                 anchor_sets[(b, h)] = gidx
             continue
-        reuse.reuse_step(w.q[step], w.K, w.V, anchor.idx, anchor.count, N, r)
-        reuse.score(w.q[step], w.K)
+        reuse.reuse_step(w.q[step], Kc, Vc, anchor.idx, anchor.count, N, r)
+        reuse.score(w.q[step], Kc)
         reuse.dropped_mass()
         torch.cuda.synchronize()
         for (b, h) in heads:

@@ -678,3 +678,25 @@ def test_scan_wide_rows_fall_back():
         assert np.all(np.abs(s_ref[0, h][diff] - sN) <= 1e-4), h
     del base, K, V, eng
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,d,pad,pos", [
+    (torch.float16, 128, 8, 0), (torch.float16, 128, 0, 999), (torch.float32, 64, 4, 517),
+    (torch.float32, 128, 0, 3), (torch.float16, 64, 0, 1000),
+])
+def test_append_kv(dtype, d, pad, pos):
+    """prhs_append_kv writes exactly row pos of every (b, KV head) of K and V,
+    bit for bit, and nothing else."""
+    dev = _dev()
+    B, Hkv, t = 3, 5, 1001
+    K = _kv(B, Hkv, t, d, dtype, 31, pad_t=pad)
+    V = _kv(B, Hkv, t, d, dtype, 32, pad_t=pad)
+    g = torch.Generator().manual_seed(33)
+    kn = torch.randn((B, Hkv, d), generator=g).to(dtype).to(dev)
+    vn = torch.randn((B, Hkv, d), generator=g).to(dtype).to(dev)
+    K_ref, V_ref = K.clone(), V.clone()
+    K_ref[:, :, pos] = kn
+    V_ref[:, :, pos] = vn
+    P.prhs_append_kv(P.make_dims(K, Hkv), kn, vn, K, V, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(K, K_ref) and torch.equal(V, V_ref)
