@@ -1084,7 +1084,8 @@ __device__ __forceinline__ void fused_decode(const SelectArgs& a, int head, int 
 // rows of A, the same products and scaling), so the row is bit-identical to
 // the one the scan would have written. Wave w scores RG consecutive 16-key
 // groups per pass (4 RG loads in flight per lane) through its 4 KiB tile;
-// RG is kept small so that this rare path adds no registers to the kernel.
+// RG is one group, so that this rare path needs few registers (the few it
+// spills in the largest instantiations stay on this path).
 template <int NT>
 __device__ __forceinline__ void rescore_row(const SelectArgs& a, int head, uint4* tiles) {
   constexpr int NWV = NT / kWave;
