@@ -1,7 +1,9 @@
 """Build libprhs.so (HIP kernels for gfx950 + the C ABI) in the package directory.
 
 Usage: python -m sparse_top_kv_head_amd.build [--jobs N] [--verbose]
-Cross-compiles without a GPU; always rebuilds.
+       python -m sparse_top_kv_head_amd.build --resources OUT.md
+Cross-compiles without a GPU; always rebuilds. --resources writes the
+compiler's per-kernel register, LDS and occupancy report instead.
 """
 
 from __future__ import annotations
@@ -71,9 +73,69 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     return LIB
 
 
+def _demangle_short(name):
+    """prhs::(anonymous namespace)::kernel<args> from an Itanium-mangled name."""
+    exe = shutil.which("llvm-cxxfilt") or shutil.which("c++filt")
+    if exe is None:
+        return name
+    out = subprocess.run([exe, name], capture_output=True, text=True).stdout.strip() or name
+    out = out.replace("prhs::(anonymous namespace)::", "").replace("void ", "")
+    return out.split("(")[0]
+
+
+def resources(out_md: str) -> None:
+    """Compile every kernel source with the compiler's resource report and
+    tabulate, per kernel, VGPRs, AGPRs, SGPRs, scratch, LDS and the occupancy
+    limit (waves per SIMD) the compiler derives from them."""
+    import re
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(CSRC, src), "-o", os.devnull]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {src}\n{r.stderr}")
+        cur = None
+        for line in r.stderr.splitlines():
+            f = re.search(r"remark: Function Name: (\S+)", line)
+            if f:
+                cur = {"kernel": _demangle_short(f.group(1)), "src": src}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+(.*?): (.*?) \[-Rpass-analysis", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = m.group(2).strip()
+    cols = [("VGPRs", "VGPRs"), ("AGPRs", "AGPRs"), ("TotalSGPRs", "SGPRs"),
+            ("ScratchSize [bytes/lane]", "scratch B/lane"), ("LDS Size [bytes/block]", "LDS B/WG"),
+            ("Occupancy [waves/SIMD]", "waves/SIMD")]
+    lines = ["# Kernel resources and occupancy limits (gfx950)\n",
+             "Command (repository root, no GPU needed):\n", "```",
+             "python -m sparse_top_kv_head_amd.build --resources profiles/kernel_resources.md", "```\n",
+             "From the compiler's kernel-resource-usage report for the flags the library is built "
+             "with. waves/SIMD is the occupancy limit those resources allow (registers, LDS, "
+             "workgroup size); the achieved occupancy of the benchmarked kernels is in the SQ "
+             "counter profiles.\n",
+             "| kernel | source | " + " | ".join(c[1] for c in cols) + " |",
+             "|---|---|" + "---|" * len(cols)]
+    for r in rows:
+        if not r["kernel"] or "kernel" not in r["kernel"]:
+            continue
+        lines.append(f"| `{r['kernel'][:70]}` | {r['src']} | " +
+                     " | ".join(r.get(c[0], "") for c in cols) + " |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resources", metavar="OUT_MD", default=None,
+                    help="write the per-kernel resource and occupancy table instead of building")
     a = ap.parse_args()
-    print(build(a.jobs, a.verbose))
+    if a.resources:
+        resources(a.resources)
+    else:
+        print(build(a.jobs, a.verbose))

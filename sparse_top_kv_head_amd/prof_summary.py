@@ -120,19 +120,35 @@ def traffic(fetch_dir, write_dir, cmds, out, title, scan_line=True):
         fh.write("\n".join(lines) + "\n")
 
 
+# MI355X: 32 shader engines (8 XCDs x 4) of 8 CUs, 4 SIMDs per CU.
+SIMDS_PER_SE = 32
+
+
 def counters(d, cmd, out, title):
     ours = set()
     agg = _counter_means(d, ours)
     names = sorted({c for k in agg for c in agg[k]})
+    occ = "SQ_WAVE_CYCLES" in names and "SQ_BUSY_CYCLES" in names
     lines = [f"# {title}\n", "Command (repository root, MI355X, one GPU):\n", "```", cmd, "```\n",
-             "Mean counter value per dispatch.\n",
-             "| kernel | dispatches | " + " | ".join(names) + " |",
-             "|---|---|" + "---|" * len(names)]
+             "Mean counter value per dispatch."]
+    if occ:
+        lines.append(
+            "waves/SIMD (achieved occupancy, estimated) = 4 * SQ_WAVE_CYCLES / SQ_BUSY_CYCLES / "
+            f"{SIMDS_PER_SE}: SQ_WAVE_CYCLES counts resident waves in 4-cycle units and "
+            "SQ_BUSY_CYCLES is summed over the 32 shader engines of 32 SIMDs each. As a check, "
+            "the plain streaming read (limit 8 waves/SIMD) comes out near 7.5, and the select "
+            "kernel (one 16-wave workgroup per CU on half of the CUs) near 2.")
+    lines += ["", "| kernel | dispatches | " + " | ".join(names) + (" | waves/SIMD |" if occ else " |"),
+              "|---|---|" + "---|" * (len(names) + (1 if occ else 0))]
     for k in sorted(agg):
         if k not in ours and COPY_KERNEL not in k:
             continue
         n = max(len(v) for v in agg[k].values())
-        vals = [f"{sum(agg[k][c]) / len(agg[k][c]):.4g}" if agg[k].get(c) else "" for c in names]
+        mean = {c: sum(agg[k][c]) / len(agg[k][c]) for c in names if agg[k].get(c)}
+        vals = [f"{mean[c]:.4g}" if c in mean else "" for c in names]
+        if occ:
+            b = mean.get("SQ_BUSY_CYCLES", 0.0)
+            vals.append(f"{4 * mean.get('SQ_WAVE_CYCLES', 0.0) / b / SIMDS_PER_SE:.2f}" if b else "")
         lines.append(f"| `{k[:60]}` | {n} | " + " | ".join(vals) + " |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
