@@ -349,3 +349,27 @@ def test_probe_argument_checks(L):
     assert L.prhs_probe_stream_read(FAKE_MIS, 64, sink, None) == P.PRHS_E_ALIGN
     assert L.prhs_probe_stream_read(FAKE, 0, sink, None) == P.PRHS_E_DIMS
     assert L.prhs_probe_stream_read(FAKE, 40, sink, None) == P.PRHS_E_DIMS
+
+
+def test_headers_compile_as_c(tmp_path):
+    """The boundary is a plain C ABI: both headers compile as C99 (with the HIP
+    runtime API header for hipStream_t) and the library links as C."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "use.c"
+    src.write_text('#include "prhs.h"\n#include "prhs_probe.h"\n'
+                   "int main(void) {\n"
+                   "  prhs_dims d = {0};\n"
+                   "  const char* s = prhs_status_string(prhs_score(&d, 0, 0, 0, 0, 0, 0, 0));\n"
+                   "  return s == 0;\n}\n")
+    inc = os.path.join(os.path.dirname(HEADER))
+    libdir = os.path.dirname(P._LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{inc}",
+                        f"-I{rocm_inc}", str(src), "-o", str(tmp_path / "use"), f"-L{libdir}",
+                        "-lprhs", f"-Wl,-rpath,{libdir}", "-Wl,--allow-shlib-undefined"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
