@@ -96,7 +96,8 @@ __device__ __forceinline__ float dot16_zero(const uint4 a, const uint4 b, __half
 
 constexpr int kScoreLoads = 16;  // 16-byte loads in flight per lane
 
-// The chunk's outputs from the staged scores sc[j][0:CHUNK) of its G heads:
+// The chunk's outputs from the staged scores sc[j][0:CHUNK) of its G heads,
+// all written through the L2 (store_through):
 // the scores themselves (not for heads with a finite theta under
 // skip_hinted), the keys >= theta as (score bits, index) candidates
 // (index-ordered: a ballot per wave, then the waves' counts give each wave its
@@ -113,14 +114,17 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
   const int nrows = min(CHUNK, t - base_row);
   // write-back: one float4 of one head's row per thread and pass
   constexpr int V4 = CHUNK / 4;
+  static_assert(V4 == kWave, "one head's row segment per wave");
 #pragma unroll
   for (int e = threadIdx.x; e < G * V4; e += kScoreThreads) {
-    const int j = e / V4;
+    // V4 = 64: one head per wave and pass, so j is wave-uniform
+    const int j = __builtin_amdgcn_readfirstlane(e / V4);
     const int i = (e - j * V4) * 4;
     if (skip_hinted && __builtin_isfinite(th[j])) continue;
-    float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;
+    float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;  // wave-uniform
     if (i + 4 <= nrows) {
-      *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(&sc[j][i]);
+      store_through(dst, (uint32_t)nrows * 4u, (uint32_t)i * 4u,
+                    *reinterpret_cast<const float4*>(&sc[j][i]));
     } else {
       for (int x = i; x < nrows; ++x) dst[x] = sc[j][x];
     }
@@ -139,7 +143,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
     for (int j = 0; j < G; ++j) {
       const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
       if (!__builtin_isfinite(th[j])) {
-        if (threadIdx.x == 0) cand_cnt[hc] = kNoCand;
+        if (threadIdx.x == 0) store_through(cand_cnt + hc, 4u, 0u, kNoCand);
         continue;
       }
       uint32_t base = 0, total = 0;
@@ -152,9 +156,10 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
       const int r = w * kWave + lane;
       if ((hits[j] >> lane) & 1ull) {
         const uint32_t pos = base + (uint32_t)__popcll(hits[j] & ((1ull << lane) - 1ull));
-        cand[hc * CHUNK + pos] = make_uint2(__float_as_uint(sc[j][r]), (uint32_t)(base_row + r));
+        store_through(cand + hc * CHUNK, CHUNK * 8u, pos * 8u,
+                      make_uint2(__float_as_uint(sc[j][r]), (uint32_t)(base_row + r)));
       }
-      if (threadIdx.x == 0) cand_cnt[hc] = total;
+      if (threadIdx.x == 0) store_through(cand_cnt + hc, 4u, 0u, total);
     }
   }
   if (part != nullptr) {
@@ -166,7 +171,9 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
       if (m != -INFINITY)
         for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
       l = wave_sum(l);
-      if (lane == 0) part[(size_t)(b * Hq + h0 + j) * nchunks + chunk] = make_float2(m, l);
+      if (lane == 0)
+        store_through(part + (size_t)(b * Hq + h0 + j) * nchunks + chunk, 8u, 0u,
+                      make_uint2(__float_as_uint(m), __float_as_uint(l)));
     }
   }
 }
