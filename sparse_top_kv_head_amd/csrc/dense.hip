@@ -163,16 +163,19 @@ __global__ __launch_bounds__(kDenseThreads) void dense_split_kernel(
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < G; ++j) {
+    // written through the L2, like the scan's outputs: they land inside the
+    // K and V read streams
     float* dst = part + ((size_t)(b * Hq + h0 + j) * nsplit + chunk) * (D + 2);
+    constexpr uint32_t kBytes = (D + 2) * 4;
     for (int col = tid; col < D; col += kDenseThreads) {
       float s = 0.f;
 #pragma unroll
       for (int u = 0; u < NW; ++u) s += so[j][u][col];
-      dst[col] = s;
+      store_through(dst, kBytes, (uint32_t)col * 4u, __float_as_uint(s));
     }
     if (tid == 0) {
-      dst[D] = mj[j];
-      dst[D + 1] = lj[j];
+      store_through(dst, kBytes, (uint32_t)D * 4u, __float_as_uint(mj[j]));
+      store_through(dst, kBytes, (uint32_t)(D + 1) * 4u, __float_as_uint(lj[j]));
     }
   }
 }
