@@ -343,7 +343,7 @@ __device__ __forceinline__ int dilate_to_lds(const int* __restrict__ src, int n,
     for (uint32_t k = 0; k < len; ++k) {
       const uint32_t o = (uint32_t)base + off + k;
       if (o < (uint32_t)out_cap) {
-        dst[o] = lo + (int)k;
+        store_through(dst, (uint32_t)out_cap * 4u, o * 4u, (uint32_t)(lo + (int)k));
         sidx[o] = lo + (int)k;
       }
     }
