@@ -21,6 +21,7 @@ from .prhs_oracle import (  # noqa: F401
     topn_select,
     delta_budget_select,
     cis_dilate,
+    random_expansion,
     cis_schedule,
     sparse_attention,
     dropped_mass,

@@ -15,7 +15,8 @@ from oracle import prhs_oracle as O
 from sparse_top_kv_head_amd import prhs as P
 from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
 from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-from tests.parity_util import DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band
+from tests.parity_util import (DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band,
+                               reorder_tols)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +114,29 @@ def test_mistral_gqa_32k_sampled():
     torch.cuda.synchronize()
     for a, b in zip(first, (eng.idx, eng.count, eng.out, eng.delta)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["mistral_gqa_32k", "llama2_4k"])
+def test_fused_decode_matches_decode_kernel(name):
+    """At full size, the attention the selection kernel computes for its own
+    head (the anchor step) and the one prhs_sparse_decode computes over the
+    same selection from the same score rows differ only by the order of their
+    fp32 sums: outputs within (4(n - 1) + 8) u max|v|, lse_sel, delta and tau
+    within (2(n - 1) + 8) u."""
+    dev = _dev()
+    cfg = CONFIGS[name]
+    w = make_workload(cfg, device=dev)
+    a = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    b = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+    q = w.q[cfg.steps // 2]
+    a.anchor_step(q, w.K, w.V, P.PRHS_TOPN, cfg.budget, hint=False)   # every score row written
+    P.prhs_sparse_decode(a.dims, q, w.K, w.V, a.idx, a.cap, a.count, a.scores, a.lse_all, b.out,
+                         b.lse_sel, b.delta, b.tau, b.ws)
+    torch.cuda.synchronize()
+    otol, ltol = reorder_tols(cfg.budget, w.V.abs().max().item())
+    assert (a.out - b.out).abs().max().item() <= otol
+    for n in ("lse_sel", "delta", "tau"):
+        assert (getattr(a, n) - getattr(b, n)).abs().max().item() <= ltol, n
 
 
 def test_llama2_cis_8k_schedule():
