@@ -182,6 +182,33 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * prhs_sparse_decode_noalloc -- prhs_sparse_decode without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * The operation, the arguments (all but ws and ws_bytes), the results and the
+ * validation are those of prhs_sparse_decode. When the decode splits a head's
+ * set over workgroups, the split partials go to a scratch array the library
+ * keeps in device memory: one per GPU, PRHS_NOALLOC_SCRATCH_BYTES bytes, held
+ * until the process ends (its address is looked up on the first call on each
+ * device). The decode splits unless idx_cap <= 256, or idx_cap <= 8192 and
+ * B * H_q >= 128 (then one workgroup per head needs no partials). A split
+ * decode needs prhs_workspace_bytes(dims, PRHS_OP_DECODE, idx_cap) bytes; a call
+ * that needs more than PRHS_NOALLOC_SCRATCH_BYTES returns PRHS_E_WORKSPACE with
+ * nothing enqueued. The call allocates nothing. All calls on one GPU share its
+ * scratch array, and each leaves its partials there: calls whose work
+ * overlaps in time on one GPU (other streams, other threads) race on it and
+ * must not be issued.
+ */
+#define PRHS_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+int prhs_sparse_decode_noalloc(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* idx, int32_t idx_cap, const int32_t* count,
+                               const float* sel_scores, const float* scores, const float* lse_all,
+                               float* out, float* lse_sel, float* delta, float* tau,
+                               hipStream_t stream);
+
+/*
  * prhs_reuse_step -- one CIS reuse step in a single call: the dilation of
  * prhs_cis_reuse (without its similarity gate) followed by prhs_sparse_decode
  * over the dilated set, with K and V rows gathered (Fig. 4: the set of an

@@ -3,6 +3,7 @@
 // Every entry point checks all of its arguments before touching the HIP
 // runtime, so an invalid call returns its status with nothing enqueued and no
 // output written. Launch errors are reported as PRHS_E_HIP.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -120,6 +121,53 @@ StepWs step_ws_layout(const prhs_dims* d, int cap) {
 
 size_t step_ws(const prhs_dims* d, int cap) { return step_ws_layout(d, cap).total; }
 
+// Argument checks of prhs_sparse_decode other than its workspace.
+int check_decode(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                 const int32_t* idx, int32_t idx_cap, const int32_t* count, const float* sel_scores,
+                 const float* scores, const float* lse_all, float* out, float* lse_sel,
+                 float* delta, float* tau) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!v || !idx || !count || !out || !lse_sel)
+    return fail(PRHS_E_NULL, "v, idx, count, out and lse_sel are required");
+  if (!scores && !sel_scores && (!q || !k))
+    return fail(PRHS_E_NULL, "without scores or sel_scores, q and k are required");
+  if (delta && !lse_all) return fail(PRHS_E_NULL, "delta needs lse_all");
+  if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
+  if (!aligned16(v) || (k && !aligned16(k)) || (q && !aligned16(q)))
+    return fail(PRHS_E_ALIGN, "q, k and v must be 16-byte aligned");
+  if (idx_cap < 1) return fail(PRHS_E_CAPACITY, "idx_cap must be >= 1");
+  return PRHS_OK;
+}
+
+// The allocation-free decode's scratch: one array per GPU (each device holds
+// its own copy of this symbol), reached through the device address that
+// hipGetSymbolAddress gives on that device. The symbol's name in host code
+// stands for a host-side shadow, never for device memory.
+static __device__ __align__(256) unsigned char scratch[PRHS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// This device's scratch address (looked up once per device, with the device
+// current).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(PRHS_E_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PRHS_E_HIP, "device %d beyond the %d the scratch table covers", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return fail(PRHS_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(err));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PRHS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,17 +276,9 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
                        const float* sel_scores, const float* scores, const float* lse_all,
                        float* out, float* lse_sel, float* delta, float* tau, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-  int st = check_dims(dims);
+  int st = check_decode(dims, q, k, v, idx, idx_cap, count, sel_scores, scores, lse_all, out,
+                        lse_sel, delta, tau);
   if (st) return st;
-  if (!v || !idx || !count || !out || !lse_sel)
-    return fail(PRHS_E_NULL, "v, idx, count, out and lse_sel are required");
-  if (!scores && !sel_scores && (!q || !k))
-    return fail(PRHS_E_NULL, "without scores or sel_scores, q and k are required");
-  if (delta && !lse_all) return fail(PRHS_E_NULL, "delta needs lse_all");
-  if (tau && !delta) return fail(PRHS_E_NULL, "tau needs delta");
-  if (!aligned16(v) || (k && !aligned16(k)) || (q && !aligned16(q)))
-    return fail(PRHS_E_ALIGN, "q, k and v must be 16-byte aligned");
-  if (idx_cap < 1) return fail(PRHS_E_CAPACITY, "idx_cap must be >= 1");
   if (!ws) return fail(PRHS_E_WORKSPACE, "workspace is required");
   if (ws_bytes < decode_ws(dims, idx_cap))
     return fail(PRHS_E_WORKSPACE, "workspace needs %zu bytes, got %zu", decode_ws(dims, idx_cap),
@@ -247,6 +287,28 @@ int prhs_sparse_decode(const prhs_dims* dims, const void* q, const void* k, cons
   return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel_scores, scores,
                                     lse_all, out, lse_sel, delta, tau, ws, stream),
                 stream, "prhs_sparse_decode");
+}
+
+int prhs_sparse_decode_noalloc(const prhs_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* idx, int32_t idx_cap, const int32_t* count,
+                               const float* sel_scores, const float* scores, const float* lse_all,
+                               float* out, float* lse_sel, float* delta, float* tau,
+                               hipStream_t stream) {
+  int st = check_decode(dims, q, k, v, idx, idx_cap, count, sel_scores, scores, lse_all, out,
+                        lse_sel, delta, tau);
+  if (st) return st;
+  // A decode that runs one workgroup per head leaves no partials.
+  const size_t need = prhs::decode_per_head(*dims, idx_cap) ? 0 : decode_ws(dims, idx_cap);
+  if (need > PRHS_NOALLOC_SCRATCH_BYTES)
+    return fail(PRHS_E_WORKSPACE,
+                "the decode needs %zu bytes of split partials; the allocation-free call holds %u",
+                need, (unsigned)PRHS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st) return st;
+  return finish(prhs::launch_decode(*dims, q, k, v, idx, idx_cap, count, sel_scores, scores,
+                                    lse_all, out, lse_sel, delta, tau, ws, stream),
+                stream, "prhs_sparse_decode_noalloc");
 }
 
 int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t anchor_cap,

@@ -39,11 +39,12 @@ PRHS_OP_ANCHOR_STEP = 3
 PRHS_OP_DENSE = 4
 PRHS_OP_EXPAND = 5
 PRHS_MAX_SELECT_CTX = 65536
+PRHS_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTED = (
     "prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step", "prhs_sparse_decode",
-    "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step", "prhs_dense_decode",
-    "prhs_random_expand", "prhs_append_kv", "prhs_workspace_bytes",
+    "prhs_sparse_decode_noalloc", "prhs_dropped_mass", "prhs_anchor_step", "prhs_adaptive_step",
+    "prhs_dense_decode", "prhs_random_expand", "prhs_append_kv", "prhs_workspace_bytes",
     "prhs_status_string", "prhs_last_error",
 )
 # measurement aid (include/prhs_probe.h)
@@ -91,6 +92,8 @@ def lib():
                                       sz, vp]
         L.prhs_sparse_decode.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp]
+        L.prhs_sparse_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                                 vp, vp, vp]
         L.prhs_dropped_mass.argtypes = [dp, vp, vp, vp, vp, vp]
         L.prhs_anchor_step.argtypes = [dp, i32, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        vp, vp, vp, vp, vp, sz, vp]
@@ -108,7 +111,7 @@ def lib():
         L.prhs_last_error.argtypes = []
         L.prhs_last_error.restype = ctypes.c_char_p
         for name in ("prhs_score", "prhs_select_topk", "prhs_cis_reuse", "prhs_reuse_step",
-                     "prhs_sparse_decode",
+                     "prhs_sparse_decode", "prhs_sparse_decode_noalloc",
                      "prhs_dropped_mass", "prhs_anchor_step", "prhs_dense_decode",
                      "prhs_adaptive_step", "prhs_random_expand", "prhs_append_kv"):
             getattr(L, name).restype = ctypes.c_int
@@ -205,6 +208,14 @@ def prhs_sparse_decode(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out,
                                     _p(count), _p(sel_scores), _p(scores), _p(lse_all), _p(out),
                                     _p(lse_sel), _p(delta), _p(tau), _p(ws), ws_bytes,
                                     _stream(stream)))
+
+
+def prhs_sparse_decode_noalloc(dims, q, k, v, idx, idx_cap, count, scores, lse_all, out, lse_sel,
+                               delta=None, tau=None, sel_scores=None, stream=None):
+    _check(lib().prhs_sparse_decode_noalloc(ctypes.byref(dims), _p(q), _p(k), _p(v), _p(idx),
+                                            idx_cap, _p(count), _p(sel_scores), _p(scores),
+                                            _p(lse_all), _p(out), _p(lse_sel), _p(delta), _p(tau),
+                                            _stream(stream)))
 
 
 def prhs_dropped_mass(dims, lse_sel, lse_all, delta, tau=None, stream=None):

@@ -46,6 +46,8 @@ def test_header_symbols_are_exported(L):
     for name in declared | _declared(PROBE_HEADER):
         assert hasattr(L, name), name
     assert P.PRHS_MAX_SELECT_CTX == int(re.search(r"PRHS_MAX_SELECT_CTX\s+(\d+)", text).group(1))
+    assert P.PRHS_NOALLOC_SCRATCH_BYTES == int(
+        re.search(r"PRHS_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << 20\)", text).group(1)) << 20
     for const, value in re.findall(r"^\s*(PRHS_\w+)\s*=\s*(-?\d+)", text, re.M):
         assert getattr(P, const) == int(value), const
 
@@ -208,6 +210,36 @@ def test_decode_argument_checks(L):
     assert _decode(L, d, v=FAKE_MIS) == P.PRHS_E_ALIGN
     assert L.prhs_dropped_mass(ctypes.byref(d), FAKE, FAKE, None, None, None) == P.PRHS_E_NULL
     assert L.prhs_dropped_mass(ctypes.byref(d), None, FAKE, FAKE, None, None) == P.PRHS_E_NULL
+
+
+def test_decode_noalloc_argument_checks(L):
+    """The allocation-free decode validates like prhs_sparse_decode and
+    refuses, before any HIP call, a decode whose split partials exceed its
+    per-device scratch."""
+    d = _dims()
+
+    def call(dims, q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cap=64, cnt=FAKE, s=FAKE, lse=FAKE, out=FAKE,
+             lsel=FAKE, dl=FAKE, tau=FAKE, sel=None):
+        return L.prhs_sparse_decode_noalloc(ctypes.byref(dims) if dims is not None else None, q, k,
+                                            v, idx, cap, cnt, sel, s, lse, out, lsel, dl, tau, None)
+    assert call(None) == P.PRHS_E_NULL
+    assert call(_dims(head_dim=96)) == P.PRHS_E_DIMS
+    for kw in ("v", "idx", "cnt", "out", "lsel"):
+        assert call(d, **{kw: None}) == P.PRHS_E_NULL, kw
+    assert call(d, s=None, k=None) == P.PRHS_E_NULL
+    assert call(d, lse=None) == P.PRHS_E_NULL
+    assert call(d, dl=None) == P.PRHS_E_NULL
+    assert call(d, cap=0) == P.PRHS_E_CAPACITY
+    assert call(d, v=FAKE_MIS) == P.PRHS_E_ALIGN
+    # the largest idx_cap whose split partials fit, and one past it
+    per_tile = L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DECODE, 256)
+    cap_fit = P.PRHS_NOALLOC_SCRATCH_BYTES // per_tile * 256
+    assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DECODE, cap_fit) <= P.PRHS_NOALLOC_SCRATCH_BYTES
+    assert L.prhs_workspace_bytes(ctypes.byref(d), P.PRHS_OP_DECODE, cap_fit + 1) > P.PRHS_NOALLOC_SCRATCH_BYTES
+    assert call(d, cap=cap_fit + 1) == P.PRHS_E_WORKSPACE
+    assert b"allocation-free" in L.prhs_last_error()
+    big = _dims(batch=64, n_q_heads=64, n_kv_heads=8, kv_stride_b=8 * 1000 * 128)
+    assert call(big, cap=8193) == P.PRHS_E_WORKSPACE    # past one workgroup per head: 64*64*33*130*4 bytes
 
 
 def test_append_argument_checks(L):
