@@ -17,13 +17,15 @@ launch stream; ``roofline.pipeline`` the whole step: its algorithmic bytes
 (K scan + distinct gathered V rows) over the step time. ``stream_read_ceiling`` is a plain read of 4 GiB with the
 library's probe kernel. ``configs`` reports the other workloads the same way:
 the LLaMA2-7B-shaped layer (top-256 of 4K), the CIS-reuse decode (anchor,
-reuse and amortised steps), the delta-budgeted layers (literal and sharp
-query scale) and the toy. ``table4`` compares dense attention with the anchor
-step, the CIS reuse step and amortised CIS-8/16 on LLaMA2-7B-shaped layers at
-the batch sizes and context lengths of the pages' Table IV. ``adaptive_cis``
-sweeps the per-head gated refresh over block size and similarity threshold.
-``table6`` compares CIS with its budget-matched DirectReuse and RandomExpansion
-controls (beta_emp, overlap, cost). ``cpu_baseline``
+reuse and amortised steps), the delta-budgeted decode over all 32 of its
+layers (literal and sharp query scale; N* and the cap-hit fraction per layer)
+and the toy. ``table4`` compares dense attention with the anchor step, the CIS
+reuse step and amortised CIS-8/16 on LLaMA2-7B-shaped layers at the batch
+sizes and context lengths of the pages' Table IV. ``adaptive_cis`` sweeps the
+per-head gated refresh over radius, block size and similarity threshold, and
+``table6`` compares CIS with its budget-matched DirectReuse and
+RandomExpansion controls (beta_emp, overlap, cost) at r = 1 and 2; both run on
+the CIS workload at query scale 1 (literal) and 3 (sharp). ``cpu_baseline``
 times the fp64 numpy oracle on a bounded sample of the headline workload.
 """
 
@@ -174,14 +176,6 @@ def cpu_model():
     except OSError:
         pass
     return None
-
-
-def sharpest_layers(cfg, n):
-    """The n layers with the largest drawn query scale (the sharpest attention):
-    the ones whose smallest N varies below the cap."""
-    from sparse_top_kv_head_amd.synth import layer_q_scale
-    scales = [layer_q_scale(cfg, l) for l in range(cfg.n_layers)]
-    return sorted(sorted(range(cfg.n_layers), key=lambda l: -scales[l])[:n])
 
 
 def _rotated(w, copies):
@@ -350,136 +344,170 @@ def bench_growing(P, cfg, dev, stream, copies, n_steps):
     return res
 
 
-def bench_delta(P, cfg, dev, stream, warmup, layer_ids, steps_per_layer):
-    """Delta-budgeted decode, one layer-step per step, cycling over the layers
-    `layer_ids` (independent KV caches, each larger than the Infinity Cache)."""
+def bench_delta(P, cfg, dev, stream, steps_per_layer):
+    """Delta-budgeted decode over every layer of the config: each layer (an
+    independent KV cache larger than the Infinity Cache, with its own drawn
+    query scale, cluster count and bias) is built, warmed up once and timed for
+    `steps_per_layer` graph-replayed layer-steps, then freed. The rate is the
+    total over all layers; the per-layer rows give N* and the cap-hit fraction
+    of each layer's last timed step."""
     from sparse_top_kv_head_amd.engine import DecodeEngine
     from sparse_top_kv_head_amd.synth import make_workload
-    layers = len(layer_ids)
-    ws = [make_workload(cfg, device=dev, layer=l) for l in layer_ids]
-    engs = [DecodeEngine(w.K, cfg.n_q_heads, cfg.budget) for w in ws]
-
-    def mk(i):
-        l, s = i % layers, (i // layers) % cfg.steps
-        w, eng = ws[l], engs[l]
-        return lambda: eng.delta_step(w.q[s], w.K, w.V, cfg.budget, cfg.delta_star)
-
-    for i in range(warmup * layers):
-        mk(i)()
-    n_steps = layers * steps_per_layer
-    per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
     e, d = cfg.elem_bytes, cfg.head_dim
     scan = cfg.batch * cfg.n_kv_heads * cfg.ctx_len * d * e
-    rows = np.mean([distinct_rows(eng.idx, eng.count, cfg.group) for eng in engs])
-    counts = torch.stack([eng.count for eng in engs]).float()
-    caps = torch.stack([eng.cap_hit for eng in engs]).float()
-    res = _summary(cfg, per, gms, n_steps, scan + rows * d * e, {
-        "unit_of_step": "layer-step", "layers_cycled": list(layer_ids), "delta_star": cfg.delta_star,
-        "cap": cfg.budget, "mean_n_star": round(float(counts.mean()), 1),
-        "min_n_star": int(counts.min()), "cap_hit_fraction": round(float(caps.mean()), 4),
-        "q_scale": list(cfg.q_scale)})
-    del ws, engs
-    torch.cuda.empty_cache()
+    per_all, total_ms, total_bytes, rows_out = [], 0.0, 0.0, []
+    for layer in range(cfg.n_layers):
+        w = make_workload(cfg, device=dev, layer=layer)
+        eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
+
+        def mk(s):
+            return lambda: eng.delta_step(w.q[s % cfg.steps], w.K, w.V, cfg.budget, cfg.delta_star)
+        mk(cfg.steps - 1)()
+        per, gms = timed_steps([mk(s) for s in range(steps_per_layer)], stream)
+        rows = distinct_rows(eng.idx, eng.count, cfg.group)
+        cnt = eng.count.float()
+        per_all.extend(per.tolist())
+        total_ms += gms
+        total_bytes += steps_per_layer * (scan + rows * d * e)
+        rows_out.append({"layer": layer, "q_scale": round(w.q_scale, 3), "bias": round(w.bias, 3),
+                         "clusters": w.n_clusters, "ms_per_step": round(gms / steps_per_layer, 5),
+                         "mean_n_star": round(float(cnt.mean()), 1), "min_n_star": int(cnt.min()),
+                         "cap_hit_fraction": round(float(eng.cap_hit.float().mean()), 4)})
+        del w, eng
+        torch.cuda.empty_cache()
+    n_steps = cfg.n_layers * steps_per_layer
+    res = _summary(cfg, np.asarray(per_all), total_ms, n_steps, total_bytes / n_steps, {
+        "unit_of_step": "layer-step", "layers": cfg.n_layers, "steps_per_layer": steps_per_layer,
+        "delta_star": cfg.delta_star, "cap": cfg.budget,
+        "mean_n_star": round(float(np.mean([r["mean_n_star"] for r in rows_out])), 1),
+        "min_n_star": min(r["min_n_star"] for r in rows_out),
+        "cap_hit_fraction": round(float(np.mean([r["cap_hit_fraction"] for r in rows_out])), 4),
+        "q_scale": list(cfg.q_scale), "per_layer": rows_out})
     return res
 
 
-def bench_adaptive(P, dev, stream, n_steps=32, copies=2):
-    """Per-head gated CIS refresh (prhs_adaptive_step) on the CIS workload's
-    shape, swept over the block size s and the similarity threshold tau.
+def reuse_quality(diag, M, N, S_idx, S_cnt, lse_sel):
+    """Per head, for a reused set S (S_idx, S_cnt, and lse_sel: the decode's
+    log-sum-exp over S) of the query diag has just scored and selected the
+    exact top-M of: beta_emp = tau(exact top-|S|) - tau(S) (the retained-mass
+    gap of Tables VI/VII, tau(X) = sum over X of the softmax weights) and the
+    overlap |S & exact top-N| / N. Device tensors [B, H] (float64)."""
+    s = diag.sel_scores[..., :M]
+    order = torch.argsort(s, dim=-1, descending=True, stable=True)
+    lse_all = diag.lse_all.double()
+    wts = torch.exp(s.gather(-1, order).double() - lse_all[..., None])
+    tau_cum = torch.cat([torch.zeros_like(wts[..., :1]), wts.cumsum(-1)], dim=-1)
+    n = S_cnt.clamp(0, M).long()
+    beta = tau_cum.gather(-1, n[..., None])[..., 0] - torch.exp(lse_sel.double() - lse_all)
+    top_n = diag.idx[..., :M].gather(-1, order[..., :N]).long()
+    t = diag.dims.ctx_len
+    member = torch.zeros(s.shape[:-1] + (t,), dtype=torch.bool, device=s.device)
+    member.scatter_(-1, top_n, True)
+    cap = S_idx.shape[-1]
+    valid = torch.arange(cap, device=s.device) < S_cnt[..., None]
+    hits = member.gather(-1, S_idx.long().clamp(0, t - 1)) & valid
+    return beta, hits.sum(-1).double() / N
+
+
+def bench_adaptive(P, dev, stream, cfg, radii=(1, 2), n_steps=32, copies=2):
+    """Per-head gated CIS refresh (prhs_adaptive_step) on one CIS workload,
+    swept over the dilation radius r, the block size s and the similarity
+    threshold tau (Table VIII's knobs).
 
     Timed: the n_steps sequence captured as a HIP graph. Untimed diagnostics on
     an eager run of the same steps, with the library's own calls: rho_hat (the
-    fraction of head-steps that refresh); for shared head-steps, the retained
-    mass tau of the reused set (its lse against a separate dense scan) and its
-    overlap with the exact top-N of that step; and, over the shared pairs, the
-    query-norm ratio |q'|/|q| of Fig. 8."""
+    fraction of head-steps that refresh); for shared head-steps, beta_emp and
+    the overlap with the exact top-N of that step (reuse_quality) and the
+    retained mass tau of the reused set; and, over the shared pairs, the
+    query-norm ratio |q'|/|q| and difference ||q'| - |q|| of Fig. 8."""
     from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
-    from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-    cfg = CONFIGS["llama2_cis_8k"]
-    N, r = cfg.budget, cfg.radius
+    from sparse_top_kv_head_amd.synth import make_workload
+    N, t = cfg.budget, cfg.ctx_len
     w = make_workload(cfg, device=dev)
     Ks, Vs = _rotated(w, copies)
-    q_host = w.q.double().cpu().numpy()
-    diag = DecodeEngine(w.K, cfg.n_q_heads, N)
-    delta_d = torch.empty((cfg.batch, cfg.n_q_heads), dtype=torch.float32, device=dev)
+    qnorm = w.q.float().norm(dim=-1)          # [steps, B, H]
     rows = []
-    for period in (4, 8, 16):
-        for sim_tau in (0.7, 0.8, 0.95):
-            eng = AdaptiveEngine(w.K, cfg.n_q_heads, N, r, period, sim_tau)
+    for r in radii:
+        M = min(t, (2 * r + 1) * N)
+        diag = DecodeEngine(w.K, cfg.n_q_heads, M)
+        for period in (4, 8, 16):
+            for sim_tau in (0.7, 0.8, 0.95):
+                eng = AdaptiveEngine(w.K, cfg.n_q_heads, N, r, period, sim_tau)
 
-            def mk(i):
-                return lambda: eng.step(w.q[i % cfg.steps], Ks[i % copies], Vs[i % copies])
+                def mk(i):
+                    return lambda: eng.step(w.q[i % cfg.steps], Ks[i % copies], Vs[i % copies])
 
-            refresh, kept, overlap, ratios = [], [], [], []
-            anchor_step = np.zeros((cfg.batch, cfg.n_q_heads), dtype=np.int64)
-            eng.step_no = 0
-            for i in range(n_steps):
-                mk(i)()
-                ref = eng.refresh.cpu().numpy().astype(bool)
-                refresh.append(ref.mean())
-                shared = ~ref
-                if shared.any():
-                    q = w.q[i % cfg.steps]
-                    diag.score(q, Ks[i % copies])
-                    diag.select(P.PRHS_TOPN, N)
-                    P.prhs_dropped_mass(diag.dims, eng.lse_sel, diag.lse_all, delta_d)
-                    kept.append(float((1.0 - delta_d)[torch.from_numpy(shared).to(dev)].mean()))
-                    dil, dcnt = eng.dil_idx.cpu().numpy(), eng.dil_count.cpu().numpy()
-                    exact = diag.idx.cpu().numpy()
-                    qs = q_host[i % cfg.steps]
-                    for b, h in zip(*np.nonzero(shared)):
-                        overlap.append(np.intersect1d(dil[b, h, :dcnt[b, h]], exact[b, h, :N]).size / N)
-                        qa = q_host[anchor_step[b, h] % cfg.steps][b, h]
-                        ratios.append(np.linalg.norm(qs[b, h]) / np.linalg.norm(qa))
-                anchor_step[ref] = i
-            eng.step_no = 0
-            per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
-            heads = cfg.batch * cfg.n_q_heads
-            rows.append({"period": period, "sim_tau": sim_tau,
-                         "rho_hat": round(float(np.mean(refresh)), 4),
-                         "heads_steps_per_s": round(heads * n_steps / (gms / 1e3), 1),
-                         "ms_per_step": round(gms / n_steps, 5),
-                         "step_ms_p50": round(float(np.median(per)), 5),
-                         "shared_tau_mean": round(float(np.mean(kept)), 4) if kept else None,
-                         "shared_overlap_mean": round(float(np.mean(overlap)), 4) if overlap else None,
-                         "fig8_norm_ratio_mean": round(float(np.mean(ratios)), 5) if ratios else None,
-                         "fig8_abs_norm_diff_mean": round(float(np.mean(np.abs(np.array(ratios) - 1.0))), 6)
-                         if ratios else None})
-            del eng
-    del w, Ks, Vs, diag
+                refresh, kept, beta, overlap, ratio = [], [], [], [], []
+                anchor_step = torch.zeros((cfg.batch, cfg.n_q_heads), dtype=torch.long, device=dev)
+                eng.step_no = 0
+                for i in range(n_steps):
+                    mk(i)()
+                    ref = eng.refresh.bool()
+                    refresh.append(float(ref.float().mean()))
+                    shared = ~ref
+                    if bool(shared.any()):
+                        q = w.q[i % cfg.steps]
+                        diag.score(q, Ks[i % copies])
+                        diag.select(P.PRHS_TOPN, M)
+                        b_, o_ = reuse_quality(diag, M, N, eng.dil_idx, eng.dil_count, eng.lse_sel)
+                        beta.append(b_[shared])
+                        overlap.append(o_[shared])
+                        kept.append(torch.exp(eng.lse_sel.double() - diag.lse_all.double())[shared])
+                        qa = qnorm.gather(0, (anchor_step % cfg.steps)[None])[0]
+                        ratio.append((qnorm[i % cfg.steps] / qa)[shared])
+                    anchor_step[ref] = i
+                eng.step_no = 0
+                per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
+                heads = cfg.batch * cfg.n_q_heads
+                cat = (lambda xs: torch.cat(xs).double().cpu().numpy()) if beta else None
+                row = {"radius": r, "period": period, "sim_tau": sim_tau,
+                       "rho_hat": round(float(np.mean(refresh)), 4),
+                       "heads_steps_per_s": round(heads * n_steps / (gms / 1e3), 1),
+                       "ms_per_step": round(gms / n_steps, 5),
+                       "step_ms_p50": round(float(np.median(per)), 5)}
+                if cat is not None:
+                    rt = cat(ratio)
+                    row.update({"shared_beta_emp_mean": round(float(cat(beta).mean()), 5),
+                                "shared_overlap_mean": round(float(cat(overlap).mean()), 4),
+                                "shared_tau_mean": round(float(cat(kept).mean()), 4),
+                                "fig8_norm_ratio_mean": round(float(rt.mean()), 5),
+                                "fig8_norm_ratio_p10_p90": [round(float(np.percentile(rt, 10)), 4),
+                                                            round(float(np.percentile(rt, 90)), 4)]})
+                rows.append(row)
+                del eng
+        del diag
+    del w, Ks, Vs
     torch.cuda.empty_cache()
-    return {"workload": "llama2_cis_8k shape: B=8, 32 MHA heads, d=128, t=8192, fp16",
-            "budget": N, "radius": r, "steps": n_steps,
+    return {"workload": f"{cfg.name}: B={cfg.batch}, {cfg.n_q_heads} MHA heads, d={cfg.head_dim}, "
+                        f"t={cfg.ctx_len}, fp16, query scale {cfg.q_scale[0]}",
+            "budget": N, "steps": n_steps,
             "rule": "refresh every s-th step, and in between when cos(q, q_anchor) < tau (per head)",
-            "note": "adjacent queries of the synthetic walk have cosine ~0.98, decaying with the anchor's "
-                    "age; norms are preserved by the walk, so the Fig. 8 ratio is 1 up to fp16 rounding",
             "rows": rows}
 
 
-def bench_table6(P, dev, stream, n_steps=16):
-    """The controls of the pages' Table VI (Panel A) on the CIS workload, at one
-    refresh period and a matched processed size m (the mean dilated size):
-    CIS (the top-N anchor set dilated by r), DirectReuse (a top-m anchor set
-    reused unchanged) and RandomExpansion (the top-N anchor set plus random
-    keys up to m, draws from the seeded input generator). On every reuse step,
-    per head: beta_emp = tau(exact top-|S|) - tau(S), with tau(S) from the
-    decode's lse over S against a dense scan, and the overlap of S with the
-    exact top-N of that step. Reuse-step costs are graph-timed per control."""
+def bench_table6(P, dev, stream, cfg, radius, n_steps=16):
+    """The controls of the pages' Table VI (Panel A) on one CIS workload, at the
+    workload's refresh period, dilation radius `radius` and a matched processed
+    size m (the mean dilated size): CIS (the top-N anchor set dilated by r),
+    DirectReuse (a top-m anchor set reused unchanged) and RandomExpansion (the
+    top-N anchor set plus random keys up to m, draws from the seeded input
+    generator). On every reuse step, per head: beta_emp and the overlap with the
+    exact top-N of that step (reuse_quality). Reuse-step costs are graph-timed
+    per control."""
     from sparse_top_kv_head_amd.engine import DecodeEngine
-    from sparse_top_kv_head_amd.synth import CONFIGS, expansion_draws, make_workload
-    cfg = CONFIGS["llama2_cis_8k"]
-    N, r, Pd, t = cfg.budget, cfg.radius, cfg.refresh_period, cfg.ctx_len
+    from sparse_top_kv_head_amd.synth import expansion_draws, make_workload
+    N, r, Pd, t = cfg.budget, radius, cfg.refresh_period, cfg.ctx_len
     B, H = cfg.batch, cfg.n_q_heads
     w = make_workload(cfg, device=dev)
     K, V = w.K, w.V
     base = DecodeEngine(K, H, N)
-    cis = DecodeEngine(K, H, min(t, (2 * r + 1) * N))
+    M = min(t, (2 * r + 1) * N)
+    cis = DecodeEngine(K, H, M)
     base.anchor_step(w.q[0], K, V, P.PRHS_TOPN, N)
     cis.reuse_step(w.q[1], K, V, base.idx, base.count, N, r)
     m = int(round(float(cis.count.float().mean())))
     direct = DecodeEngine(K, H, m)
     rexp = DecodeEngine(K, H, m)
-    M = min(t, (2 * r + 1) * N)
     diag = DecodeEngine(K, H, M)
     draws = expansion_draws(B, H, t, seed=cfg.seed, device=dev)
     exp_ws = P.alloc_workspace(base.dims, P.PRHS_OP_EXPAND, device=dev)
@@ -488,7 +516,8 @@ def bench_table6(P, dev, stream, n_steps=16):
         P.prhs_random_expand(base.dims, base.idx, N, base.count, draws, m, rexp.idx, m, rexp.count,
                              exp_ws)
 
-    stats = {k: {"beta": [], "overlap": [], "size": []} for k in ("CIS", "DirectReuse", "RandomExpansion")}
+    controls = (("CIS", cis), ("DirectReuse", direct), ("RandomExpansion", rexp))
+    stats = {k: {"beta": [], "overlap": [], "size": []} for k, _ in controls}
     for step in range(n_steps):
         q = w.q[step]
         if step % Pd == 0:
@@ -501,22 +530,12 @@ def bench_table6(P, dev, stream, n_steps=16):
         rexp.decode(q, K, V, use_scores=False)
         diag.score(q, K)
         diag.select(P.PRHS_TOPN, M)
-        lse_all = diag.lse_all.cpu().numpy().astype(np.float64)
-        top_s = diag.sel_scores.cpu().numpy().astype(np.float64)
-        top_i = diag.idx.cpu().numpy()
-        for b in range(B):
-            for h in range(H):
-                order = np.argsort(-top_s[b, h], kind="stable")
-                tau_top = np.concatenate([[0.0], np.cumsum(np.exp(top_s[b, h][order] - lse_all[b, h]))])
-                exact_n = top_i[b, h][order[:N]]
-                for name, eng in (("CIS", cis), ("DirectReuse", direct), ("RandomExpansion", rexp)):
-                    n = int(eng.count[b, h])
-                    S = eng.idx[b, h, :n].cpu().numpy()
-                    tau_s = float(np.exp(float(eng.lse_sel[b, h]) - lse_all[b, h]))
-                    st = stats[name]
-                    st["beta"].append(tau_top[min(n, M)] - tau_s)
-                    st["overlap"].append(np.intersect1d(S, exact_n).size / N)
-                    st["size"].append(n)
+        for name, eng in controls:
+            b_, o_ = reuse_quality(diag, M, N, eng.idx, eng.count, eng.lse_sel)
+            st = stats[name]
+            st["beta"].append(b_.flatten())
+            st["overlap"].append(o_.flatten())
+            st["size"].append(eng.count.double().flatten())
     # reuse-step costs (graph-timed): CIS dilates and decodes; the controls decode
     steps = [w.q[i] for i in range(1, 9)]
     costs = {}
@@ -530,14 +549,16 @@ def bench_table6(P, dev, stream, n_steps=16):
     expand_ms = g / 8
     rows = []
     for name, st in stats.items():
-        rows.append({"control": name, "mean_size": round(float(np.mean(st["size"])), 1),
-                     "beta_emp_mean": round(float(np.mean(st["beta"])), 5),
-                     "overlap_top_n_mean": round(float(np.mean(st["overlap"])), 4),
+        mean = lambda xs: float(torch.cat(xs).mean())  # noqa: E731
+        rows.append({"control": name, "mean_size": round(mean(st["size"]), 1),
+                     "beta_emp_mean": round(mean(st["beta"]), 5),
+                     "overlap_top_n_mean": round(mean(st["overlap"]), 4),
                      "reuse_step_ms": round(costs[name], 5)})
     del w, K, V, base, cis, direct, rexp, diag, draws, exp_ws
     torch.cuda.empty_cache()
-    return {"workload": "llama2_cis_8k: B=8, 32 MHA heads, t=8192", "budget": N, "radius": r,
-            "refresh_period": Pd, "matched_size_m": m, "reuse_steps_measured": n_steps - len(range(0, n_steps, Pd)),
+    return {"workload": f"{cfg.name}: B={B}, {H} MHA heads, t={t}, query scale {cfg.q_scale[0]}",
+            "budget": N, "radius": r, "refresh_period": Pd, "matched_size_m": m,
+            "reuse_steps_measured": n_steps - len(range(0, n_steps, Pd)),
             "random_expand_ms": round(expand_ms, 5), "rows": rows}
 
 
@@ -708,18 +729,20 @@ def main():
                          ("llama2_cis_8k", lambda: bench_cis(P, CONFIGS["llama2_cis_8k"], dev, stream, 1, 2, 32)),
                          ("llama2_cis_8k_growing", lambda: bench_growing(
                              P, CONFIGS["llama2_cis_8k"], dev, stream, 2, 32)),
-                         ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 1, [0, 1], 8)),
-                         ("delta_16k_sharp", lambda: bench_delta(
-                             P, SHARP, dev, stream, 1, sharpest_layers(SHARP, 2), 8))):
+                         ("delta_16k", lambda: bench_delta(P, CONFIGS["delta_16k"], dev, stream, 4)),
+                         ("delta_16k_sharp", lambda: bench_delta(P, SHARP, dev, stream, 4))):
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             other[name] = fn()
         res["configs"] = other
         print("[bench] table4 sweep", file=sys.stderr, flush=True)
         res["table4"] = bench_table4(P, dev, stream)
-        print("[bench] adaptive CIS sweep", file=sys.stderr, flush=True)
-        res["adaptive_cis"] = bench_adaptive(P, dev, stream)
-        print("[bench] table6 controls", file=sys.stderr, flush=True)
-        res["table6"] = bench_table6(P, dev, stream)
+        res["adaptive_cis"], res["table6"] = {}, {}
+        for regime, name in (("literal", "llama2_cis_8k"), ("sharp", "llama2_cis_8k_sharp")):
+            print(f"[bench] adaptive CIS sweep ({regime})", file=sys.stderr, flush=True)
+            res["adaptive_cis"][regime] = bench_adaptive(P, dev, stream, CONFIGS[name])
+            for r in (1, 2):
+                print(f"[bench] table6 controls ({regime}, r={r})", file=sys.stderr, flush=True)
+                res["table6"][f"{regime}_r{r}"] = bench_table6(P, dev, stream, CONFIGS[name], r)
     if a.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -247,13 +247,16 @@ int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t an
  * lse_sel, delta and tau equal theirs up to the order of the fp32 sums.
  *
  * theta (nullable, fp32 [B, H_q], in/out; TOPN only): a per-head score
- * threshold hint. The scan also hands the keys whose score is >= theta to
- * the selection, which selects among them alone when they include the top
+ * threshold hint, per unit query norm. The scan also hands the keys whose
+ * score is >= theta * |q[b,h]| (fp32 Euclidean norm of the query row) to the
+ * selection, which selects among them alone when they include the top
  * n_budget (at least n_budget of them and at most a few thousand) and
- * otherwise searches all keys, so the result never depends on the hint. NaN
- * means no hint. On return theta holds a hint for the next step of the same
- * heads: this step's boundary score less a margin (adjacent decode queries
- * are highly similar: Fig. 2, Fig. 10). Initialise it to NaN.
+ * otherwise searches all keys, so the result never depends on the hint. NaN,
+ * or a product theta * |q| that is not finite, means no hint. On return theta
+ * holds a hint for the next step of the same heads: this step's boundary
+ * score less a margin, divided by this step's |q| (adjacent decode queries
+ * point in similar directions: Fig. 2, Fig. 10; their norms may differ:
+ * Fig. 8). Initialise it to NaN.
  * With fp16 rows of head_dim 128 (and ctx_len * kv_stride_t * 2 < 2^32), a
  * head with a finite hint gets no scores row from the scan: its row is left
  * as it was, unless its hinted keys miss the answer, in which case the

@@ -398,6 +398,9 @@ int prhs_adaptive_step(const prhs_dims* dims, int32_t n_budget, int32_t radius,
     a.cand = cd.cand;
     a.cand_cnt = cd.cand_cnt;
     a.theta_out = theta;
+    a.hint_q = q;
+    a.hint_q_f16 = dims->dtype == PRHS_F16;
+    a.hint_d = dims->head_dim;
     a.active = refresh;
     err = prhs::launch_select(*dims, a, stream);
   }
@@ -530,6 +533,9 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     a.cand = cd.cand;
     a.cand_cnt = cd.cand_cnt;
     a.theta_out = hint ? theta : nullptr;
+    a.hint_q = q;
+    a.hint_q_f16 = dims->dtype == PRHS_F16;
+    a.hint_d = dims->head_dim;
     a.kv_sb = dims->kv_stride_b;
     a.kv_sh = dims->kv_stride_h;
     a.kv_st = dims->kv_stride_t;

@@ -223,6 +223,19 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// fp32 Euclidean norm of one query row of D elements (lane-strided loads);
+// every lane of the wave returns it.
+template <typename T, int D>
+__device__ __forceinline__ float query_norm(const T* __restrict__ row, int lane) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = lane; e < D; e += kWave) {
+    const float x = static_cast<float>(row[e]);
+    s = __builtin_fmaf(x, x, s);
+  }
+  return __builtin_sqrtf(wave_sum(s));
+}
+
 // Combine two (max, sum-of-exp) pairs: sum is relative to its max; an empty
 // pair is (-inf, 0).
 __device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l2) {

@@ -67,7 +67,10 @@ struct SelectArgs {
   float* sel_scores = nullptr;    // scores of the selected keys, in idx order
   const uint2* cand = nullptr;    // scan candidates (TOPN)
   const uint32_t* cand_cnt = nullptr;
-  float* theta_out = nullptr;     // next-step threshold hint (TOPN)
+  float* theta_out = nullptr;     // next-step threshold hint per unit query norm (TOPN)
+  const void* hint_q = nullptr;   // the queries [heads, head_dim] whose norms scale theta_out
+  int hint_q_f16 = 1;             // hint_q element type: fp16 (else fp32)
+  int hint_d = 128;               // hint_q row length (64 or 128)
   // Score rows skipped by a hinted matrix-core scan: when the candidates of
   // such a head miss, its row is recomputed from q and K (strides kv_*,
   // heads hq / hkv) into rescore_row before the full search.

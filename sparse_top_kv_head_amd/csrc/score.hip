@@ -179,10 +179,11 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
 }
 
 // With `active` (per query head), a workgroup whose group has no active head
-// does nothing. With `theta` (a per-head score threshold), the chunk's keys whose score is
-// >= theta are also written, in index order, as (score bits, index) pairs to
-// cand[head][chunk][0:n] with n in cand_cnt[head][chunk]; a head whose theta is
-// not finite gets the count kNoCand.
+// does nothing. With `theta` (a per-head threshold per unit query norm), the
+// chunk's keys whose score is >= theta * |q| are also written, in index order,
+// as (score bits, index) pairs to cand[head][chunk][0:n] with n in
+// cand_cnt[head][chunk]; a head whose theta * |q| is not finite gets the count
+// kNoCand.
 template <typename T, int D, int G, int CHUNK = kScoreChunk, int UMAX = kScoreLoads>
 __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
@@ -225,7 +226,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
   }
 
   // The thresholds are read now, so that their latency hides behind the K
-  // loads instead of stalling the workgroup's tail.
+  // loads instead of stalling the workgroup's tail; each is scaled by its
+  // head's query norm after the scoring loop.
   float th[G] = {};
   if (theta != nullptr) {
 #pragma unroll
@@ -284,10 +286,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
       }
     }
   }
+  if (theta != nullptr) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) th[j] *= query_norm<T, D>(q + (size_t)(b * Hq + h0 + j) * D, lane);
+  }
   __syncthreads();
 
-  scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b, Hq, h0, t, ld,
-                                 nchunks, chunk, w, lane);
+  scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b,
+                                 Hq, h0, t, ld, nchunks, chunk, w, lane);
 }
 
 // Matrix-core scan of fp16 rows with d = 128; same outputs and grid as
@@ -339,6 +345,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
 
   half8_t qa[4];
   mfma_query_operand(q + (size_t)(b * Hq + h0) * D, G, lane, qa);
+  if (theta != nullptr) {
+    // lanes c, c + 16, c + 32 and c + 48 hold the four quarters of head c's
+    // row: their sums of squares give |q| of head c in lane c
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(qa[j][e]);
+        ss = __builtin_fmaf(x, x, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      th[j] *= __builtin_sqrtf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss), j)));
+  }
 
   // The unit's rows span less than 4 GiB (checked by the launcher), so a
   // load address is the unit's base plus a 32-bit byte offset.

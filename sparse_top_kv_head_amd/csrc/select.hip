@@ -101,6 +101,7 @@ struct SelShared {
   uint32_t wtot2[NT / kWave];
   unsigned long long wmass[NT / kWave];
   float lse;                      // dense log-sum-exp merged from the scan partials
+  float qnorm;                    // |q| of the head, for the threshold hint
   uint32_t ncand;                 // candidate list length (keys and indices)
   uint32_t ncand_r;               // boundary-bin list length of the streamed searches (keys only)
   uint32_t kmax;
@@ -919,11 +920,15 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
 }
 
 // Threshold hint for the next step of the same head: the boundary score less
-// a margin that grows with the spread between the top score and the boundary.
-__device__ __forceinline__ float next_theta(uint32_t T, uint32_t kmax) {
+// a margin that grows with the spread between the top score and the boundary,
+// divided by the query norm (scores scale with |q| at a fixed direction, so
+// the next scan multiplies it by its own query's norm). A zero norm gives NaN:
+// no hint.
+__device__ __forceinline__ float next_theta(uint32_t T, uint32_t kmax, float qnorm) {
   const float ts = key_to_score(T), ms = key_to_score(kmax);
   const float spread = ms - ts;
-  return ts - (0.1f * (spread > 0.f ? spread : 0.f) + 0.05f);
+  const float th = ts - (0.1f * (spread > 0.f ? spread : 0.f) + 0.05f);
+  return qnorm > 0.f ? th / qnorm : __builtin_nanf("");
 }
 
 // Load the head's scores (raw fp32 bits; finish_keys turns them into keys):
@@ -990,7 +995,7 @@ __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const
   if (threadIdx.x == 0) {
     a.count[head] = n_sel;
     if (a.cap_hit) a.cap_hit[head] = hit;
-    if (!MASS && a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+    if (!MASS && a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax, sh.qnorm);
   }
 }
 
@@ -1183,6 +1188,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     }
   }
 
+  // the query norm for the threshold hint, by the last wave (the first merges
+  // the partials); read only after the barriers that follow
+  if (!MASS && a.theta_out != nullptr && threadIdx.x / kWave == NT / kWave - 1) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t off = (size_t)head * a.hint_d;
+    const float qn = a.hint_q_f16
+        ? (a.hint_d == 128 ? query_norm<__half, 128>(static_cast<const __half*>(a.hint_q) + off, lane)
+                           : query_norm<__half, 64>(static_cast<const __half*>(a.hint_q) + off, lane))
+        : (a.hint_d == 128 ? query_norm<float, 128>(static_cast<const float*>(a.hint_q) + off, lane)
+                           : query_norm<float, 64>(static_cast<const float*>(a.hint_q) + off, lane));
+    if (lane == 0) sh.qnorm = qn;
+  }
+
   for (int i = threadIdx.x; i < kBins * kRep1; i += NT) sh.hist[i] = 0;
   if constexpr (MASS)
     for (int i = threadIdx.x; i < kBins; i += NT) sh.mhist[i] = 0;
@@ -1203,7 +1221,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         if (threadIdx.x == 0) {
           a.count[head] = a.n_budget;
           if (a.cap_hit) a.cap_hit[head] = 0;
-          if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax);
+          if (a.theta_out) a.theta_out[head] = next_theta(T, sh.kmax, sh.qnorm);
         }
         if constexpr (FUSE) fused_decode<NT, MASS>(a, head, a.n_budget, sh.kmax, sh.lse, sh);
         return;
@@ -1305,6 +1323,9 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t
   while (kpt * kSelThreads < d.ctx_len) kpt *= 2;
   const int nheads = d.batch * d.n_q_heads;
   SelectArgs a = args;
+  // the hint is stored per unit query norm: it needs the queries
+  if (a.theta_out != nullptr && (a.hint_q == nullptr || (a.hint_d != 64 && a.hint_d != 128)))
+    return hipErrorInvalidValue;
   a.t = d.ctx_len;
   a.ld = d.scores_ld;
   a.nchunks = score_nchunks(d);

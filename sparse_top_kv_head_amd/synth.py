@@ -54,6 +54,7 @@ class DecodeConfig:
     delta_star: float = 0.05    # delta mode target
     n_layers: int = 1           # independent KV caches (delta config)
     q_scale: tuple = (1.0, 1.0)  # per-layer query scale range (the "sharp" variant)
+    q_norm_jitter: float = 0.0  # sigma of the per-step log-normal query-norm factor
 
     @property
     def group(self):
@@ -82,9 +83,17 @@ CONFIGS = {
                               (32, 32), (4, 32), (1.5, 1.5), "step", 3.0),
     # LLaMA2-7B-shaped CIS reuse: batch 8, t=8192, N=512, 128 steps,
     # exact retrieval every 4th step, +-2 dilation otherwise.
+    # Query norms vary by a log-normal factor (sigma 0.05) per step, for Fig. 8's
+    # norm statistics of sharing pairs.
     "llama2_cis_8k": DecodeConfig("llama2_cis_8k", 8, 32, 32, 128, 8192, 512, 128, "f16", 1003,
                                   (32, 32), (4, 32), (1.5, 1.5), "step", 3.0,
-                                  mode="cis", refresh_period=4, radius=2),
+                                  mode="cis", refresh_period=4, radius=2, q_norm_jitter=0.05),
+    # The same with queries scaled by 3: attention concentrated enough that the
+    # exact top-512 keeps about 97 % of the mass (the regime of Tables VI/VII).
+    "llama2_cis_8k_sharp": DecodeConfig("llama2_cis_8k_sharp", 8, 32, 32, 128, 8192, 512, 128, "f16",
+                                        1003, (32, 32), (4, 32), (1.5, 1.5), "step", 3.0,
+                                        mode="cis", refresh_period=4, radius=2, q_norm_jitter=0.05,
+                                        q_scale=(3.0, 3.0)),
     # Mistral-7B-shaped GQA: batch 4, 32 query heads on 8 KV heads, t=32768, N=2048, 32 steps.
     "mistral_gqa_32k": DecodeConfig("mistral_gqa_32k", 4, 32, 8, 128, 32768, 2048, 32, "f16", 1004,
                                     (256, 256), (8, 64), (1.5, 1.5), "step", 3.0),
@@ -104,6 +113,9 @@ class Workload:
     K: torch.Tensor            # [B, H_kv, t, d]
     V: torch.Tensor            # [B, H_kv, t, d]
     clusters: list = field(default_factory=list)  # (b, g, start, length, owner_h, target_step)
+    q_scale: float = 1.0       # the drawn query scale of this layer
+    bias: float = 0.0          # the drawn cluster bias of this layer
+    n_clusters: int = 0        # the drawn cluster count per (b, h_kv)
 
 
 def _layer_rng(cfg: DecodeConfig, layer: int):
@@ -114,40 +126,55 @@ def _layer_rng(cfg: DecodeConfig, layer: int):
 
 
 def query_walk(cfg: DecodeConfig, rng, q_scale=1.0):
-    """[steps, B, H_q, d] float64 correlated query walk (host)."""
+    """[steps, B, H_q, d] float64 correlated query walk (host). Each step keeps
+    the direction of the last one plus noise; its norm is |q_0|, times
+    exp(sigma * xi) with a fresh standard normal xi per step when
+    cfg.q_norm_jitter = sigma > 0."""
     B, H, d, S = cfg.batch, cfg.n_q_heads, cfg.head_dim, cfg.steps
     q = np.empty((S, B, H, d), dtype=np.float64)
     q[0] = rng.standard_normal((B, H, d)) * q_scale
     norm0 = np.linalg.norm(q[0], axis=-1, keepdims=True)
     for s in range(1, S):
         x = q[s - 1] + 0.2 * q_scale * rng.standard_normal((B, H, d))
-        q[s] = x / np.linalg.norm(x, axis=-1, keepdims=True) * norm0
+        norm = norm0
+        if cfg.q_norm_jitter > 0.0:
+            norm = norm0 * np.exp(cfg.q_norm_jitter * rng.standard_normal((B, H, 1)))
+        q[s] = x / np.linalg.norm(x, axis=-1, keepdims=True) * norm
     return q
 
 
-def _place_clusters(rng, t, count, len_lo, len_hi):
-    """Non-overlapping runs with starts uniform in [N_SINKS, t - L]."""
-    taken = np.zeros(t, dtype=bool)
-    out = []
-    attempts = 0
-    while len(out) < count and attempts < 50 * count + 100:
-        attempts += 1
-        L = int(rng.integers(len_lo, len_hi + 1))
-        if t - L < N_SINKS:
-            continue
-        start = int(rng.integers(N_SINKS, t - L + 1))
-        if taken[start:start + L].any():
-            continue
-        taken[start:start + L] = True
-        out.append((start, L))
-    return out
+def _place_clusters(rng, t, rows, count, len_lo, len_hi):
+    """For each of ``rows`` (b, g) pairs, ``count`` non-overlapping runs in
+    [N_SINKS, t): lengths uniform in [len_lo, len_hi], then the free rows cut
+    into count + 1 gaps at uniformly drawn points (every ordered arrangement of
+    those lengths is equally likely; runs may touch). Runs that would not fit
+    are dropped from the end. Returns (row, start, length) int64 arrays."""
+    span = t - N_SINKS
+    L = rng.integers(len_lo, len_hi + 1, size=(rows, count))
+    keep = np.cumsum(L, axis=1) <= span
+    L = np.where(keep, L, 0)
+    free = span - L.sum(axis=1)
+    cuts = np.sort(rng.integers(0, free[:, None] + 1, size=(rows, count)), axis=1)
+    starts = N_SINKS + cuts + np.cumsum(L, axis=1) - L
+    r, c = np.nonzero(keep)
+    return r, starts[r, c], L[r, c]
 
 
-def layer_q_scale(cfg: DecodeConfig, layer: int) -> float:
-    """The query scale make_workload draws for ``layer`` (the first draw of its stream)."""
-    if cfg.q_scale[0] == cfg.q_scale[1]:
-        return cfg.q_scale[0]
-    return float(_layer_rng(cfg, layer).uniform(*cfg.q_scale))
+def _layer_head(cfg: DecodeConfig, rng):
+    """The first draws of a layer's stream: query scale, query walk, cluster
+    bias and cluster count."""
+    q_scale = float(rng.uniform(*cfg.q_scale)) if cfg.q_scale[0] != cfg.q_scale[1] else cfg.q_scale[0]
+    qw = query_walk(cfg, rng, q_scale)
+    bias = cfg.bias[0] if cfg.bias[0] == cfg.bias[1] else float(rng.uniform(*cfg.bias))
+    n_cl = int(rng.integers(cfg.n_clusters[0], cfg.n_clusters[1] + 1))
+    return q_scale, qw, bias, n_cl
+
+
+def layer_draws(cfg: DecodeConfig, layer: int):
+    """(query scale, cluster bias, cluster count) that make_workload draws for
+    ``layer``, computed on the host without building the layer."""
+    q_scale, _, bias, n_cl = _layer_head(cfg, _layer_rng(cfg, layer))
+    return q_scale, bias, n_cl
 
 
 def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
@@ -155,24 +182,15 @@ def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
     rng = _layer_rng(cfg, layer)
     B, Hq, Hkv, d, t = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ctx_len
     G = cfg.group
-    q_scale = float(rng.uniform(*cfg.q_scale)) if cfg.q_scale[0] != cfg.q_scale[1] else cfg.q_scale[0]
-    qw = query_walk(cfg, rng, q_scale)
-    if cfg.bias[0] == cfg.bias[1]:
-        bias = cfg.bias[0]
-    else:
-        bias = float(rng.uniform(*cfg.bias))
-    n_lo, n_hi = cfg.n_clusters
-    n_cl = int(rng.integers(n_lo, n_hi + 1))
+    q_scale, qw, bias, n_cl = _layer_head(cfg, rng)
 
     # Per (b, g): cluster runs, owners and target steps; per-row bias vectors.
-    plan = []
-    for b in range(B):
-        for g in range(Hkv):
-            runs = _place_clusters(rng, t, n_cl, *cfg.cluster_len)
-            for (start, L) in runs:
-                owner = g * G + int(rng.integers(0, G))
-                step = 0 if cfg.bias_target == "q0" else int(rng.integers(0, cfg.steps))
-                plan.append((b, g, start, L, owner, step))
+    row, start, L = _place_clusters(rng, t, B * Hkv, n_cl, *cfg.cluster_len)
+    b_of, g_of = row // Hkv, row % Hkv
+    owner = g_of * G + rng.integers(0, G, size=row.size)
+    step = (np.zeros(row.size, dtype=np.int64) if cfg.bias_target == "q0"
+            else rng.integers(0, cfg.steps, size=row.size))
+    plan_arr = np.stack([b_of, g_of, start, L, owner, step], axis=1).astype(np.int64)
     seeds = rng.integers(0, 2**62, size=2 * B)
 
     dev = torch.device(device)
@@ -180,7 +198,6 @@ def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
     V = torch.empty((B, Hkv, t, d), dtype=cfg.torch_dtype, device=dev)
     unit = qw / np.linalg.norm(qw, axis=-1, keepdims=True)
     unit_dev = torch.as_tensor(unit, dtype=torch.float32, device=dev)
-    plan_arr = np.asarray(plan, dtype=np.int64).reshape(-1, 6)
     for b in range(B):
         gk = torch.Generator(device=dev)
         gk.manual_seed(int(seeds[2 * b]))
@@ -207,7 +224,8 @@ def make_workload(cfg: DecodeConfig, device="cpu", layer: int = 0) -> Workload:
         V[b] = vb.to(cfg.torch_dtype)
         del kb, vb
     q = torch.as_tensor(qw, dtype=cfg.torch_dtype).to(dev)
-    return Workload(cfg, layer, q.contiguous(), K, V, plan)
+    plan = [tuple(r) for r in plan_arr.tolist()]
+    return Workload(cfg, layer, q.contiguous(), K, V, plan, q_scale, bias, n_cl)
 
 
 def expansion_draws(batch, n_heads, t, seed, device="cpu", bits=23):

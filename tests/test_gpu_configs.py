@@ -14,7 +14,7 @@ import torch
 from oracle import prhs_oracle as O
 from sparse_top_kv_head_amd import prhs as P
 from sparse_top_kv_head_amd.engine import AdaptiveEngine, DecodeEngine
-from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
+from sparse_top_kv_head_amd.synth import CONFIGS, layer_draws, make_workload
 from tests.parity_util import (DELTA_TOL, OUT_TOL, check_delta_choice, check_set_band,
                                reorder_tols)
 
@@ -139,12 +139,14 @@ def test_fused_decode_matches_decode_kernel(name):
         assert (getattr(a, n) - getattr(b, n)).abs().max().item() <= ltol, n
 
 
-def test_llama2_cis_8k_schedule():
+@pytest.mark.parametrize("name", ["llama2_cis_8k", "llama2_cis_8k_sharp"])
+def test_llama2_cis_8k_schedule(name):
     """CIS reuse at full size: exact retrieval every 4th step, +-2 dilation of the
     anchor's set otherwise (not chained), attention over the reused set with
-    gathered K and V rows; delta of the reused set against the oracle."""
+    gathered K and V rows; delta of the reused set against the oracle. Also at
+    query scale 3, where the exact top-512 keeps most of the mass."""
     dev = _dev()
-    cfg = CONFIGS["llama2_cis_8k"]
+    cfg = CONFIGS[name]
     w = make_workload(cfg, device=dev)
     r = cfg.radius
     dil_cap = min(cfg.ctx_len, (2 * r + 1) * cfg.budget)
@@ -182,16 +184,30 @@ def test_llama2_cis_8k_schedule():
             assert O.beta_emp(s, D_ref) >= -1e-12
 
 
+def _delta_layer(cfg, which):
+    """The layer of lowest, median or highest drawn cluster bias (sharp
+    variant: of lowest, median or highest drawn query scale) among the 32."""
+    draws = [layer_draws(cfg, l) for l in range(cfg.n_layers)]
+    key = (lambda l: draws[l][0]) if cfg.q_scale[0] != cfg.q_scale[1] else (lambda l: draws[l][1])
+    order = sorted(range(cfg.n_layers), key=key)
+    return order[{"low": 0, "mid": cfg.n_layers // 2, "high": -1}[which]]
+
+
+@pytest.mark.parametrize("which", ["low", "mid", "high"])
 @pytest.mark.parametrize("variant", ["literal", "sharp"])
-def test_delta_16k_layer_sampled(variant):
-    """Delta-budgeted layer at full size (one of the 32 layers; each layer is an
-    independent KV cache): smallest N with delta <= 0.05, capped at 2048. The
-    "sharp" variant draws a per-layer query scale in [1, 4] so that N* varies."""
+def test_delta_16k_layer_sampled(variant, which):
+    """Delta-budgeted layers at full size (each of the 32 layers is an
+    independent KV cache with its own drawn cluster count and bias in
+    [0.5, 2]): smallest N with delta <= 0.05, capped at 2048, on the layers of
+    lowest, median and highest bias. The "sharp" variant draws a per-layer
+    query scale in [1, 4] so that N* varies; there the layers are picked by
+    that scale."""
     dev = _dev()
     cfg = CONFIGS["delta_16k"]
     if variant == "sharp":
         cfg = cfg.replace(q_scale=(1.0, 4.0))
-    layer = 7
+    layer = _delta_layer(cfg, which)
+    print(f"delta_16k {variant} layer {layer} draws {layer_draws(cfg, layer)}", flush=True)
     w = make_workload(cfg, device=dev, layer=layer)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
     cache = _KVCache(w)
