@@ -2,8 +2,11 @@
 
 Usage: python -m sparse_top_kv_head_amd.build [--jobs N] [--verbose]
        python -m sparse_top_kv_head_amd.build --resources OUT.md
+       python -m sparse_top_kv_head_amd.build --sanitize
 Cross-compiles without a GPU; always rebuilds. --resources writes the
-compiler's per-kernel register, LDS and occupancy report instead.
+compiler's per-kernel register, LDS and occupancy report instead. --sanitize
+builds the host code with address and undefined-behaviour checks into
+_build/asan and runs the host-side ABI tests on it (sanitize.py).
 """
 
 from __future__ import annotations
@@ -134,7 +137,15 @@ if __name__ == "__main__":
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resources", metavar="OUT_MD", default=None,
                     help="write the per-kernel resource and occupancy table instead of building")
+    ap.add_argument("--sanitize", action="store_true",
+                    help="sanitizer build of the host code, then the host-side ABI tests on it")
     a = ap.parse_args()
+    if a.sanitize:
+        from sparse_top_kv_head_amd import sanitize
+        print(sanitize.build_sanitized(a.jobs), flush=True)
+        res = sanitize.run_host_tests()
+        print(res.stdout[-4000:], res.stderr[-4000:])
+        sys.exit(res.returncode)
     if a.resources:
         resources(a.resources)
     else:

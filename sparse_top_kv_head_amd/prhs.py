@@ -16,7 +16,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprhs.so")
+# PRHS_LIB names another build of the same library (the sanitizer build)
+_LIB_PATH = os.environ.get("PRHS_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       "libprhs.so")
 
 PRHS_OK = 0
 PRHS_E_NULL = -1
