@@ -726,6 +726,7 @@ def main():
         other = {}
         for name, fn in (("toy", lambda: bench_topn(P, CONFIGS["toy"], dev, stream, 2, 1)),
                          ("llama2_4k", lambda: bench_topn(P, CONFIGS["llama2_4k"], dev, stream, 2, 16)),
+                         ("gqa16_32k", lambda: bench_topn(P, CONFIGS["gqa16_32k"], dev, stream, 2, 8)),
                          ("llama2_cis_8k", lambda: bench_cis(P, CONFIGS["llama2_cis_8k"], dev, stream, 1, 2, 32)),
                          ("llama2_cis_8k_growing", lambda: bench_growing(
                              P, CONFIGS["llama2_cis_8k"], dev, stream, 2, 32)),

@@ -194,13 +194,19 @@ void launch_dense_split(const prhs_dims& d, const void* q, const void* k, const 
 template <typename T, int D>
 void launch_dense_group(const prhs_dims& d, const void* q, const void* k, const void* v,
                         float* part, int nsplit, hipStream_t stream) {
-  // power-of-two sub-groups of the query heads that share one KV head
+  // Power-of-two sub-groups of the query heads that share one KV head, up to
+  // one lane per head of a row group (16 heads at fp16 d = 128): each
+  // sub-group reads K and V once.
+  constexpr int kMaxSub = D / Elem<T>::kPer16B < 16 ? D / Elem<T>::kPer16B : 16;
   const int G = d.n_q_heads / d.n_kv_heads;
   int off = 0;
   while (off < G) {
-    const int rest = G - off;
-    const int sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
+    int sub = 1;
+    while (sub * 2 <= G - off && sub * 2 <= kMaxSub) sub *= 2;
     switch (sub) {
+      case 16:
+        if constexpr (kMaxSub >= 16) launch_dense_split<T, D, 16>(d, q, k, v, part, nsplit, off, stream);
+        break;
       case 8: launch_dense_split<T, D, 8>(d, q, k, v, part, nsplit, off, stream); break;
       case 4: launch_dense_split<T, D, 4>(d, q, k, v, part, nsplit, off, stream); break;
       case 2: launch_dense_split<T, D, 2>(d, q, k, v, part, nsplit, off, stream); break;

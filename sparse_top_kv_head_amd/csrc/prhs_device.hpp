@@ -134,17 +134,34 @@ __device__ __forceinline__ float4_t mfma_score16(const uint4 k0, const uint4 k1,
   return acc;
 }
 
-// The query sub-group of head h_local within a GQA group of G heads, as the
-// scan launches them: power-of-two sub-groups of 8, 4, 2 and 1 heads in
-// order. Returns the sub-group's first head (within the group) and size.
-__host__ __device__ inline void scan_subgroup(int G, int h_local, int& off, int& sub) {
-  off = 0;
-  for (;;) {
-    const int rest = G - off;
-    sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
-    if (h_local < off + sub) return;
-    off += sub;
-  }
+// Query sub-groups of a GQA group of G heads, as the scans launch them. The
+// matrix-core scan takes up to 16 heads per launch (the rows of its A
+// operand; a group of 12 is one launch, padded to 16 rows), in consecutive
+// runs of 16. The dot-product scan takes power-of-two sub-groups of at most 8,
+// largest first.
+constexpr int kMfmaMaxGroup = 16;
+constexpr int kDotMaxGroup = 8;
+
+// Size of the next dot-product sub-group when `rest` heads are left.
+__host__ __device__ inline int dot_subgroup_size(int rest) {
+  int sub = 1;
+  while (sub * 2 <= rest && sub * 2 <= kDotMaxGroup) sub *= 2;
+  return sub;
+}
+
+// The matrix-core sub-group of head h_local: its first head (within the
+// group) and its size.
+__host__ __device__ inline void mfma_subgroup(int G, int h_local, int& off, int& sub) {
+  off = h_local / kMfmaMaxGroup * kMfmaMaxGroup;
+  sub = G - off < kMfmaMaxGroup ? G - off : kMfmaMaxGroup;
+}
+
+// Rows of the A operand (and template size) for a sub-group of nq heads: the
+// next power of two.
+__host__ __device__ inline int mfma_rows(int nq) {
+  int r = 1;
+  while (r < nq) r *= 2;
+  return r;
 }
 
 // ---------------------------------------------------------------------------

@@ -109,7 +109,9 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
                                           float2* __restrict__ part, uint2* __restrict__ cand,
                                           uint32_t* __restrict__ cand_cnt, const bool use_theta,
                                           int b, int Hq, int h0, int t, int ld, int nchunks,
-                                          int chunk, int w, int lane, bool skip_hinted = false) {
+                                          int chunk, int w, int lane, bool skip_hinted = false,
+                                          int nq = G) {
+  // heads j >= nq pad the matrix-core operand and have no outputs
   const int base_row = chunk * CHUNK;
   const int nrows = min(CHUNK, t - base_row);
   // write-back: one float4 of one head's row per thread and pass
@@ -120,7 +122,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
     // V4 = 64: one head per wave and pass, so j is wave-uniform
     const int j = __builtin_amdgcn_readfirstlane(e / V4);
     const int i = (e - j * V4) * 4;
-    if (skip_hinted && __builtin_isfinite(th[j])) continue;
+    if (j >= nq || (skip_hinted && __builtin_isfinite(th[j]))) continue;
     float* dst = scores + (size_t)(b * Hq + h0 + j) * ld + base_row;  // wave-uniform
     if (i + 4 <= nrows) {
       store_through(dst, (uint32_t)nrows * 4u, (uint32_t)i * 4u,
@@ -134,13 +136,14 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int r = w * kWave + lane;
-      const bool hit = __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
+      const bool hit = j < nq && __builtin_isfinite(th[j]) && r < nrows && sc[j][r] >= th[j];
       hits[j] = __ballot(hit);
       if (lane == 0) wcnt[j][w] = (uint32_t)__popcll(hits[j]);
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < G; ++j) {
+      if (j >= nq) break;
       const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
       if (!__builtin_isfinite(th[j])) {
         if (threadIdx.x == 0) store_through(cand_cnt + hc, 4u, 0u, kNoCand);
@@ -163,7 +166,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
     }
   }
   if (part != nullptr) {
-    for (int j = w; j < G; j += NW) {
+    for (int j = w; j < nq; j += NW) {
       float m = -INFINITY;
       for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
       m = wave_max(m);
@@ -301,7 +304,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_kernel(
 // scored 16 keys at a time by mfma_score16 (query heads as the rows of A,
 // keys as the columns of B). Rows at or past t (last chunk only) load row
 // t - 1 instead, so every load is in bounds and branch-free; their scores are
-// never written. With skip_hinted, a head whose threshold is finite gets its
+// never written. The sub-group has nq <= G heads (G the operand's rows): a
+// group of up to 16 heads is one launch, so K is read once for all of them.
+// With skip_hinted, a head whose threshold is finite gets its
 // candidates but no score row (the selection recomputes the row with the same
 // helpers if the candidates do not hold its answer).
 template <int G>
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
     const __half* __restrict__ q, const __half* __restrict__ k, float* __restrict__ scores,
     float2* __restrict__ part, const float* __restrict__ theta, uint2* __restrict__ cand,
     uint32_t* __restrict__ cand_cnt, const int* __restrict__ active, int Hq, int Hkv, int t,
-    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, float scale,
+    long long sb, long long sh, long long st, int ld, int nchunks, int g_off, int nq, float scale,
     int skip_hinted) {
   constexpr int D = 128;
   constexpr int NW = kScoreThreads / kWave;
@@ -334,17 +339,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
   if (active != nullptr) {
     bool any = false;
 #pragma unroll
-    for (int j = 0; j < G; ++j) any |= active[b * Hq + h0 + j] != 0;
+    for (int j = 0; j < G; ++j) any |= j < nq && active[b * Hq + h0 + j] != 0;
     if (!any) return;
   }
   float th[G] = {};
   if (theta != nullptr) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) th[j] = theta[b * Hq + h0 + j];
+    for (int j = 0; j < G; ++j) th[j] = j < nq ? theta[b * Hq + h0 + j] : 0.f;
   }
 
   half8_t qa[4];
-  mfma_query_operand(q + (size_t)(b * Hq + h0) * D, G, lane, qa);
+  mfma_query_operand(q + (size_t)(b * Hq + h0) * D, nq, lane, qa);
   if (theta != nullptr) {
     // lanes c, c + 16, c + 32 and c + 48 hold the four quarters of head c's
     // row: their sums of squares give |q| of head c in lane c
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
   __syncthreads();
   scan_tail<G, NW, CHUNK, PITCH>(sc, wcnt, th, scores, part, cand, cand_cnt, theta != nullptr, b,
                                  Hq, h0, t, ld, nchunks, chunk, w, lane,
-                                 skip_hinted != 0 && theta != nullptr);
+                                 skip_hinted != 0 && theta != nullptr, nq);
 }
 
 // Merge the per-chunk partials of each head into its dense log-sum-exp: one
@@ -412,42 +417,59 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float2* __restrict
   if (lane == 0) lse_all[h] = (l > 0.f) ? m + __logf(l) : -INFINITY;
 }
 
-template <typename T, int D, int G>
-void launch_scan(const prhs_dims& d, const void* q, const void* k, float* scores, float2* part,
-                 const ScanCand& cd, int g_off, hipStream_t stream) {
+template <int G>
+void launch_scan_mfma(const prhs_dims& d, const void* q, const void* k, float* scores,
+                      float2* part, const ScanCand& cd, int g_off, int nq, hipStream_t stream) {
   const int nchunks = score_nchunks(d);
-  const int units = d.batch * d.n_kv_heads;
+  dim3 grid(nchunks, d.batch * d.n_kv_heads);
   const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
-  if (scan_uses_mfma(d)) {
-    dim3 grid(nchunks, units);
-    hipLaunchKernelGGL((score_scan_mfma_kernel<G>), grid, dim3(kScoreThreads), 0, stream,
-                       static_cast<const __half*>(q), static_cast<const __half*>(k), scores, part,
-                       cd.theta, cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads,
-                       d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
-                       (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale,
-                       cd.skip_hinted ? 1 : 0);
-    return;
-  }
-  dim3 grid(nchunks, units);
+  hipLaunchKernelGGL((score_scan_mfma_kernel<G>), grid, dim3(kScoreThreads), 0, stream,
+                     static_cast<const __half*>(q), static_cast<const __half*>(k), scores, part,
+                     cd.theta, cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads,
+                     d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
+                     (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, nq, scale,
+                     cd.skip_hinted ? 1 : 0);
+}
+
+template <typename T, int D, int G>
+void launch_scan_dot(const prhs_dims& d, const void* q, const void* k, float* scores,
+                     float2* part, const ScanCand& cd, int g_off, hipStream_t stream) {
+  const int nchunks = score_nchunks(d);
+  dim3 grid(nchunks, d.batch * d.n_kv_heads);
+  const float scale = (float)(1.0 / __builtin_sqrt((double)d.head_dim));
   hipLaunchKernelGGL((score_scan_kernel<T, D, G>), grid, dim3(kScoreThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), scores, part, cd.theta,
-                     cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads, d.ctx_len, (long long)d.kv_stride_b, (long long)d.kv_stride_h,
-                     (long long)d.kv_stride_t, d.scores_ld, nchunks, g_off, scale);
+                     cd.cand, cd.cand_cnt, cd.active, d.n_q_heads, d.n_kv_heads, d.ctx_len,
+                     (long long)d.kv_stride_b, (long long)d.kv_stride_h, (long long)d.kv_stride_t,
+                     d.scores_ld, nchunks, g_off, scale);
 }
 
 template <typename T, int D>
 void launch_scan_group(const prhs_dims& d, const void* q, const void* k, float* scores,
                        float2* part, const ScanCand& cd, int G, hipStream_t stream) {
-  // Power-of-two sub-groups of the query heads that share one KV head.
-  int off = 0;
-  while (off < G) {
-    const int rest = G - off;
-    const int sub = rest >= 8 ? 8 : rest >= 4 ? 4 : rest >= 2 ? 2 : 1;
+  if (scan_uses_mfma(d)) {
+    // Runs of up to 16 query heads per launch, each padded to a power-of-two
+    // operand: every group of at most 16 heads reads K once.
+    for (int off = 0; off < G; off += kMfmaMaxGroup) {
+      const int nq = G - off < kMfmaMaxGroup ? G - off : kMfmaMaxGroup;
+      switch (mfma_rows(nq)) {
+        case 16: launch_scan_mfma<16>(d, q, k, scores, part, cd, off, nq, stream); break;
+        case 8: launch_scan_mfma<8>(d, q, k, scores, part, cd, off, nq, stream); break;
+        case 4: launch_scan_mfma<4>(d, q, k, scores, part, cd, off, nq, stream); break;
+        case 2: launch_scan_mfma<2>(d, q, k, scores, part, cd, off, nq, stream); break;
+        default: launch_scan_mfma<1>(d, q, k, scores, part, cd, off, nq, stream); break;
+      }
+    }
+    return;
+  }
+  // Power-of-two sub-groups of at most 8 heads on the dot-product path.
+  for (int off = 0; off < G;) {
+    const int sub = dot_subgroup_size(G - off);
     switch (sub) {
-      case 8: launch_scan<T, D, 8>(d, q, k, scores, part, cd, off, stream); break;
-      case 4: launch_scan<T, D, 4>(d, q, k, scores, part, cd, off, stream); break;
-      case 2: launch_scan<T, D, 2>(d, q, k, scores, part, cd, off, stream); break;
-      default: launch_scan<T, D, 1>(d, q, k, scores, part, cd, off, stream); break;
+      case 8: launch_scan_dot<T, D, 8>(d, q, k, scores, part, cd, off, stream); break;
+      case 4: launch_scan_dot<T, D, 4>(d, q, k, scores, part, cd, off, stream); break;
+      case 2: launch_scan_dot<T, D, 2>(d, q, k, scores, part, cd, off, stream); break;
+      default: launch_scan_dot<T, D, 1>(d, q, k, scores, part, cd, off, stream); break;
     }
     off += sub;
   }

@@ -1105,7 +1105,7 @@ __device__ __forceinline__ void rescore_row(const SelectArgs& a, int head, uint4
   const int G = a.hq / a.hkv;
   const int g = h / G;
   int off, sub;
-  scan_subgroup(G, h - g * G, off, sub);
+  mfma_subgroup(G, h - g * G, off, sub);
   const int m = h - g * G - off;  // the head's row of A
   half8_t qa[4];
   mfma_query_operand(static_cast<const __half*>(a.rescore_q) + (size_t)(b * a.hq + g * G + off) * 128,

@@ -97,6 +97,11 @@ CONFIGS = {
     # Mistral-7B-shaped GQA: batch 4, 32 query heads on 8 KV heads, t=32768, N=2048, 32 steps.
     "mistral_gqa_32k": DecodeConfig("mistral_gqa_32k", 4, 32, 8, 128, 32768, 2048, 32, "f16", 1004,
                                     (256, 256), (8, 64), (1.5, 1.5), "step", 3.0),
+    # GQA with 16 query heads per KV head: batch 2, 32 query heads on 2 KV
+    # heads, t=32768, N=2048, 16 steps (the grouping one matrix-core scan
+    # launch covers whole).
+    "gqa16_32k": DecodeConfig("gqa16_32k", 2, 32, 2, 128, 32768, 2048, 16, "f16", 1006,
+                              (256, 256), (8, 64), (1.5, 1.5), "step", 3.0),
     # Delta-budgeted 32-layer decode: batch 16, 32 MHA heads, t=16384,
     # smallest N with delta <= 0.05, capped at 2048, 16 steps.
     "delta_16k": DecodeConfig("delta_16k", 16, 32, 32, 128, 16384, 2048, 16, "f16", 1005,

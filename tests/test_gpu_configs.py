@@ -95,11 +95,13 @@ def test_llama2_4k_full():
         assert _check_topn_heads(eng, w, cfg, step, heads, cache) >= len(heads) - 2
 
 
-def test_mistral_gqa_32k_sampled():
-    """Mistral-7B-shaped GQA layer at 32K: 16 sampled heads at three steps, plus
-    run-to-run determinism of every head's indices and outputs."""
+@pytest.mark.parametrize("name", ["mistral_gqa_32k", "gqa16_32k"])
+def test_mistral_gqa_32k_sampled(name):
+    """GQA layers at 32K (Mistral-7B-shaped, 4 query heads per KV head; and 16
+    per KV head, one scan launch per group): 16 sampled heads at three steps,
+    plus run-to-run determinism of every head's indices and outputs."""
     dev = _dev()
-    cfg = CONFIGS["mistral_gqa_32k"]
+    cfg = CONFIGS[name]
     w = make_workload(cfg, device=dev)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
     cache = _KVCache(w)

@@ -74,6 +74,8 @@ HINT_CASES = [
     (2, 64, 8, 5000, 700, (64, 64)),       # G = 8, ragged t, a short last split
     (1, 16, 8, 300, 100, (4, 4)),          # G = 2, two chunks, the last one partial
     (2, 48, 8, 3001, 192, (16, 16)),       # G = 6 (sub-groups of 4 and 2), ragged t
+    (2, 32, 2, 8192, 512, (64, 64)),       # G = 16: one scan launch per KV head
+    (1, 28, 4, 6000, 256, (32, 32)),       # G = 7 (Qwen2.5-7B grouping), ragged t
     (1, 128, 64, 65536, 256, (128, 128)),  # the largest context the selection takes
 ]
 

@@ -55,6 +55,11 @@ SCORE_CASES = [
     (1, 4, 4, 128, 1, torch.float16, 0),      # t = 1
     (2, 4, 2, 128, 2048, torch.float32, 4),   # fp32, d = 128, strided rows
     (1, 16, 2, 128, 700, torch.float16, 0),   # G = 8, one partial chunk
+    (1, 16, 1, 128, 3000, torch.float16, 0),  # G = 16: one matrix-core launch reads K once
+    (2, 24, 1, 128, 1000, torch.float16, 8),  # G = 24: sub-groups of 16 and 8, strided rows
+    (1, 16, 1, 64, 900, torch.float16, 0),    # G = 16 on the dot-product path: 8 + 8
+    (1, 28, 4, 128, 2000, torch.float16, 0),  # G = 7 (Qwen2.5-7B grouping): one launch, 8-row operand
+    (1, 24, 2, 128, 1500, torch.float16, 0),  # G = 12: one launch, 16-row operand
 ]
 
 
@@ -364,6 +369,10 @@ DENSE_CASES = [
     (1, 32, 8, 128, 9000, torch.float16, 0),    # Mistral-7B-shaped GQA layer
     (1, 16, 2, 128, 255, torch.float16, 0),     # G = 8, a single partial chunk
     (1, 2, 1, 128, 1, torch.float32, 0),        # one key
+    (1, 16, 1, 128, 3000, torch.float16, 0),    # G = 16: one launch reads K and V once
+    (1, 32, 2, 128, 600, torch.float32, 4),     # G = 16, fp32, strided rows
+    (1, 16, 1, 64, 700, torch.float32, 0),      # G = 16, fp32, d = 64
+    (1, 16, 1, 64, 300, torch.float16, 0),      # G = 16, fp16, d = 64: sub-groups of 8 and 8
 ]
 
 
@@ -612,7 +621,9 @@ def test_anchor_step_hint_exact(ctx):
 @pytest.mark.parametrize("B,Hq,Hkv,t,pad,N", [
     (1, 6, 2, 3001, 0, 128),     # G = 3: sub-groups of 2 and 1, ragged t
     (2, 12, 2, 2048, 8, 256),    # G = 6: sub-groups of 4 and 2, strided rows
-    (1, 16, 1, 1537, 0, 64),     # G = 16: two sub-groups of 8
+    (1, 16, 1, 1537, 0, 64),     # G = 16: one sub-group
+    (1, 24, 1, 2500, 0, 128),    # G = 24: sub-groups of 16 and 8
+    (1, 12, 1, 2000, 0, 128),    # G = 12: one sub-group, 16-row operand
     (1, 4, 4, 9000, 0, 512),     # MHA, t past the selection's 8192-entry list
     (1, 4, 1, 65536, 0, 1024),   # G = 4 at the largest context the selection takes
 ])
