@@ -36,6 +36,8 @@ ANCHOR_CASES = [
     (1, 2, 2, 128, 1, torch.float16, 1, P.PRHS_TOPN, 0.0),          # one key
     (1, 4, 4, 128, 300, torch.float16, 300, P.PRHS_TOPN, 0.0),      # N = t
     (1, 4, 1, 128, 9000, torch.float16, 700, P.PRHS_DELTA, 0.05),   # DELTA, scan candidates off
+    (1, 16, 1, 128, 2500, torch.float16, 256, P.PRHS_TOPN, 0.0),    # G = 16: one scan launch
+    (1, 24, 2, 128, 1800, torch.float16, 200, P.PRHS_DELTA, 0.1),   # G = 12: one launch, DELTA
 ]
 
 
@@ -424,3 +426,43 @@ def test_dense_decode_deterministic_and_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eng.out)
+
+
+def test_most_heads_one_call():
+    """The largest head count a call takes (B * H_q = 65535: the scan's grid
+    has one row of workgroups per KV head): an anchor step and a CIS reuse step
+    over 65535 MHA heads, with sampled heads against the oracle."""
+    dev = _dev()
+    B, H, d, t, N, r = 3, 21845, 64, 160, 8, 1
+    assert B * H == 65535
+    g = torch.Generator().manual_seed(65535)
+    K = torch.randn((B, H, t, d), generator=g).half().to(dev)
+    V = torch.randn((B, H, t, d), generator=g).half().to(dev)
+    q = (torch.randn((B, H, d), generator=g) * 2.0).half().to(dev)
+    anchor = DecodeEngine(K, H, N)
+    reuse = DecodeEngine(K, H, min(t, (2 * r + 1) * N))
+    anchor.anchor_step(q, K, V, P.PRHS_TOPN, N)
+    reuse.reuse_step(q, K, V, anchor.idx, anchor.count, N, r)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    heads = [(0, 0), (B - 1, H - 1)] + [(int(b), int(h)) for b, h in
+                                        zip(rng.integers(0, B, 40), rng.integers(0, H, 40))]
+    for (b, h) in heads:
+        q64 = _np(q[b, h])[None, None]
+        K64, V64 = _np(K[b, h]), _np(V[b, h])
+        s = O.attention_scores(q64, K64[None, None])[0, 0]
+        n = int(anchor.count[b, h])
+        assert n == N
+        gidx = anchor.idx[b, h, :n].cpu().numpy()
+        exact = check_set_band(gidx, s, N)
+        S = O.topn_select(s, N) if exact else gidx
+        o_ref, lse_ref = O.sparse_attention(s, V64, S)
+        assert np.max(np.abs(_np(anchor.out[b, h]) - o_ref)) <= OUT_TOL, (b, h)
+        assert abs(anchor.lse_sel[b, h].item() - lse_ref) <= 1e-3, (b, h)
+        D = O.cis_dilate(gidx, r, t)
+        nd = int(reuse.count[b, h])
+        assert np.array_equal(reuse.idx[b, h, :nd].cpu().numpy(), D), (b, h)
+        o_ref, lse_ref = O.sparse_attention(s, V64, D)
+        assert np.max(np.abs(_np(reuse.out[b, h]) - o_ref)) <= OUT_TOL, (b, h)
+    del K, V, anchor, reuse
+    torch.cuda.empty_cache()
