@@ -74,8 +74,11 @@ enum { PRHS_TOPN = 0, PRHS_DELTA = 1 };
 enum { PRHS_OP_SCORE = 0, PRHS_OP_SELECT = 1, PRHS_OP_DECODE = 2, PRHS_OP_ANCHOR_STEP = 3,
        PRHS_OP_DENSE = 4, PRHS_OP_EXPAND = 5 };
 
-/* Largest context length the selection kernel keeps resident on chip. */
-#define PRHS_MAX_SELECT_CTX 65536
+/* Largest context length the selection takes (calls that select:
+ * prhs_select_topk, prhs_anchor_step, prhs_adaptive_step, prhs_random_expand).
+ * Up to 65536 keys a head's scores are held on chip; longer rows are searched
+ * and emitted by streaming the score row, in tiles of 65536 positions. */
+#define PRHS_MAX_SELECT_CTX 262144
 
 typedef struct prhs_dims {
   int32_t batch;        /* B >= 1                                           */

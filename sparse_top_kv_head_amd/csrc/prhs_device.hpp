@@ -253,6 +253,36 @@ __device__ __forceinline__ float query_norm(const T* __restrict__ row, int lane)
   return __builtin_sqrtf(wave_sum(s));
 }
 
+// The same in two halves, so that the loads can be issued early and summed
+// later: this lane's elements e = lane, lane + 64 of a row of d (64 or 128)
+// fp16 or fp32 elements, as raw bits (zero past the row).
+__device__ __forceinline__ uint2 query_share(const void* __restrict__ q, size_t row, int d,
+                                             bool f16, int lane) {
+  uint2 r = make_uint2(0u, 0u);
+  if (f16) {
+    const uint16_t* p = static_cast<const uint16_t*>(q) + row * d;
+    r.x = p[lane];
+    if (lane + kWave < d) r.y = p[lane + kWave];
+  } else {
+    const uint32_t* p = static_cast<const uint32_t*>(q) + row * d;
+    r.x = p[lane];
+    if (lane + kWave < d) r.y = p[lane + kWave];
+  }
+  return r;
+}
+
+__device__ __forceinline__ float query_share_norm(uint2 r, bool f16) {
+  float x, y;
+  if (f16) {
+    x = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)r.x));
+    y = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)r.y));
+  } else {
+    x = __uint_as_float(r.x);
+    y = __uint_as_float(r.y);
+  }
+  return __builtin_sqrtf(wave_sum(__builtin_fmaf(x, x, y * y)));
+}
+
 // Combine two (max, sum-of-exp) pairs: sum is relative to its max; an empty
 // pair is (-inf, 0).
 __device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l2) {

@@ -350,7 +350,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
 
   half8_t qa[4];
   mfma_query_operand(q + (size_t)(b * Hq + h0) * D, nq, lane, qa);
+
+  // The unit's rows span less than 4 GiB (checked by the launcher), so a
+  // load address is the unit's base plus a 32-bit byte offset.
+  const char* kunit = reinterpret_cast<const char*>(k + b * sb + g * sh);
+  const uint32_t rb = (uint32_t)st * (uint32_t)sizeof(__half);
+  const int chunk = blockIdx.x;
+  const int row0 = chunk * CHUNK + w * RW + rr;
+  uint4 kv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int r = min(row0 + 4 * u, t - 1);
+    kv[u] = load16_stream(kunit + ((uint32_t)c * 16u + (uint32_t)r * rb));
+  }
   if (theta != nullptr) {
+    // (after the K loads are issued, so that they do not wait for the query)
     // lanes c, c + 16, c + 32 and c + 48 hold the four quarters of head c's
     // row: their sums of squares give |q| of head c in lane c
     float ss = 0.f;
@@ -367,19 +381,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < G; ++j)
       th[j] *= __builtin_sqrtf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss), j)));
-  }
-
-  // The unit's rows span less than 4 GiB (checked by the launcher), so a
-  // load address is the unit's base plus a 32-bit byte offset.
-  const char* kunit = reinterpret_cast<const char*>(k + b * sb + g * sh);
-  const uint32_t rb = (uint32_t)st * (uint32_t)sizeof(__half);
-  const int chunk = blockIdx.x;
-  const int row0 = chunk * CHUNK + w * RW + rr;
-  uint4 kv[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int r = min(row0 + 4 * u, t - 1);
-    kv[u] = load16_stream(kunit + ((uint32_t)c * 16u + (uint32_t)r * rb));
   }
 
   uint4* tile = xt[w];

@@ -35,6 +35,12 @@
 // selection and output offset, and the indices and scores are scattered from
 // the LDS list (or the streamed row) in ascending index order.
 //
+// Contexts longer than the keys the registers hold (64K) take the streamed
+// path from the start: the top key and the exact boundary come from passes
+// over the row, and the selection is emitted in 64K-position tiles of the
+// bitmaps, each tile continuing the previous one's output offset and its
+// count of keys equal to T already taken.
+//
 // DELTA mode first finds the cap-th largest key Tc as above and sums the
 // dense weights exp(s - lse) of the keys outside the top-cap set, in 2^-40
 // fixed point (exact, order-free integer sums). If that dropped mass exceeds
@@ -53,7 +59,9 @@ namespace {
 constexpr int kBins = 2048;
 constexpr int kRep1 = 4;                 // copies of the first-pass count histogram
 constexpr int kCandCap = 8192;           // LDS candidate list capacity (keys and indices)
-constexpr int kMaxWords = PRHS_MAX_SELECT_CTX / 32;
+// Positions the LDS bitmaps cover at once; longer rows are emitted in tiles.
+constexpr int kTileKeys = 65536;
+constexpr int kMaxWords = kTileKeys / 32;
 constexpr double kMassScale = 1099511627776.0;  // 2^40
 
 struct Pass {
@@ -426,7 +434,9 @@ __device__ __forceinline__ void mark_row(const float* __restrict__ row, int t, u
 // offset, stored in place of gt_bits and eq_bits. Thread i owns WPT
 // consecutive words.
 template <int NT, bool MASS>
-__device__ __forceinline__ void emit_offsets(int t, uint32_t take_eq, SelShared<NT, MASS>& sh) {
+__device__ __forceinline__ void emit_offsets(int t, uint32_t take_eq, SelShared<NT, MASS>& sh,
+                                             uint32_t out_base = 0u, uint32_t* n_out = nullptr,
+                                             uint32_t* n_eq_taken = nullptr) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -449,15 +459,22 @@ __device__ __forceinline__ void emit_offsets(int t, uint32_t take_eq, SelShared<
     sh.wtot2[w] = einc;
   }
   __syncthreads();
-  uint32_t gb = ginc - ng, eb = einc - ne;
+  uint32_t gb = ginc - ng, eb = einc - ne, gtot = 0, etot = 0;
 #pragma unroll
   for (int u = 0; u < NW; ++u) {
     if (u < w) {
       gb += sh.wtot[u];
       eb += sh.wtot2[u];
     }
+    gtot += sh.wtot[u];
+    etot += sh.wtot2[u];
   }
-  uint32_t pos = gb + (eb < take_eq ? eb : take_eq);
+  if (n_out != nullptr) {
+    // selected in this range: every key above T and the equal ones still due
+    *n_eq_taken = etot < take_eq ? etot : take_eq;
+    *n_out = gtot + *n_eq_taken;
+  }
+  uint32_t pos = out_base + gb + (eb < take_eq ? eb : take_eq);
   uint32_t eq_left = take_eq > eb ? take_eq - eb : 0u;
 #pragma unroll
   for (int q = 0; q < WPT; ++q) {
@@ -510,16 +527,66 @@ __device__ __forceinline__ void scatter_list(uint32_t C, int* __restrict__ out,
 }
 
 // Write the row's selected keys to their slots.
+// Write the row's selected keys to their slots. `row` and the bitmaps start at
+// key index i0 (a tile of a longer row).
 template <int NT, bool MASS>
 __device__ __forceinline__ void scatter_row(const float* __restrict__ row, int t,
                                             int* __restrict__ out, float* __restrict__ out_s,
                                             uint32_t cap, const SelShared<NT, MASS>& sh,
-                                            uint2* mirror) {
+                                            uint2* mirror, int i0 = 0) {
   for (int i = threadIdx.x; i < t; i += NT) {
     const int pos = out_slot<NT, MASS>((uint32_t)i, sh);
     if (pos >= 0 && (uint32_t)pos < cap)
-      put_sel(out, out_s, mirror, pos, (uint32_t)i, key_to_score(score_key(row[i])));
+      put_sel(out, out_s, mirror, pos, (uint32_t)(i0 + i), key_to_score(score_key(row[i])));
   }
+}
+
+// The streamed row's selection in tiles of kTileKeys positions: each tile's
+// bitmaps are cleared, marked and turned into offsets that continue the
+// previous tiles' output count and their count of keys equal to T taken.
+template <int NT, bool MASS>
+__device__ __forceinline__ void emit_row_tiled(const float* __restrict__ row, int t, uint32_t T,
+                                               uint32_t take_eq, int* __restrict__ out,
+                                               float* __restrict__ out_s, uint32_t cap,
+                                               SelShared<NT, MASS>& sh, uint2* mirror) {
+  uint32_t out_base = 0, eq_left = take_eq;
+  for (int t0 = 0; t0 < t; t0 += kTileKeys) {
+    const int tt = t - t0 < kTileKeys ? t - t0 : kTileKeys;
+    const int nw = (tt + 31) >> 5;
+    __syncthreads();  // the previous tile's scatter has read the bitmaps
+    for (int i = threadIdx.x; i < nw; i += NT) {
+      sh.gt_bits[i] = 0;
+      sh.eq_bits[i] = 0;
+    }
+    __syncthreads();
+    mark_row<NT, MASS>(row + t0, tt, T, sh);
+    uint32_t n_out = 0, n_eq = 0;
+    emit_offsets<NT, MASS>(tt, eq_left, sh, out_base, &n_out, &n_eq);
+    scatter_row<NT, MASS>(row + t0, tt, out, out_s, cap, sh, mirror, t0);
+    out_base += n_out;
+    eq_left -= n_eq;
+  }
+}
+
+// The row's top key into sh.kmax, streamed (for rows whose keys the registers
+// do not hold).
+template <int NT, bool MASS>
+__device__ __forceinline__ void stream_kmax(const float* __restrict__ row, int t,
+                                            SelShared<NT, MASS>& sh) {
+  if (threadIdx.x == 0) sh.kmax = 0;
+  __syncthreads();
+  uint32_t kmx = 0;
+  for (int i = threadIdx.x; i < t; i += NT) {
+    const uint32_t key = score_key(row[i]);
+    kmx = key > kmx ? key : kmx;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t y = __shfl_xor(kmx, o);
+    kmx = y > kmx ? y : kmx;
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh.kmax, kmx);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -821,7 +888,8 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
                                                   int head, int nch, uint32_t N, uint32_t& C,
                                                   SelShared<NT, MASS>& sh) {
   constexpr int NW = NT / kWave;
-  static_assert((PRHS_MAX_SELECT_CTX / kScoreChunk + NW - 1) / NW <= kSlots, "chunks per wave");
+  static_assert((PRHS_MAX_SELECT_CTX / kScoreChunk + NW - 1) / NW <= kWave,
+                "one lane per chunk count in a wave");
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   const int cpw = cand_cpw<NT>(nch);
@@ -893,10 +961,33 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
       }
     }
   }
-  // rows past the first round (chunks holding more than rows * 64 candidates)
+  // chunks past the first round's kSlots (more than 16 chunks per wave, i.e.
+  // contexts beyond 64K): their first 64-entry rows, kSlots chunks per round
+  const int first = kSlots / rows;  // chunks the first round covered
+  for (int k0 = first; k0 < cpw; k0 += kSlots) {
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int k = k0 + sl;
+      e[sl] = make_uint2(0u, 0u);
+      if (k < cpw && (uint32_t)lane < lane_read(cc, k < cpw ? k : 0))
+        e[sl] = src[(uint32_t)k * kScoreChunk + (uint32_t)lane];
+    }
+#pragma unroll
+    for (int sl = 0; sl < kSlots; ++sl) {
+      const int k = k0 + sl;
+      if (k < cpw && (uint32_t)lane < lane_read(cc, k < cpw ? k : 0)) {
+        const uint32_t key = score_key(__uint_as_float(e[sl].x));
+        sh.cand[base + lane_read(ex, k) + (uint32_t)lane] = make_uint2(key, e[sl].y);
+        kmx = key > kmx ? key : kmx;
+        kmn = key < kmn ? key : kmn;
+      }
+    }
+  }
+  // rows past the first 64-entry row (or past the first round's rows)
   for (int k = 0; k < cpw; ++k) {
     const uint32_t n = lane_read(cc, k);
-    for (uint32_t j = (uint32_t)(lane + rows * kWave); j < n; j += kWave) {
+    const int done = k < first ? rows : 1;
+    for (uint32_t j = (uint32_t)(lane + done * kWave); j < n; j += kWave) {
       const uint2 x = src[(size_t)k * kScoreChunk + j];
       const uint32_t key = score_key(__uint_as_float(x.x));
       sh.cand[base + lane_read(ex, k) + j] = make_uint2(key, x.y);
@@ -979,7 +1070,8 @@ __device__ __forceinline__ void load_keys(Keys<KPT>& K, const float* __restrict_
   finish_keys<KPT>(K);
 }
 
-// Write the selection once T and take are known and the bitmaps are marked:
+// Write the selection once T and take are known and (up to kTileKeys
+// positions) the bitmaps are marked:
 // indices and scores in ascending index order, scattered from the LDS list
 // (`list`) or from the streamed row, then the count, the cap flag and the
 // threshold hint.
@@ -989,9 +1081,14 @@ __device__ __forceinline__ void finish_head(const SelectArgs& a, int head, const
                                             uint32_t T, uint32_t take, int n_sel, int hit,
                                             SelShared<NT, MASS>& sh, uint2* mirror) {
   const uint32_t cap = (uint32_t)a.idx_cap;
-  emit_offsets<NT, MASS>(a.t, take, sh);
-  if (list) scatter_list<NT, MASS>(C, out, out_s, cap, sh, mirror);
-  else scatter_row<NT, MASS>(row, a.t, out, out_s, cap, sh, mirror);
+  if (a.t > kTileKeys) {
+    // longer rows are streamed (never listed): marked and emitted per tile
+    emit_row_tiled<NT, MASS>(row, a.t, T, take, out, out_s, cap, sh, mirror);
+  } else {
+    emit_offsets<NT, MASS>(a.t, take, sh);
+    if (list) scatter_list<NT, MASS>(C, out, out_s, cap, sh, mirror);
+    else scatter_row<NT, MASS>(row, a.t, out, out_s, cap, sh, mirror);
+  }
   if (threadIdx.x == 0) {
     a.count[head] = n_sel;
     if (a.cap_hit) a.cap_hit[head] = hit;
@@ -1163,8 +1260,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // Without scan candidates the scores are needed in registers: their loads
   // go out first and complete under the partial merge and the LDS clearing.
   const bool from_scan = !MASS && a.cand != nullptr;
+  // rows longer than the registers hold take the streamed path throughout
+  const bool regs = t <= KPT * NT;
   Keys<KPT> K;
-  if (!from_scan) load_keys_raw<KPT>(K, row, t);
+  K.valid = 0;
+  if (!from_scan && regs) load_keys_raw<KPT>(K, row, t);
   // the chunk counts of the scan's candidates (lane l of wave w: chunk
   // w * cpw + l), in flight under the partial merge
   uint32_t ccount = 0u;
@@ -1189,25 +1289,24 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
 
   // the query norm for the threshold hint, by the last wave (the first merges
-  // the partials); read only after the barriers that follow
-  if (!MASS && a.theta_out != nullptr && threadIdx.x / kWave == NT / kWave - 1) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const size_t off = (size_t)head * a.hint_d;
-    const float qn = a.hint_q_f16
-        ? (a.hint_d == 128 ? query_norm<__half, 128>(static_cast<const __half*>(a.hint_q) + off, lane)
-                           : query_norm<__half, 64>(static_cast<const __half*>(a.hint_q) + off, lane))
-        : (a.hint_d == 128 ? query_norm<float, 128>(static_cast<const float*>(a.hint_q) + off, lane)
-                           : query_norm<float, 64>(static_cast<const float*>(a.hint_q) + off, lane));
-    if (lane == 0) sh.qnorm = qn;
-  }
+  // the partials): its loads go out now and are summed after the LDS
+  // clearing; read only after the barriers that follow
+  const bool qwave = !MASS && a.theta_out != nullptr && threadIdx.x / kWave == NT / kWave - 1;
+  uint2 qshare = make_uint2(0u, 0u);
+  if (qwave) qshare = query_share(a.hint_q, (size_t)head, a.hint_d, a.hint_q_f16 != 0,
+                                  (int)(threadIdx.x & (kWave - 1)));
 
   for (int i = threadIdx.x; i < kBins * kRep1; i += NT) sh.hist[i] = 0;
   if constexpr (MASS)
     for (int i = threadIdx.x; i < kBins; i += NT) sh.mhist[i] = 0;
-  const int nwords = (t + 31) >> 5;
+  const int nwords = t < kTileKeys ? (t + 31) >> 5 : kMaxWords;
   for (int i = threadIdx.x; i < nwords; i += NT) {
     sh.gt_bits[i] = 0;
     sh.eq_bits[i] = 0;
+  }
+  if (qwave) {
+    const float qn = query_share_norm(qshare, a.hint_q_f16 != 0);
+    if ((threadIdx.x & (kWave - 1)) == 0) sh.qnorm = qn;
   }
 
   if constexpr (!MASS) {
@@ -1235,7 +1334,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         rescore_row<NT>(a, head, reinterpret_cast<uint4*>(sh.cand));
         __syncthreads();
       }
-      load_keys_raw<KPT>(K, row, t);
+      if (regs) load_keys_raw<KPT>(K, row, t);
     }
   }
 
@@ -1248,7 +1347,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // streams the row. sh.kmax is the top key either way.
   const uint32_t nb = (uint32_t)a.n_budget;
   uint32_t theta = 0;
-  const bool list = build_candidates<KPT, NT, MASS>(K, t, nb, theta, sh);
+  bool list = false;
+  if (regs) list = build_candidates<KPT, NT, MASS>(K, t, nb, theta, sh);
+  else stream_kmax<NT, MASS>(row, t, sh);
   const uint32_t C = sh.ncand;
   uint32_t Tn = 0, taken = nb;
   if (list) cand_radix<NT, MASS>(theta, sh.kmax, C, nb, Tn, taken, sh);
@@ -1291,13 +1392,16 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       }
     }
   }
-  if (list) mark_from_list<NT, MASS>(C, T, sh);
-  else mark_row<NT, MASS>(row, t, T, sh);
+  if (t <= kTileKeys) {
+    if (list) mark_from_list<NT, MASS>(C, T, sh);
+    else mark_row<NT, MASS>(row, t, T, sh);
+  }
   finish_head<NT, MASS>(a, head, row, out, out_s, list, C, T, take, n_sel, hit, sh, mirror);
   if constexpr (FUSE) fused_decode<NT, MASS>(a, head, n_sel, sh.kmax, sh.lse, sh);
 }
 
 constexpr int kSelThreads = 1024;
+static_assert(64 * kSelThreads == kTileKeys, "the largest register instantiation fills one tile");
 
 template <int MODE, bool FUSE>
 void launch_mode(int kpt, int nheads, const SelectArgs& a, hipStream_t stream) {

@@ -40,7 +40,7 @@ PRHS_OP_DECODE = 2
 PRHS_OP_ANCHOR_STEP = 3
 PRHS_OP_DENSE = 4
 PRHS_OP_EXPAND = 5
-PRHS_MAX_SELECT_CTX = 65536
+PRHS_MAX_SELECT_CTX = 262144
 PRHS_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTED = (

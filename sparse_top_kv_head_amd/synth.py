@@ -97,6 +97,10 @@ CONFIGS = {
     # Mistral-7B-shaped GQA: batch 4, 32 query heads on 8 KV heads, t=32768, N=2048, 32 steps.
     "mistral_gqa_32k": DecodeConfig("mistral_gqa_32k", 4, 32, 8, 128, 32768, 2048, 32, "f16", 1004,
                                     (256, 256), (8, 64), (1.5, 1.5), "step", 3.0),
+    # Mistral-7B-shaped GQA at 128K context: batch 1, 32 query heads on 8 KV
+    # heads, t=131072, N=2048, 16 steps (selection streams rows past 64K).
+    "mistral_gqa_128k": DecodeConfig("mistral_gqa_128k", 1, 32, 8, 128, 131072, 2048, 16, "f16",
+                                     1007, (1024, 1024), (8, 64), (1.5, 1.5), "step", 3.0),
     # GQA with 16 query heads per KV head: batch 2, 32 query heads on 2 KV
     # heads, t=32768, N=2048, 16 steps (the grouping one matrix-core scan
     # launch covers whole).

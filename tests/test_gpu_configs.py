@@ -95,11 +95,12 @@ def test_llama2_4k_full():
         assert _check_topn_heads(eng, w, cfg, step, heads, cache) >= len(heads) - 2
 
 
-@pytest.mark.parametrize("name", ["mistral_gqa_32k", "gqa16_32k"])
+@pytest.mark.parametrize("name", ["mistral_gqa_32k", "gqa16_32k", "mistral_gqa_128k"])
 def test_mistral_gqa_32k_sampled(name):
     """GQA layers at 32K (Mistral-7B-shaped, 4 query heads per KV head; and 16
-    per KV head, one scan launch per group): 16 sampled heads at three steps,
-    plus run-to-run determinism of every head's indices and outputs."""
+    per KV head, one scan launch per group) and at 128K (selection streams the
+    rows past 64K keys): 16 sampled heads at three steps, plus run-to-run
+    determinism of every head's indices and outputs."""
     dev = _dev()
     cfg = CONFIGS[name]
     w = make_workload(cfg, device=dev)

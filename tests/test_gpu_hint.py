@@ -76,7 +76,9 @@ HINT_CASES = [
     (2, 48, 8, 3001, 192, (16, 16)),       # G = 6 (sub-groups of 4 and 2), ragged t
     (2, 32, 2, 8192, 512, (64, 64)),       # G = 16: one scan launch per KV head
     (1, 28, 4, 6000, 256, (32, 32)),       # G = 7 (Qwen2.5-7B grouping), ragged t
-    (1, 128, 64, 65536, 256, (128, 128)),  # the largest context the selection takes
+    (1, 128, 64, 65536, 256, (128, 128)),  # the largest context the registers hold
+    (1, 8, 2, 131072, 2048, (512, 512)),   # 512 candidate chunks per head; streamed when unhinted
+    (1, 4, 1, 262144, 1024, (256, 256)),   # the largest context the selection takes
 ]
 
 

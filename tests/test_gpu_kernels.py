@@ -121,6 +121,9 @@ SELECT_CASES = [
     # sampled threshold and its streamed fallback at larger t
     ("flat", 2, 16384), ("ties", 2, 8192), ("neg_inf", 2, 32768), ("wide", 1, 65536),
     ("signed_zero", 2, 20000),
+    # past the keys the registers hold: streamed search, emission in 64K tiles
+    ("normal", 2, 65537), ("ties", 2, 100000), ("flat", 1, 131072), ("neg_inf", 1, 200000),
+    ("signed_zero", 1, 140000), ("normal", 1, 262144),
 ]
 
 
@@ -178,6 +181,8 @@ DELTA_CASES = [
     (2.0, 32768, 4096, 0.1, 0), (12.0, 65536, 512, 0.01, 0), (3.0, 8192, 1024, 0.3, 0),
     # coarse score grids: many keys tie with the boundary key
     (4.0, 16384, 2048, 0.05, 0.5), (1.0, 6000, 3000, 0.2, 0.25), (6.0, 20000, 800, 0.1, 1.0),
+    # past 64K keys: streamed searches, tiled emission
+    (4.0, 131072, 2048, 0.05, 0), (12.0, 100000, 512, 0.01, 0), (2.0, 262144, 4096, 0.1, 0.5),
 ]
 
 
@@ -409,7 +414,7 @@ def test_dense_decode(B, Hq, Hkv, d, t, dtype, pad):
 
 @pytest.mark.parametrize("t,n,m,bits", [(8192, 512, 2139, 23), (1000, 300, 1000, 23),
                                          (5000, 64, 64, 23), (3000, 200, 900, 3),
-                                         (20000, 512, 2000, 23)])
+                                         (20000, 512, 2000, 23), (150000, 512, 2500, 23)])
 def test_random_expand_exact(t, n, m, bits):
     """Bit-exact against the oracle: anchor sets from a clustered workload and
     random ones, draws from the seeded generator (bits=3: many equal draws, so
@@ -625,7 +630,8 @@ def test_anchor_step_hint_exact(ctx):
     (1, 24, 1, 2500, 0, 128),    # G = 24: sub-groups of 16 and 8
     (1, 12, 1, 2000, 0, 128),    # G = 12: one sub-group, 16-row operand
     (1, 4, 4, 9000, 0, 512),     # MHA, t past the selection's 8192-entry list
-    (1, 4, 1, 65536, 0, 1024),   # G = 4 at the largest context the selection takes
+    (1, 4, 1, 65536, 0, 1024),   # G = 4 at the largest context the registers hold
+    (1, 4, 1, 262144, 0, 1024),  # the largest context the selection takes (streamed)
 ])
 def test_anchor_step_recomputed_rows(B, Hq, Hkv, t, pad, N):
     """A hinted anchor step whose hints miss (too high: no key listed; too low:
