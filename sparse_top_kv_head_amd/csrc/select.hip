@@ -1415,7 +1415,11 @@ void launch_mode(int kpt, int nheads, const SelectArgs& a, hipStream_t stream) {
     case 8: PRHS_SEL(8); break;
     case 16: PRHS_SEL(16); break;
     case 32: PRHS_SEL(32); break;
-    default: PRHS_SEL(64); break;
+    case 64: PRHS_SEL(64); break;
+    // longer rows hold no keys in registers (streamed throughout): the
+    // smallest instantiation, whose register budget leaves the candidate and
+    // streamed paths free of spills
+    default: PRHS_SEL(1); break;
   }
 #undef PRHS_SEL
 }
