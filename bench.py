@@ -709,7 +709,18 @@ def main():
                                   "ms_per_step": round(total_ms / a.steps, 5),
                                   "achieved": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
                                   "frac": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "target_frac": 0.70}},
+                                  "target_frac": 0.70},
+                     # the selection with its fused decode, by difference of the two
+                     # graph-timed loops: the distinct V rows it gathers over its time
+                     "select_decode": {
+                         "kernel": "select_kernel<32, 1024, TOPN, fused decode>",
+                         "ms_per_step_by_difference": round(total_ms / a.steps - scan_ms, 5),
+                         "algorithmic_bytes_per_step": int(step_bytes - scan_bytes),
+                         "achieved": round((step_bytes - scan_bytes)
+                                           / max(total_ms / a.steps - scan_ms, 1e-6) * 1e-6, 1),
+                         "frac": round((step_bytes - scan_bytes)
+                                       / max(total_ms / a.steps - scan_ms, 1e-6) * 1e-6
+                                       / HBM_PEAK_GBS, 4)}},
         "step": {"hbm_alg_bytes": int(step_bytes), "hbm_alg_gbs": round(step_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
                  "hbm_lit_bytes": int(lit_bytes),
                  "hbm_lit_gbs": round(lit_bytes / (total_ms / a.steps / 1e3) / 1e9, 1),
