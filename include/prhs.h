@@ -24,6 +24,14 @@
  *    unless the environment variable PRHS_DEBUG_SYNC=1 is set, in which case
  *    each call synchronises its stream and reports kernel faults as
  *    PRHS_E_HIP.
+ *  - The device-checked build of this library (libprhs_checked.so, compiled
+ *    with PRHS_DEVICE_CHECKS) also synchronises after each call and returns
+ *    PRHS_E_HIP when a kernel met a broken input contract -- an index of a
+ *    given set outside [0, t), an anchor set not strictly ascending -- or a
+ *    broken internal invariant; the kernels themselves behave as in the
+ *    normal build (such entries are skipped) and never trap. Neither the
+ *    debug synchronisation nor the checks apply to work enqueued while the
+ *    stream is being captured into a graph.
  *  - Layout: q is [B, H_q, d] contiguous. K and V are [B, H_kv, t, d] with the
  *    element strides given in prhs_dims (the d axis is contiguous). Scores are
  *    fp32 [B, H_q, scores_ld]. Index sets are int32 [B, H_q, cap] plus int32

@@ -1,9 +1,11 @@
 """Build libprhs.so (HIP kernels for gfx950 + the C ABI) in the package directory.
 
-Usage: python -m sparse_top_kv_head_amd.build [--jobs N] [--verbose]
+Usage: python -m sparse_top_kv_head_amd.build [--jobs N] [--verbose] [--checked]
        python -m sparse_top_kv_head_amd.build --resources OUT.md
        python -m sparse_top_kv_head_amd.build --sanitize
-Cross-compiles without a GPU; always rebuilds. --resources writes the
+Cross-compiles without a GPU; always rebuilds. --checked builds
+libprhs_checked.so, whose kernels check input contracts and invariants and
+whose calls report a broken one as an error. --resources writes the
 compiler's per-kernel register, LDS and occupancy report instead. --sanitize
 builds the host code with address and undefined-behaviour checks into
 _build/asan and runs the host-side ABI tests on it (sanitize.py).
@@ -27,6 +29,10 @@ LIB = os.path.join(PKG, "libprhs.so")
 
 SOURCES = ["score.hip", "select.hip", "cis.hip", "decode.hip", "dense.hip", "append.hip", "probe.hip",
            "prhs_abi.cpp"]
+# The checked build: kernels record broken input contracts and invariants in
+# device check words that every call reads back (an error, never a trap).
+CHECKED_LIB = os.path.join(PKG, "libprhs_checked.so")
+CHECKED_FLAGS = ["-DPRHS_DEVICE_CHECKS"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -45,9 +51,9 @@ def hipcc():
     return exe
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, out_dir=BUILD, extra=()):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -60,20 +66,24 @@ def _compile(src, verbose):
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, checked: bool = False) -> str:
+    """libprhs.so, or with `checked` the device-checked libprhs_checked.so."""
+    out_dir = os.path.join(BUILD, "checked") if checked else BUILD
+    lib = CHECKED_LIB if checked else LIB
+    extra = CHECKED_FLAGS if checked else ()
+    os.makedirs(out_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, out_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _demangle_short(name):
@@ -137,6 +147,8 @@ if __name__ == "__main__":
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resources", metavar="OUT_MD", default=None,
                     help="write the per-kernel resource and occupancy table instead of building")
+    ap.add_argument("--checked", action="store_true",
+                    help="build the device-checked library libprhs_checked.so")
     ap.add_argument("--sanitize", action="store_true",
                     help="sanitizer build of the host code, then the host-side ABI tests on it")
     a = ap.parse_args()
@@ -149,4 +161,4 @@ if __name__ == "__main__":
     if a.resources:
         resources(a.resources)
     else:
-        print(build(a.jobs, a.verbose))
+        print(build(a.jobs, a.verbose, a.checked))

@@ -54,6 +54,8 @@ __global__ __launch_bounds__(kCisThreads) void cis_dilate_kernel(
     const int j = tile + tid;
     const int i = next;
     next = j + kCisThreads < n ? src[j + kCisThreads] : -1;
+    PRHS_CHECK(j >= n || (i >= 0 && i < t), kCheckIndex);
+    PRHS_CHECK(j >= n || j == 0 || src[j - 1] < i, kCheckOrder);
     int lo = 0, hi = -1;
     if (j < n && i >= 0 && i < t) {
       lo = i - r > 0 ? i - r : 0;
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(256) void expand_scores_kernel(
   const int* src = anchor_idx + (size_t)head * anchor_cap;
   for (int j = threadIdx.x; j < n; j += 256) {
     const int i = src[j];
+    PRHS_CHECK(i >= 0 && i < t, kCheckIndex);
     if (i >= 0 && i < t) atomicOr(&member[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
@@ -259,5 +262,7 @@ hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,
                        static_cast<const float*>(q_anchor), sim_tau, reuse_ok, d.head_dim, skip);
   return hipGetLastError();
 }
+
+PRHS_CHECK_READER(take_checks_cis)
 
 }  // namespace prhs

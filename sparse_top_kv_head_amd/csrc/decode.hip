@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   for (int i = tid; i < nr; i += kDecThreads) {
     const int id = irow[i];
     const bool ok = id >= 0 && id < t;
+    PRHS_CHECK(ok, kCheckIndex);
     sidx[i] = ok ? id : -1;
     if (has_scores)
       sp[i] = !ok ? -INFINITY
@@ -308,6 +309,8 @@ __device__ __forceinline__ int dilate_to_lds(const int* __restrict__ src, int n,
     const int j = tile + tid;
     const int i = next;
     next = j + NT < n ? src[j + NT] : -1;
+    PRHS_CHECK(j >= n || (i >= 0 && i < t), kCheckIndex);
+    PRHS_CHECK(j >= n || j == 0 || src[j - 1] < i, kCheckOrder);
     int lo = 0, hi = -1;
     if (j < n && i >= 0 && i < t) {
       lo = i - r > 0 ? i - r : 0;
@@ -407,6 +410,7 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   } else {
     for (int r = threadIdx.x; r < n; r += kHeadThreads) {
       const int id = r < kHeadThreads ? first : irow[r];
+      PRHS_CHECK(id >= 0 && id < t, kCheckIndex);
       sidx[r] = id >= 0 && id < t ? id : -1;
     }
   }
@@ -753,5 +757,7 @@ hipError_t launch_dropped_mass(const prhs_dims& d, const float* lse_sel, const f
                      lse_sel, lse_all, delta, tau, nheads);
   return hipGetLastError();
 }
+
+PRHS_CHECK_READER(take_checks_decode)
 
 }  // namespace prhs

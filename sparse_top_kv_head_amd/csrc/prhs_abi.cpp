@@ -39,12 +39,38 @@ bool debug_sync() {
   return on;
 }
 
+#ifdef PRHS_DEVICE_CHECKS
+constexpr bool kDeviceChecks = true;
+#else
+constexpr bool kDeviceChecks = false;
+#endif
+
+// True while `stream` is being captured into a graph: nothing may wait on it.
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 int finish(hipError_t err, hipStream_t stream, const char* what) {
-  if (err == hipSuccess && debug_sync()) {
+  // the debug synchronisation and the device checks are skipped for work
+  // being captured into a graph (it has not run yet)
+  const bool check = kDeviceChecks && err == hipSuccess && !capturing(stream);
+  if (err == hipSuccess && (debug_sync() || check) && !capturing(stream)) {
     err = hipStreamSynchronize(stream);
     if (err == hipSuccess) err = hipGetLastError();
   }
   if (err != hipSuccess) return fail(PRHS_E_HIP, "%s: %s", what, hipGetErrorString(err));
+  if (check) {
+    // the checked build: every kernel source's check word, read and cleared
+    const uint32_t bits =
+        prhs::take_checks_select() | prhs::take_checks_decode() | prhs::take_checks_cis();
+    if (bits != 0u)
+      return fail(PRHS_E_HIP, "%s: device check failed (0x%x):%s%s%s%s", what, bits,
+                  (bits & prhs::kCheckIndex) ? " an index outside [0, t)" : "",
+                  (bits & prhs::kCheckOrder) ? " an anchor set not strictly ascending" : "",
+                  (bits & prhs::kCheckList) ? " a candidate list past its capacity" : "",
+                  (bits & 0x80000000u) ? " (check words unreadable)" : "");
+  }
   return ok();
 }
 

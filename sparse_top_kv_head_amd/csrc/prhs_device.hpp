@@ -165,6 +165,38 @@ __host__ __device__ inline int mfma_rows(int nq) {
 }
 
 // ---------------------------------------------------------------------------
+// Device checks. Built with -DPRHS_DEVICE_CHECKS (the checked library), a
+// kernel that meets a broken input contract or internal invariant sets a bit
+// in its source file's check word with a vector atomic and carries on as the
+// unchecked build does (nothing traps); the library reads and clears the
+// words after each call and reports the bits as an error. Without the macro
+// every check compiles to nothing.
+// ---------------------------------------------------------------------------
+#ifdef PRHS_DEVICE_CHECKS
+static __device__ unsigned int g_check_word = 0u;
+#define PRHS_CHECK(cond, bit)                                        \
+  do {                                                               \
+    if (!(cond)) __hip_atomic_fetch_or(&g_check_word, (bit), __ATOMIC_RELAXED, \
+                                       __HIP_MEMORY_SCOPE_AGENT);    \
+  } while (0)
+// Host side: this source file's check word, read and cleared (synchronous).
+#define PRHS_CHECK_READER(fn)                                                      \
+  uint32_t fn() {                                                                  \
+    uint32_t v = 0u, zero = 0u;                                                    \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_word), sizeof v) != hipSuccess) \
+      return 0x80000000u;                                                          \
+    if (v != 0u) (void)hipMemcpyToSymbol(HIP_SYMBOL(g_check_word), &zero, sizeof zero); \
+    return v;                                                                      \
+  }
+#else
+#define PRHS_CHECK(cond, bit) \
+  do {                        \
+  } while (0)
+#define PRHS_CHECK_READER(fn) \
+  uint32_t fn() { return 0u; }
+#endif
+
+// ---------------------------------------------------------------------------
 // Write-through stores: the system-scope cache policy (sc0 sc1) sends the data
 // through the L2 to memory at once instead of leaving dirty lines behind. The
 // scan's outputs are written this way: interleaved with its K read stream,

@@ -182,6 +182,19 @@ hipError_t launch_dense(const prhs_dims& d, const void* q, const void* k, const 
 // Read `bytes` (a multiple of 16) of device memory once (HBM ceiling probe).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+// Bits of the device-check words (builds with PRHS_DEVICE_CHECKS).
+enum : uint32_t {
+  kCheckIndex = 1u,  // an index of a given set lies outside [0, t)
+  kCheckOrder = 2u,  // an anchor set is not strictly ascending
+  kCheckList = 4u,   // a candidate list would exceed its LDS capacity
+};
+
+// Device-check words of the kernel sources (read and cleared; always 0 unless
+// the library is built with PRHS_DEVICE_CHECKS; bit 31 if the read failed).
+uint32_t take_checks_select();
+uint32_t take_checks_decode();
+uint32_t take_checks_cis();
+
 hipError_t launch_dropped_mass(const prhs_dims& d, const float* lse_sel, const float* lse_all,
                                float* delta, float* tau, hipStream_t stream);
 

@@ -310,7 +310,8 @@ __device__ __forceinline__ void compact_row(const float* __restrict__ row, int t
       if (lane == 0) base = atomicAdd(&sh.ncand_r, (uint32_t)__popcll(m));
       base = lane_read(base, 0);
       const uint32_t pos = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-      if (h && pos < (uint32_t)kCandCap) sh.cand[pos].x = key;
+      PRHS_CHECK(!h || pos < (uint32_t)kCandCap, kCheckList);  // the caller knows they fit
+    if (h && pos < (uint32_t)kCandCap) sh.cand[pos].x = key;
     }
   }
   __syncthreads();
@@ -1447,5 +1448,7 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t
   }
   return hipGetLastError();
 }
+
+PRHS_CHECK_READER(take_checks_select)
 
 }  // namespace prhs
