@@ -143,7 +143,7 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      if (j >= nq) break;
+      if (j >= nq) continue;
       const size_t hc = (size_t)(b * Hq + h0 + j) * nchunks + chunk;
       if (!__builtin_isfinite(th[j])) {
         if (threadIdx.x == 0) store_through(cand_cnt + hc, 4u, 0u, kNoCand);
@@ -363,24 +363,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
     const int r = min(row0 + 4 * u, t - 1);
     kv[u] = load16_stream(kunit + ((uint32_t)c * 16u + (uint32_t)r * rb));
   }
+  // Each lane's two fp16 elements of every head's query row, for the norms
+  // that scale the thresholds; requested after the K loads and summed just
+  // before they are needed, so nothing waits for them.
+  uint32_t qw[G] = {};
   if (theta != nullptr) {
-    // (after the K loads are issued, so that they do not wait for the query)
-    // lanes c, c + 16, c + 32 and c + 48 hold the four quarters of head c's
-    // row: their sums of squares give |q| of head c in lane c
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = static_cast<float>(qa[j][e]);
-        ss = __builtin_fmaf(x, x, ss);
-      }
-    }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
 #pragma unroll
     for (int j = 0; j < G; ++j)
-      th[j] *= __builtin_sqrtf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss), j)));
+      if (j < nq)
+        qw[j] = reinterpret_cast<const uint32_t*>(q + (size_t)(b * Hq + h0 + j) * D)[lane];
   }
 
   uint4* tile = xt[w];
@@ -393,6 +384,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_scan_mfma_kernel(
       const int row = w * RW + 16 * a + c;
 #pragma unroll
       for (int r = 0; r < NR; ++r) sc[4 * rr + r][row] = acc[r] * scale;
+    }
+  }
+  if (theta != nullptr) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const __half2 h = __builtin_bit_cast(__half2, qw[j]);
+      const float x = __low2float(h), y = __high2float(h);
+      th[j] *= __builtin_sqrtf(wave_sum(__builtin_fmaf(x, x, y * y)));
     }
   }
   __syncthreads();
