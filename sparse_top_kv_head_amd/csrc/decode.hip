@@ -284,8 +284,8 @@ constexpr int kHeadThreads = 1024;
 constexpr int kHeadLoads = 8;
 constexpr int kShortWindow = 64;
 
-// CIS dilation of one head's anchor list src[0:n) into the LDS list sidx and
-// the output dst[0:out_cap), as the dilation kernel defines it: anchor i
+// CIS dilation of one head's anchor list src[0:n) into the LDS list
+// sidx[0:out_cap), as the dilation kernel defines it: anchor i
 // proposes [i - r, i + r] clipped to [0, t), starting after the largest end of
 // every earlier window (a running maximum over the list), so the output is the
 // sorted union for an ascending list and strictly ascending for any list;
@@ -295,7 +295,7 @@ constexpr int kShortWindow = 64;
 // `first` is src[threadIdx.x] (or anything past n), loaded by the caller
 // together with the count.
 __device__ __forceinline__ int dilate_to_lds(const int* __restrict__ src, int n, int first, int r,
-                                             int t, int* sidx, int* __restrict__ dst, int out_cap,
+                                             int t, int* sidx, int out_cap,
                                              int (*s_wmax)[kHeadThreads / kWave],
                                              uint32_t (*s_wsum)[kHeadThreads / kWave]) {
   constexpr int NT = kHeadThreads, NW = NT / kWave;
@@ -345,10 +345,7 @@ __device__ __forceinline__ int dilate_to_lds(const int* __restrict__ src, int n,
     off += incl - len;
     for (uint32_t k = 0; k < len; ++k) {
       const uint32_t o = (uint32_t)base + off + k;
-      if (o < (uint32_t)out_cap) {
-        store_through(dst, (uint32_t)out_cap * 4u, o * 4u, (uint32_t)(lo + (int)k));
-        sidx[o] = lo + (int)k;
-      }
+      if (o < (uint32_t)out_cap) sidx[o] = lo + (int)k;
     }
     base += (int)tile_total;
     prev_end = tile_max;
@@ -404,17 +401,35 @@ __global__ __launch_bounds__(kHeadThreads) void decode_head_kernel(
   // the index list in LDS (indices outside [0, t) become -1): the given list,
   // or the dilation of the anchor list
   if (dilate) {  // uniform over the workgroup
-    n = dilate_to_lds(irow, n, first, radius < t ? radius : t, t, sidx,
-                      dil_idx + (size_t)head * dil_cap, dil_cap, s_wmax, s_wsum);
+    n = dilate_to_lds(irow, n, first, radius < t ? radius : t, t, sidx, dil_cap, s_wmax, s_wsum);
     if (threadIdx.x == 0) dil_count[head] = n;
   } else {
-    for (int r = threadIdx.x; r < n; r += kHeadThreads) {
-      const int id = r < kHeadThreads ? first : irow[r];
-      PRHS_CHECK(id >= 0 && id < t, kCheckIndex);
-      sidx[r] = id >= 0 && id < t ? id : -1;
+    // the rest of the list, four entries per thread requested together
+    for (int r0 = 0; r0 < n; r0 += 4 * kHeadThreads) {
+      int ids[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u * kHeadThreads + (int)threadIdx.x;
+        ids[u] = r >= n ? -1 : r < kHeadThreads ? first : irow[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u * kHeadThreads + (int)threadIdx.x;
+        if (r < n) {
+          PRHS_CHECK(ids[u] >= 0 && ids[u] < t, kCheckIndex);
+          sidx[r] = ids[u] >= 0 && ids[u] < t ? ids[u] : -1;
+        }
+      }
     }
   }
   __syncthreads();
+  if (dilate) {
+    // the dilated list goes out from LDS in whole rows, through the L2, while
+    // the K and V rows are gathered
+    int* dst = dil_idx + (size_t)head * dil_cap;
+    for (int r = threadIdx.x; r < n; r += kHeadThreads)
+      store_through(dst, (uint32_t)dil_cap * 4u, (uint32_t)r * 4u, (uint32_t)sidx[r]);
+  }
   const int rw = ((n + NW - 1) / NW + RPW - 1) / RPW * RPW;
   const int rb = w * rw;
   const int re = min(n, rb + rw);
