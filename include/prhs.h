@@ -252,9 +252,8 @@ int prhs_reuse_step(const prhs_dims* dims, const int32_t* anchor_idx, int32_t an
  * rules are the union of the three calls' rules.
  *
  * In either mode, with fp16 rows of head_dim 128 and n_budget (the TOPN
- * budget or the DELTA cap) <= 2048, when there are >= 128 (b, h) heads or
- * n_budget <= 256, each head's selection workgroup also computes its
- * attention: the selection is bit-identical to the three calls, and out,
+ * budget or the DELTA cap) <= 2048, each head's selection workgroup also
+ * computes its attention: the selection is bit-identical to the three calls, and out,
  * lse_sel, delta and tau equal theirs up to the order of the fp32 sums.
  *
  * theta (nullable, fp32 [B, H_q], in/out; TOPN only): a per-head score

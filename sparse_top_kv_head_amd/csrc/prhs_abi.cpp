@@ -539,8 +539,8 @@ int prhs_anchor_step(const prhs_dims* dims, int32_t mode, int32_t n_budget, floa
     // recomputes the row of a head whose candidates miss
     cd.skip_hinted = prhs::scan_uses_mfma(*dims);
   }
-  // With enough heads (or a one-split budget) each head's select workgroup
-  // also decodes its head: no split partials and no merge launch.
+  // With fp16 rows of 128 and a budget of at most 2048 each head's select
+  // workgroup also decodes its head: no split partials and no merge launch.
   const bool fuse = prhs::fuse_decode(*dims, mode, n_budget);
   hipError_t err = prhs::launch_score(*dims, q, k, scores, nullptr, part, stream, &cd);
   if (err == hipSuccess) {

@@ -96,15 +96,14 @@ struct SelectArgs {
 
 hipError_t launch_select(const prhs_dims& d, const SelectArgs& a, hipStream_t stream);
 
-// Largest budget the fused select-and-decode takes, and the fewest heads for
-// which it beats the split decode (one workgroup per head must still cover
-// about half of the 256 CUs; budgets of one split never need more).
+// Largest budget the fused select-and-decode takes. At any head count it
+// beats the select kernel followed by the split decode and its merge: a head's
+// V rows (at most 512 KiB) take one CU about as long as the two launches and
+// the round trips through the selection's outputs that it saves.
 constexpr int kFuseRows = 2048;
-constexpr int kFuseMinHeads = 128;
 inline bool fuse_decode(const prhs_dims& d, int mode, int n_budget) {
   return (mode == PRHS_TOPN || mode == PRHS_DELTA) && d.dtype == PRHS_F16 && d.head_dim == 128 &&
-         n_budget <= kFuseRows &&
-         (d.batch * d.n_q_heads >= kFuseMinHeads || n_budget <= kDecodeRows);
+         n_budget <= kFuseRows;
 }
 
 hipError_t launch_cis(const prhs_dims& d, const int* anchor_idx, int anchor_cap,

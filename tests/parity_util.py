@@ -41,11 +41,10 @@ def reorder_tols(n, vmax):
 def fused_anchor_decode(dtype_f16, head_dim, n_heads, mode_topn, n_budget):
     """Whether the anchor step decodes inside the select kernel (the library's
     rule, the same for top-N and for the delta budget, where n_budget is the
-    cap: fp16 rows of 128, n_budget <= 2048, and >= 128 heads or a one-split
-    budget of <= 256). mode_topn is accepted for the callers' clarity only."""
-    del mode_topn
-    return (dtype_f16 and head_dim == 128 and n_budget <= 2048
-            and (n_heads >= 128 or n_budget <= 256))
+    cap: fp16 rows of 128 and n_budget <= 2048, at any head count). n_heads and
+    mode_topn are accepted for the callers' clarity only."""
+    del mode_topn, n_heads
+    return dtype_f16 and head_dim == 128 and n_budget <= 2048
 
 
 def score_bound(q, K):

@@ -1,7 +1,7 @@
 """Anchor steps with the carried threshold hint, at the shapes where the
-selection also decodes its head (fp16 rows of 128, >= 128 heads or a one-split
-budget): the scan hands the selection only the keys at or above each head's
-hint, and heads whose hinted keys miss the answer take the full search.
+selection also decodes its head (fp16 rows of 128, budgets up to 2048): the
+scan hands the selection only the keys at or above each head's hint, and heads
+whose hinted keys miss the answer take the full search.
 
 The results must not depend on the hint: every case compares hinted steps
 with unhinted ones bit for bit -- the selected sets, the dense log-sum-exp,

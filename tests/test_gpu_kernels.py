@@ -510,9 +510,11 @@ def test_engine_topn_step_small():
 
 @pytest.mark.parametrize("mode,budget,heads", [
     (P.PRHS_TOPN, 256, 8),     # one-split budget: decoded inside the select kernel
-    (P.PRHS_TOPN, 512, 8),     # split decode and merge
-    (P.PRHS_TOPN, 512, 128),   # 128 heads: fused again
+    (P.PRHS_TOPN, 512, 8),     # decoded inside the select kernel at any head count
+    (P.PRHS_TOPN, 2560, 8),    # budget over 2048: split decode and merge
+    (P.PRHS_TOPN, 512, 128),
     (P.PRHS_DELTA, 256, 8),
+    (P.PRHS_DELTA, 2560, 8),   # cap over 2048: split decode and merge
 ])
 def test_anchor_step_matches_separate_calls(mode, budget, heads):
     """The one-call step selects exactly what the separate calls select; its
@@ -551,14 +553,14 @@ def test_anchor_step_matches_separate_calls(mode, budget, heads):
         assert torch.equal(a.cap_hit, b.cap_hit)
 
 
-@pytest.mark.parametrize("batch", [1, 4])
-def test_anchor_step_graph_replay_matches_eager(batch):
+@pytest.mark.parametrize("batch,budget", [(1, 512), (4, 512), (1, 2560)])
+def test_anchor_step_graph_replay_matches_eager(batch, budget):
     """A captured step replays to the eager results, replay after replay, with
-    eager work and synchronisations between the replays (32 heads: split
-    decode and merge; 128 heads: decoded inside the select kernel)."""
+    eager work and synchronisations between the replays (budget 512: decoded
+    inside the select kernel; 2560: split decode and merge)."""
     dev = _dev()
     from sparse_top_kv_head_amd.synth import CONFIGS, make_workload
-    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=batch, ctx_len=8192, budget=512, steps=3,
+    cfg = CONFIGS["mistral_gqa_32k"].replace(batch=batch, ctx_len=8192, budget=budget, steps=3,
                                              n_clusters=(64, 64))
     w = make_workload(cfg, device=dev)
     eng = DecodeEngine(w.K, cfg.n_q_heads, cfg.budget)
