@@ -260,6 +260,20 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over aligned groups of L consecutive lanes, the exchanges of
+// group_sum; every lane of the group receives it. L in {4, 8, 16, 32, 64}.
+template <int L>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (L >= 8) x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  if constexpr (L >= 16) x = fmaxf(x, dpp<kDppRowMirror>(x));
+  if constexpr (L >= 32)
+    x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F)));
+  if constexpr (L >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

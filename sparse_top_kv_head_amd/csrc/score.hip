@@ -166,17 +166,44 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
     }
   }
   if (part != nullptr) {
-    for (int j = w; j < nq; j += NW) {
+    // L lanes per head: with G >= 4 heads (L <= 64) every head's partial is
+    // formed at once by its own lanes, G values each, and reduced by lane
+    // exchanges inside the wave; fewer heads take one wave per head in turn
+    constexpr int L = (NW * kWave) / G;
+    if constexpr (G >= 4 && L * G == NW * kWave && L * G == CHUNK) {
+      const int j = (int)threadIdx.x / L;
+      const int sub = (int)threadIdx.x % L;
+      float v[G];
       float m = -INFINITY;
-      for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
-      m = wave_max(m);
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int i = sub + k * L;
+        v[k] = i < nrows ? sc[j][i] : -INFINITY;
+        m = fmaxf(m, v[k]);
+      }
+      m = group_max<L>(m);
       float l = 0.f;
-      if (m != -INFINITY)
-        for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
-      l = wave_sum(l);
-      if (lane == 0)
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) l += __expf(v[k] - m);
+      }
+      l = group_sum<L>(l);
+      if (sub == 0 && j < nq)
         store_through(part + (size_t)(b * Hq + h0 + j) * nchunks + chunk, 8u, 0u,
                       make_uint2(__float_as_uint(m), __float_as_uint(l)));
+    } else {
+      for (int j = w; j < nq; j += NW) {
+        float m = -INFINITY;
+        for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
+        m = wave_max(m);
+        float l = 0.f;
+        if (m != -INFINITY)
+          for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
+        l = wave_sum(l);
+        if (lane == 0)
+          store_through(part + (size_t)(b * Hq + h0 + j) * nchunks + chunk, 8u, 0u,
+                        make_uint2(__float_as_uint(m), __float_as_uint(l)));
+      }
     }
   }
 }
