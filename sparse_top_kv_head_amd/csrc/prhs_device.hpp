@@ -274,17 +274,12 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
+// Whole-wave reductions (every lane receives the result; called with the
+// whole wave active): the DPP and swizzle exchanges of group_max/group_sum,
+// which take a few cycles each, with one cross-half exchange at the end.
+__device__ __forceinline__ float wave_max(float x) { return group_max<kWave>(x); }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<kWave>(x); }
 
 // fp32 Euclidean norm of one query row of D elements (lane-strided loads);
 // every lane of the wave returns it.
@@ -338,13 +333,19 @@ __device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l
   m = mn;
 }
 
+// The (max, sum-of-exp) pair of the whole wave, through the exchanges of
+// group_sum (each pairs every lane with a distinct partner, so all lanes end
+// with the same pair).
+__device__ __forceinline__ float swizzle_half(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
 __device__ __forceinline__ void wave_ml(float& m, float& l) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o);
-    const float l2 = __shfl_xor(l, o);
-    ml_combine(m, l, m2, l2);
-  }
+  ml_combine(m, l, dpp<kDppXor1>(m), dpp<kDppXor1>(l));
+  ml_combine(m, l, dpp<kDppXor2>(m), dpp<kDppXor2>(l));
+  ml_combine(m, l, dpp<kDppRowHalfMirror>(m), dpp<kDppRowHalfMirror>(l));
+  ml_combine(m, l, dpp<kDppRowMirror>(m), dpp<kDppRowMirror>(l));
+  ml_combine(m, l, swizzle_half(m), swizzle_half(l));
+  ml_combine(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
 }
 
 // Inclusive prefix sum of 32-bit values over the 64 lanes of a wave, with DPP

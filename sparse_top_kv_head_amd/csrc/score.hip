@@ -195,11 +195,11 @@ __device__ __forceinline__ void scan_tail(const float (&sc)[G][PITCH], uint32_t 
       for (int j = w; j < nq; j += NW) {
         float m = -INFINITY;
         for (int i = lane; i < nrows; i += kWave) m = fmaxf(m, sc[j][i]);
-        m = wave_max(m);
+        m = group_max<kWave>(m);
         float l = 0.f;
         if (m != -INFINITY)
           for (int i = lane; i < nrows; i += kWave) l += __expf(sc[j][i] - m);
-        l = wave_sum(l);
+        l = group_sum<kWave>(l);
         if (lane == 0)
           store_through(part + (size_t)(b * Hq + h0 + j) * nchunks + chunk, 8u, 0u,
                         make_uint2(__float_as_uint(m), __float_as_uint(l)));
