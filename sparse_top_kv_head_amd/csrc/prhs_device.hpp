@@ -360,16 +360,47 @@ __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x) {
   return x;
 }
 
-// Inclusive running maximum over the 64 lanes of a wave.
+// Inclusive running maximum over the 64 lanes of a wave: the DPP steps of
+// wave_scan_u32, with the smallest int as the value of lanes that have no
+// source.
 __device__ __forceinline__ int wave_inclusive_max(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x = x > y ? x : y;
-  }
+  constexpr int kLow = -2147483647 - 1;
+  int y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x = x > y ? x : y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x = x > y ? x : y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x = x > y ? x : y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x = x > y ? x : y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x = x > y ? x : y;
+  y = __builtin_amdgcn_update_dpp(kLow, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  x = x > y ? x : y;
   return x;
 }
+
+// Maximum and minimum of 32-bit unsigned values over the whole wave (every
+// lane receives it; called with the whole wave active), through the
+// exchanges of group_sum.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t x) {
+  auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = pick(x, dpp_u32<kDppXor1>(x));
+  x = pick(x, dpp_u32<kDppXor2>(x));
+  x = pick(x, dpp_u32<kDppRowHalfMirror>(x));
+  x = pick(x, dpp_u32<kDppRowMirror>(x));
+  x = pick(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F));
+  x = pick(x, (uint32_t)__shfl_xor((int)x, 32));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) { return wave_extreme_u32<true>(x); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return wave_extreme_u32<false>(x); }
 
 __device__ __forceinline__ uint32_t lane_read(uint32_t x, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);

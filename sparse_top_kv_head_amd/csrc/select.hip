@@ -581,11 +581,7 @@ __device__ __forceinline__ void stream_kmax(const float* __restrict__ row, int t
     const uint32_t key = score_key(row[i]);
     kmx = key > kmx ? key : kmx;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t y = __shfl_xor(kmx, o);
-    kmx = y > kmx ? y : kmx;
-  }
+  kmx = wave_max_u32(kmx);
   if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(&sh.kmax, kmx);
   __syncthreads();
 }
@@ -777,11 +773,7 @@ __device__ __forceinline__ bool build_candidates(const Keys<KPT>& K, int t, uint
   const uint32_t cnt = (uint32_t)__builtin_popcountll(hit);
   const uint32_t incl = wave_scan_u32(cnt);
   const uint32_t wtotal = lane_read(incl, kWave - 1);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t y = __shfl_xor(kmx, o);
-    kmx = y > kmx ? y : kmx;
-  }
+  kmx = wave_max_u32(kmx);
   uint32_t base = 0;
   if (lane == 0 && wtotal) {
     base = atomicAdd(&sh.ncand, wtotal);
@@ -996,13 +988,8 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
       kmn = key < kmn ? key : kmn;
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t y = __shfl_xor(kmx, o);
-    const uint32_t z = __shfl_xor(kmn, o);
-    kmx = y > kmx ? y : kmx;
-    kmn = z < kmn ? z : kmn;
-  }
+  kmx = wave_max_u32(kmx);
+  kmn = wave_min_u32(kmn);
   if (lane == 0) {
     atomicMax(&sh.kmax, kmx);
     atomicMin(&sh.kmin, kmn);
