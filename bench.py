@@ -64,7 +64,7 @@ def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", default="mistral_gqa_32k")
     ap.add_argument("--rotate", type=int, default=4, help="independent KV copies cycled over steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
