@@ -80,11 +80,11 @@ def pct(a):
     return [round(float(np.percentile(a, p)), 5) for p in (10, 50, 90)]
 
 
-def timed_steps(step_fns, stream, warm_replays=2):
+def timed_steps(step_fns, stream, warm_replays=8):
     """Run the steps eagerly with events between them, then capture the same
     sequence once as a HIP graph, replay it `warm_replays` times untimed (the
-    first replays of a fresh graph run 2-4 % slower than the steady state), and
-    time one more replay.
+    first replays of a fresh graph run 2-4 % slower than the steady state; two
+    were not enough to reach it, eight are), and time one more replay.
 
     Returns (per-step eager ms, graph replay ms for the whole sequence)."""
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(step_fns) + 1)]
