@@ -62,6 +62,17 @@ constexpr int kCandCap = 8192;           // LDS candidate list capacity (keys an
 // Positions the LDS bitmaps cover at once; longer rows are emitted in tiles.
 constexpr int kTileKeys = 65536;
 constexpr int kMaxWords = kTileKeys / 32;
+// Threads per selection workgroup: 1024, or 512 for top-N rows of at most
+// kShortCtx keys, where half the waves make the latency-bound phases cheaper
+// and 8 keys per thread still hold the row (LLaMA2-shaped 4K step 19.0 ->
+// 17.7 us with the two-chunk read-ahead of gather_candidates).
+constexpr int kSelThreads = 1024;
+constexpr int kShortSelThreads = 512;
+constexpr int kShortCtx = 4096;
+template <int NT>
+constexpr int max_select_ctx() {
+  return NT == kSelThreads ? PRHS_MAX_SELECT_CTX : kShortCtx;
+}
 constexpr double kMassScale = 1099511627776.0;  // 2^40
 
 struct Pass {
@@ -881,7 +892,7 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
                                                   int head, int nch, uint32_t N, uint32_t& C,
                                                   SelShared<NT, MASS>& sh) {
   constexpr int NW = NT / kWave;
-  static_assert((PRHS_MAX_SELECT_CTX / kScoreChunk + NW - 1) / NW <= kWave,
+  static_assert((max_select_ctx<NT>() / kScoreChunk + NW - 1) / NW <= kWave,
                 "one lane per chunk count in a wave");
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -893,16 +904,19 @@ __device__ __forceinline__ bool gather_candidates(const uint2* __restrict__ cand
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint2* src = cand + ((size_t)head * nch + (size_t)wu * cpw) * kScoreChunk;
   uint2 e[kSlots];
-  // Up to 4K keys (one chunk per wave, all of its slots in the first round)
-  // the wave requests its whole chunk before its count is in: 2 KiB per wave
-  // read ahead, one dependent round trip saved. Slots past the count hold
+  // Up to 4K keys (one chunk per wave of the 1024-thread workgroup, two per
+  // wave of the 512-thread one; all four rows of each in the first round) the
+  // wave requests its whole chunks before their counts are in: 2 or 4 KiB per
+  // wave read ahead, one dependent round trip saved. Slots past a count hold
   // stale entries and are never used.
-  const bool ahead = cpw == 1 && rows == 4;
+  const bool ahead = cpw <= (NT == kShortSelThreads ? 2 : 1) && rows == 4;
   if (ahead) {
 #pragma unroll
     for (int sl = 0; sl < kSlots; ++sl) {
+      const int k = sl / 4, r = sl - k * 4;
       e[sl] = make_uint2(0u, 0u);
-      if (sl < rows && wu < nch) e[sl] = src[(uint32_t)(lane + sl * kWave)];
+      if (k < cpw && wu * cpw + k < nch)
+        e[sl] = src[(uint32_t)(k * kScoreChunk + lane + r * kWave)];
     }
   }
   const bool bad = __ballot(c == kNoCand) != 0ull;
@@ -1388,8 +1402,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   if constexpr (FUSE) fused_decode<NT, MASS>(a, head, n_sel, sh.kmax, sh.lse, sh);
 }
 
-constexpr int kSelThreads = 1024;
 static_assert(64 * kSelThreads == kTileKeys, "the largest register instantiation fills one tile");
+static_assert(kShortCtx <= kTileKeys && kShortCtx % kShortSelThreads == 0, "short rows fit one tile");
+
+// Short top-N rows: the 512-thread workgroup, kShortCtx / 512 keys per thread.
+template <bool FUSE>
+void launch_short(int nheads, const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((select_kernel<kShortCtx / kShortSelThreads, kShortSelThreads, PRHS_TOPN, FUSE>),
+                     dim3(nheads), dim3(kShortSelThreads), 0, stream, a);
+}
 
 template <int MODE, bool FUSE>
 void launch_mode(int kpt, int nheads, const SelectArgs& a, hipStream_t stream) {
@@ -1425,7 +1446,10 @@ hipError_t launch_select(const prhs_dims& d, const SelectArgs& args, hipStream_t
   a.t = d.ctx_len;
   a.ld = d.scores_ld;
   a.nchunks = score_nchunks(d);
-  if (a.mode == PRHS_DELTA) {
+  if (a.mode == PRHS_TOPN && d.ctx_len <= kShortCtx) {
+    if (a.v != nullptr) launch_short<true>(nheads, a, stream);
+    else launch_short<false>(nheads, a, stream);
+  } else if (a.mode == PRHS_DELTA) {
     if (a.v != nullptr) launch_mode<PRHS_DELTA, true>(kpt, nheads, a, stream);
     else launch_mode<PRHS_DELTA, false>(kpt, nheads, a, stream);
   } else if (a.v != nullptr) {
