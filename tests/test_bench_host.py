@@ -57,3 +57,17 @@ def test_reuse_quality_matches_oracle():
         row = s[b, h].astype(np.float64)
         assert abs(float(beta[b, h]) - O.beta_emp(row, S)) < 1e-5, (b, h)
         assert float(overlap[b, h]) == O.overlap_with_oracle(S, O.topn_select(row, N)), (b, h)
+
+
+def test_pages_context_quotes_the_abstract_and_picks_the_largest_ratio():
+    """The context block carries the pages' A100 figures (Abstract) unchanged and
+    this run's largest dense-over-CIS-16 ratio with its shape."""
+    ctx = bench.pages_context()
+    assert ctx["attention_operator_latency_speedup_over_dense"] == 9.9
+    assert ctx["throughput_gain_over_dense"] == 2.8 and "this_run" not in ctx
+    rows = [{"batch": 8, "ctx_len": 2048, "dense_over_cis16": 2.0, "dense_over_anchor": 1.3},
+            {"batch": 16, "ctx_len": 16384, "dense_over_cis16": 9.0, "dense_over_anchor": 1.9},
+            {"batch": 8, "ctx_len": 16384, "dense_over_cis16": 8.9, "dense_over_anchor": 2.0}]
+    run = bench.pages_context({"rows": rows})["this_run"]
+    assert run["dense_over_cis16_max"] == 9.0 and run["shape"] == "batch 16, t 16384"
+    assert run["dense_over_anchor_same_shape"] == 1.9
