@@ -247,6 +247,13 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
     for i in range(warmup * Pd):
         mk(i)()
     per, gms = timed_steps([mk(i) for i in range(n_steps)], stream)
+    # each kind of step alone, graph-replayed back to back (no host launch gaps):
+    # the anchor steps of the sequence, and the reuse steps against one anchor set
+    a_steps = [i for i in range(n_steps) if i % Pd == 0]
+    r_steps = [i for i in range(n_steps) if i % Pd != 0][:16]
+    _, a_g = timed_steps([mk(i) for i in a_steps], stream)
+    _, r_g = timed_steps([mk(i) for i in r_steps], stream)
+    a_graph_ms, r_graph_ms = a_g / len(a_steps), r_g / len(r_steps)
     e, d = cfg.elem_bytes, cfg.head_dim
     heads = cfg.batch * cfg.n_q_heads
     a_rows = distinct_rows(anchor.idx, anchor.count, cfg.group)
@@ -279,9 +286,13 @@ def bench_cis(P, cfg, dev, stream, warmup, copies, n_steps):
     res = _summary(cfg, per, gms, n_steps, mean_bytes, {
         "kv_copies_rotated": copies, "budget": N, "radius": r, "refresh_period": Pd,
         "anchor": {"ms_p10_p50_p90": pct(a_ms), "hbm_alg_bytes": int(a_bytes),
-                   "hbm_alg_gbs_p50": round(a_bytes / (np.median(a_ms) / 1e3) / 1e9, 1)},
+                   "hbm_alg_gbs_p50": round(a_bytes / (np.median(a_ms) / 1e3) / 1e9, 1),
+                   "graph_ms_per_step": round(a_graph_ms, 5),
+                   "frac_of_peak_graph": round(a_bytes / (a_graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "reuse": {"ms_p10_p50_p90": pct(r_ms), "hbm_alg_bytes": int(r_bytes),
                   "hbm_alg_gbs_p50": round(r_bytes / (np.median(r_ms) / 1e3) / 1e9, 1),
+                  "graph_ms_per_step": round(r_graph_ms, 5),
+                  "frac_of_peak_graph": round(r_bytes / (r_graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mean_dilated_rows_per_head": round(float(reuse.count.float().mean()), 1),
                   "heads_steps_per_s_p50": round(heads / (np.median(r_ms) / 1e3), 1),
                   "delta_reused_set_mean": round(float(np.mean(d_reuse)), 5),
