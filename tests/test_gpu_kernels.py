@@ -117,6 +117,9 @@ def _score_rows(kind, H, t, seed):
 SELECT_CASES = [
     ("normal", 3, 1), ("normal", 3, 2), ("normal", 5, 7), ("normal", 4, 1000), ("normal", 2, 1025),
     ("normal", 2, 4097), ("normal", 2, 32768), ("normal", 1, 65536), ("ties", 3, 5000),
+    # the last length of the 512-thread workgroup (4096) and short rows of it with
+    # ties, flat scores and -inf
+    ("normal", 2, 4096), ("ties", 2, 4096), ("flat", 2, 2048), ("neg_inf", 2, 4000),
     ("flat", 2, 3000), ("signed_zero", 2, 777), ("neg_inf", 2, 2049), ("wide", 2, 16384),
     # sampled threshold and its streamed fallback at larger t
     ("flat", 2, 16384), ("ties", 2, 8192), ("neg_inf", 2, 32768), ("wide", 1, 65536),
